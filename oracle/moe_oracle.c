@@ -1,0 +1,317 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the DeepSeekMoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header or constant with the GPU path.
+ *
+ * Arithmetic is IEEE fp32 with a fixed, ascending summation order and no
+ * fused multiply-add; OpenMP splits only independent tokens, so results are
+ * identical at any thread count.  bf16 inputs are widened to fp32 exactly.
+ *
+ * What it computes (DeepSeekMoE pages, deepforge.srivtx.xyz "DeepSeekMoE"):
+ *   - fine-grained segmentation: n = m*N routed experts, mK activated, of
+ *     which K_s are shared, so k = m*K - K_s routed experts are kept
+ *     (sections "What it is" and "The idea in two moves");
+ *   - routing of section "Routing in a classic MoE layer":
+ *       s_i = softmax_i(u^T e_i) over all n routed experts,
+ *       g_i = s_i if s_i is among the k largest, else 0 (no renormalisation,
+ *       as the note under "Top-k routing, from affinities to gates" states),
+ *       h   = sum_i g_i FFN_i(u) + [shared experts] + u;
+ *   - selection order of the "Top-k routing" sketch: experts ordered by
+ *     descending affinity logit, ties kept in index order (a stable sort);
+ *   - balance statistics of section "Expert-level balance loss": f_i from the
+ *     share of tokens that picked expert i, P_i the mean affinity s_i;
+ *   - expert FFN = SwiGLU ("GLU Variants Improve Transformer", cited on the
+ *     observer.broadside.tech card): FFN(x) = W2 (SiLU(W1 x) * (W3 x)),
+ *     SiLU(z) = z / (1 + exp(-z)), no biases.
+ * Readings where the pages are silent: softmax over the routed experts only
+ * (shared experts have no centroid and weight one); f_i = n/(k T) * count_i so
+ * that sum_i f_i = n; the layer is dropless (no capacity limit).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+#define ORC_OK 0
+#define ORC_ERR_ARG 1
+#define ORC_ERR_MEM 2
+
+/* Element i of a stored tensor as fp32 (bf16 widening is exact). */
+static float orc_get(const void *p, size_t i, int dtype) {
+  if (dtype == ORC_BF16) {
+    uint32_t b = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &b, sizeof f);
+    return f;
+  }
+  return ((const float *)p)[i];
+}
+
+/* Step 1: routed experts n = m N, kept experts k = m K - K_s. */
+int oracle_sizes(int N, int m, int K, int K_s, int *n, int *k) {
+  if (N < 1 || m < 1 || K < 1 || K_s < 0) return ORC_ERR_ARG;
+  *n = m * N;
+  *k = m * K - K_s;
+  if (*k < 1 || *k > *n) return ORC_ERR_ARG;
+  return ORC_OK;
+}
+
+/* Affinity logit u^T e_i, summed over j ascending. */
+static float orc_logit(const void *u, const void *cent, int64_t t, int i, int d, int dtype) {
+  float acc = 0.0f;
+  for (int j = 0; j < d; ++j)
+    acc += orc_get(u, (size_t)t * d + j, dtype) * orc_get(cent, (size_t)i * d + j, dtype);
+  return acc;
+}
+
+/*
+ * Routing for one token.  logit[n] in; s[n] = softmax, order[n] = expert
+ * indices sorted by descending logit, ties by ascending index (stable
+ * insertion sort; selection on the logit equals selection on s because the
+ * softmax is monotone).
+ */
+static void orc_route_token(const float *logit, int n, float *s, int *order) {
+  float mx = logit[0];
+  for (int i = 1; i < n; ++i)
+    if (logit[i] > mx) mx = logit[i];
+  float z = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    s[i] = expf(logit[i] - mx);
+    z += s[i];
+  }
+  for (int i = 0; i < n; ++i) s[i] = s[i] / z;
+  for (int i = 0; i < n; ++i) {
+    int p = i;
+    while (p > 0 && logit[order[p - 1]] < logit[i]) {
+      order[p] = order[p - 1];
+      --p;
+    }
+    order[p] = i;
+  }
+}
+
+/*
+ * Steps 2-6 over all T tokens.
+ *   u [T][d], cent [n][d]                    (dtype storage)
+ *   topk_idx [T][k], topk_gate [T][k]        kept experts in selection order
+ *   logits, scores [T][n]                    optional (NULL to skip)
+ *   counts [n]; f [n] = (count_i * n) / (k * T); P [n] = (sum_t s_ti) / T
+ */
+int oracle_route(int64_t T, int d, int n, int k, int dtype, const void *u, const void *cent,
+                 int32_t *topk_idx, float *topk_gate, float *logits, float *scores,
+                 int32_t *counts, float *f, float *P) {
+  if (T < 1 || d < 1 || n < 1 || k < 1 || k > n) return ORC_ERR_ARG;
+  float *s_all = scores;
+  float *own = NULL;
+  if (!s_all) {
+    own = (float *)malloc(sizeof(float) * (size_t)T * n);
+    if (!own) return ORC_ERR_MEM;
+    s_all = own;
+  }
+  int fail = 0;
+#pragma omp parallel
+  {
+    float *lg = (float *)malloc(sizeof(float) * n);
+    int *order = (int *)malloc(sizeof(int) * n);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      if (!lg || !order) {
+#pragma omp atomic write
+        fail = 1;
+        continue;
+      }
+      {
+        for (int i = 0; i < n; ++i) lg[i] = orc_logit(u, cent, t, i, d, dtype);
+        float *s = s_all + (size_t)t * n;
+        orc_route_token(lg, n, s, order);
+        for (int j = 0; j < k; ++j) {
+          topk_idx[(size_t)t * k + j] = order[j];
+          topk_gate[(size_t)t * k + j] = s[order[j]];
+        }
+        if (logits) memcpy(logits + (size_t)t * n, lg, sizeof(float) * n);
+      }
+    }
+    free(lg);
+    free(order);
+  }
+  if (fail) {
+    free(own);
+    return ORC_ERR_MEM;
+  }
+  for (int i = 0; i < n; ++i) counts[i] = 0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) counts[topk_idx[(size_t)t * k + j]] += 1;
+  for (int i = 0; i < n; ++i) {
+    f[i] = (float)((int64_t)counts[i] * n) / (float)((int64_t)k * T);
+    float acc = 0.0f;
+    for (int64_t t = 0; t < T; ++t) acc += s_all[(size_t)t * n + i];
+    P[i] = acc / (float)T;
+  }
+  free(own);
+  return ORC_OK;
+}
+
+/* L_ExpBal = alpha * sum_i f_i P_i (section "Expert-level balance loss"). */
+float oracle_balance_loss(int n, const float *f, const float *P, float alpha) {
+  float acc = 0.0f;
+  for (int i = 0; i < n; ++i) acc += f[i] * P[i];
+  return alpha * acc;
+}
+
+/*
+ * Grouping of (token, slot) pairs by expert: a stable counting sort, expert
+ * major and token ascending.  offsets [n+1]; perm_token [T*k] = token of each
+ * grouped row; slot_of [T][k] = grouped row of (t, j).
+ */
+int oracle_permute(int64_t T, int n, int k, const int32_t *topk_idx, int32_t *offsets,
+                   int32_t *perm_token, int32_t *slot_of) {
+  int32_t *cursor = (int32_t *)calloc((size_t)n + 1, sizeof(int32_t));
+  if (!cursor) return ORC_ERR_MEM;
+  for (int64_t r = 0; r < T * k; ++r) {
+    int e = topk_idx[r];
+    if (e < 0 || e >= n) {
+      free(cursor);
+      return ORC_ERR_ARG;
+    }
+    cursor[e + 1] += 1;
+  }
+  for (int e = 0; e < n; ++e) cursor[e + 1] += cursor[e];
+  memcpy(offsets, cursor, sizeof(int32_t) * ((size_t)n + 1));
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      int e = topk_idx[(size_t)t * k + j];
+      int32_t pos = cursor[e]++;
+      perm_token[pos] = (int32_t)t;
+      slot_of[(size_t)t * k + j] = pos;
+    }
+  free(cursor);
+  return ORC_OK;
+}
+
+static float orc_silu(float z) { return z / (1.0f + expf(-z)); }
+
+/*
+ * One SwiGLU expert on one fp32 vector x [d]:
+ *   a = W1 x, b = W3 x (W1, W3 rows of length d, row stride ldw13),
+ *   hid = SiLU(a) * b,
+ *   y = W2 hid (W2 rows of length d_ff, row stride ldw2).
+ * Weights are read from dtype storage starting at element offsets o13 / o2.
+ * hid is scratch of d_ff floats; y [d] is overwritten.
+ */
+static void orc_swiglu(int d, int d_ff, const float *x, const void *w1, const void *w3,
+                       size_t o13, size_t ldw13, const void *w2, size_t o2, size_t ldw2,
+                       int dtype, float *hid, float *y) {
+  for (int c = 0; c < d_ff; ++c) {
+    float a = 0.0f, b = 0.0f;
+    for (int j = 0; j < d; ++j) {
+      a += orc_get(w1, o13 + (size_t)c * ldw13 + j, dtype) * x[j];
+      b += orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * x[j];
+    }
+    hid[c] = orc_silu(a) * b;
+  }
+  for (int i = 0; i < d; ++i) {
+    float acc = 0.0f;
+    for (int c = 0; c < d_ff; ++c) acc += orc_get(w2, o2 + (size_t)i * ldw2 + c, dtype) * hid[c];
+    y[i] = acc;
+  }
+}
+
+/*
+ * Routed expert e on x: w1, w3 [n][d_ff][d], w2 [n][d][d_ff].
+ */
+int oracle_expert(int d, int d_ff, int e, int dtype, const float *x, const void *w1,
+                  const void *w3, const void *w2, float *y) {
+  float *hid = (float *)malloc(sizeof(float) * (size_t)d_ff);
+  if (!hid) return ORC_ERR_MEM;
+  orc_swiglu(d, d_ff, x, w1, w3, (size_t)e * d_ff * d, (size_t)d, w2, (size_t)e * d * d_ff,
+             (size_t)d_ff, dtype, hid, y);
+  free(hid);
+  return ORC_OK;
+}
+
+/*
+ * Whole layer for a list of tokens (all T tokens are routed, since counts and
+ * P need the full batch; the expert sums are formed only for the listed ones).
+ *
+ * Inputs (dtype storage): u [T][d], cent [n][d], routed w1, w3 [n][d_ff][d],
+ * w2 [n][d][d_ff]; shared ws1, ws3 [K_s*d_ff][d], ws2 [d][K_s*d_ff] where
+ * shared expert q owns rows (resp. columns) q*d_ff .. q*d_ff + d_ff - 1; the
+ * shared expert sum is formed expert by expert.
+ * toks [nt]: token indices (NULL: all T tokens in order, nt = T).
+ * Outputs (all fp32, rows in toks order; any may be NULL except the routing
+ * ones): topk_idx, topk_gate [T][k], counts, f, P [n];
+ *   Y [nt][k][d]  ungated routed expert outputs per slot,
+ *   S [nt][d]     shared expert sum,
+ *   ysum [nt][d]  sum_j g_j Y_j + S,
+ *   h [nt][d]     ysum + u.
+ */
+int oracle_layer(int64_t T, int d, int N, int m, int K, int K_s, int d_ff, int dtype,
+                 const void *u, const void *cent, const void *w1, const void *w3,
+                 const void *w2, const void *ws1, const void *ws3, const void *ws2,
+                 const int64_t *toks, int64_t nt, int32_t *topk_idx, float *topk_gate,
+                 int32_t *counts, float *f, float *P, float *Y, float *S, float *ysum,
+                 float *h) {
+  int n, k;
+  if (oracle_sizes(N, m, K, K_s, &n, &k) != ORC_OK) return ORC_ERR_ARG;
+  if (d < 1 || d_ff < 1 || (K_s > 0 && (!ws1 || !ws3 || !ws2))) return ORC_ERR_ARG;
+  if (!toks) nt = T;
+  int rc = oracle_route(T, d, n, k, dtype, u, cent, topk_idx, topk_gate, NULL, NULL, counts,
+                        f, P);
+  if (rc != ORC_OK) return rc;
+  const size_t ldws2 = (size_t)K_s * d_ff;
+  int fail = 0;
+#pragma omp parallel
+  {
+    float *x = (float *)malloc(sizeof(float) * (size_t)d);
+    float *hid = (float *)malloc(sizeof(float) * (size_t)d_ff);
+    float *yk = (float *)malloc(sizeof(float) * (size_t)k * d);
+    float *sh = (float *)malloc(sizeof(float) * (size_t)d);
+    float *tmp = (float *)malloc(sizeof(float) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nt; ++r) {
+      if (!x || !hid || !yk || !sh || !tmp) {
+#pragma omp atomic write
+        fail = 1;
+        continue;
+      }
+      {
+        int64_t t = toks ? toks[r] : r;
+        for (int j = 0; j < d; ++j) x[j] = orc_get(u, (size_t)t * d + j, dtype);
+        /* routed experts, ungated, in selection order */
+        for (int j = 0; j < k; ++j) {
+          int e = topk_idx[(size_t)t * k + j];
+          orc_swiglu(d, d_ff, x, w1, w3, (size_t)e * d_ff * d, (size_t)d, w2,
+                     (size_t)e * d * d_ff, (size_t)d_ff, dtype, hid, yk + (size_t)j * d);
+        }
+        /* shared experts, always on, weight one */
+        for (int i = 0; i < d; ++i) sh[i] = 0.0f;
+        for (int q = 0; q < K_s; ++q) {
+          orc_swiglu(d, d_ff, x, ws1, ws3, (size_t)q * d_ff * d, (size_t)d, ws2,
+                     (size_t)q * d_ff, ldws2, dtype, hid, tmp);
+          for (int i = 0; i < d; ++i) sh[i] += tmp[i];
+        }
+        /* h = sum_j g_j FFN_j(u) + shared + u */
+        for (int i = 0; i < d; ++i) {
+          float acc = 0.0f;
+          for (int j = 0; j < k; ++j) acc += topk_gate[(size_t)t * k + j] * yk[(size_t)j * d + i];
+          acc += sh[i];
+          if (ysum) ysum[(size_t)r * d + i] = acc;
+          if (h) h[(size_t)r * d + i] = acc + x[i];
+          if (S) S[(size_t)r * d + i] = sh[i];
+        }
+        if (Y) memcpy(Y + (size_t)r * k * d, yk, sizeof(float) * (size_t)k * d);
+      }
+    }
+    free(x);
+    free(hid);
+    free(yk);
+    free(sh);
+    free(tmp);
+  }
+  return fail ? ORC_ERR_MEM : ORC_OK;
+}

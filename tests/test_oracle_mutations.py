@@ -1,0 +1,54 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source, builds it on
+the CPU, and runs the pin suite against it: the suite has to fail.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+MUTATIONS = {
+    "silu_on_w3_branch": ("hid[c] = orc_silu(a) * b;", "hid[c] = a * orc_silu(b);"),
+    "no_residual": ("h[(size_t)r * d + i] = acc + x[i];", "h[(size_t)r * d + i] = acc;"),
+    "ties_to_higher_index": ("logit[order[p - 1]] < logit[i]", "logit[order[p - 1]] <= logit[i]"),
+    "select_smallest": ("logit[order[p - 1]] < logit[i]", "logit[order[p - 1]] > logit[i]"),
+    "no_max_subtraction": ("s[i] = expf(logit[i] - mx);", "s[i] = expf(logit[i]);"),
+    "renormalised_gates": ("topk_gate[(size_t)t * k + j] = s[order[j]];",
+                           "topk_gate[(size_t)t * k + j] = s[order[j]] * (float)n / (float)k;"),
+    "w2_transposed": ("orc_get(w2, o2 + (size_t)i * ldw2 + c, dtype)",
+                      "orc_get(w2, o2 + (size_t)c * d + i, dtype)"),
+    "shared_dropped": ("acc += sh[i];", "acc += 0.0f;"),
+    "P_unnormalised": ("P[i] = acc / (float)T;", "P[i] = acc;"),
+    "f_is_plain_fraction": ("f[i] = (float)((int64_t)counts[i] * n) / (float)((int64_t)k * T);",
+                            "f[i] = (float)counts[i] / (float)T;"),
+    "k_without_shared": ("*k = m * K - K_s;", "*k = m * K;"),
+    "unstable_permute": ("int32_t pos = cursor[e]++;",
+                         "int32_t pos = cursor[e + 1] - 1 - (cursor[e]++ - offsets[e]);"),
+    "shared_slice_stride": ("(size_t)q * d_ff, ldws2, dtype, hid, tmp);",
+                            "(size_t)q * d_ff * d, ldws2, dtype, hid, tmp);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-fopenmp", "-ffp-contract=off",
+                    "-shared", "-o", str(lib), str(mut), "-lm"], check=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
