@@ -1,0 +1,172 @@
+/*
+ * moe.h -- C ABI of the DeepSeekMoE layer forward on one AMD MI355X (gfx950).
+ *
+ * The layer (DeepSeekMoE explainer, deepforge.srivtx.xyz "DeepSeekMoE",
+ * sections "Routing in a classic MoE layer", "Expert-level balance loss" and
+ * "What the 16B configuration looks like"):
+ *
+ *   s_i = softmax_i(u^T e_i)   over the n = m*N routed (fine-grained) experts
+ *   g_i = s_i if s_i is among the k = m*K - K_s largest, else 0
+ *         (no renormalisation: the kept gates do not sum to one)
+ *   h   = sum_i g_i FFN_i(u) + sum_{q < K_s} FFN^shared_q(u) + u
+ *
+ * with FFN(x) = W2 (SiLU(W1 x) * (W3 x)) (SwiGLU, no biases), K_s shared
+ * experts that every token uses with weight one, and the expert-level
+ * balance statistics f_i = n/(k T) * count_i and P_i = (1/T) sum_t s_{t,i}.
+ *
+ * Conventions for every entry point:
+ *   - Buffers are DEVICE pointers owned by the caller; the library never
+ *     allocates.  Scratch space comes from the caller's workspace `ws` of
+ *     `ws_bytes` bytes (see moe_workspace_bytes).
+ *   - Every pointer must be 16-byte aligned; tensors are dense row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; no call synchronises the device or copies
+ *     data to the host.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     any error nothing is launched and the status says why.  Errors raised
+ *     by the HIP runtime at launch map to MOE_ERR_HIP.
+ *   - Element type: MOE_BF16 (bf16 storage, fp32 accumulation) or MOE_F32.
+ *     u, h, centroids, weights, x_perm and y use the problem's dtype; gates,
+ *     f and P are fp32; indices and counts are int32.
+ *   - Inputs must be finite; results are unspecified otherwise.
+ *   - Calls on different streams that share a workspace race.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* sizes out of range (see moe_problem) */
+  MOE_ERR_DTYPE = 3,       /* unknown element type */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 5,   /* ws is NULL or ws_bytes is too small */
+  MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not handle */
+  MOE_ERR_HIP = 7          /* the HIP runtime reported an error */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+#define MOE_MAX_EXPERTS 256 /* n = m*N */
+#define MOE_MAX_TOPK 64     /* k = m*K - K_s */
+
+/*
+ * The pages' statement of the problem.  Valid when
+ *   T >= 1, T*k < 2^31;  d, d_ff >= 32 and multiples of 32;
+ *   N, m, K >= 1;  K_s >= 0;  n = m*N <= MOE_MAX_EXPERTS;
+ *   1 <= k = m*K - K_s <= min(n, MOE_MAX_TOPK).
+ * Only the products m*N and m*K enter the result.
+ */
+typedef struct moe_problem {
+  int64_t T;     /* tokens */
+  int32_t d;     /* hidden size */
+  int32_t N;     /* experts before fine-grained segmentation */
+  int32_t m;     /* segmentation factor */
+  int32_t K;     /* activated experts before segmentation */
+  int32_t K_s;   /* shared (always-on) experts */
+  int32_t d_ff;  /* SwiGLU intermediate size of one fine-grained expert */
+  int32_t dtype; /* moe_dtype */
+} moe_problem;
+
+/* moe_layer_fwd flags (component checks). */
+enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2 };
+
+/* Bytes of workspace that suffice for every entry point on this problem;
+ * 0 when the problem is invalid. */
+size_t moe_workspace_bytes(const moe_problem *p);
+
+/*
+ * Router ("Routing in a classic MoE layer" and "Top-k routing, from
+ * affinities to gates"; statistics from "Expert-level balance loss").
+ *   u [T][d], centroids [n][d]                        in
+ *   topk_idx [T][k]   kept experts, descending logit u^T e_i, equal logits
+ *                     in ascending expert index (the sketch's stable sort)
+ *   topk_gate [T][k]  s of the kept experts (fp32)
+ *   counts [n]        tokens that kept expert i
+ *   f [n]             (float)(count_i * n) / (float)(k * T)
+ *   P [n]             mean over tokens of s_i (fp32)
+ * Logits are accumulated in fp32; selection is made on the fp32 logits.
+ */
+moe_status moe_route(const moe_problem *p, const void *u, const void *centroids,
+                     int32_t *topk_idx, float *topk_gate, int32_t *counts, float *f, float *P,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Grouping of the T*k (token, slot) pairs by expert (the page's note that a
+ * production layer groups tokens per expert), expert-major with ascending
+ * token inside each expert (a stable counting sort).
+ *   u [T][d], topk_idx [T][k]                         in
+ *   offsets [n+1]     first grouped row of each expert, offsets[n] = T*k
+ *   perm_token [T*k]  token of each grouped row
+ *   slot_of [T][k]    grouped row of (t, j)
+ *   x_perm [T*k][d]   row r = u[perm_token[r]]; may be NULL (indices only)
+ */
+moe_status moe_permute(const moe_problem *p, const void *u, const int32_t *topk_idx,
+                       int32_t *offsets, int32_t *perm_token, int32_t *slot_of, void *x_perm,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Grouped SwiGLU FFN: rows offsets[g] .. offsets[g+1]-1 of x go through
+ * expert g: y = W2_g (SiLU(W1_g x) * (W3_g x)).  The intermediate is rounded
+ * to the dtype (bf16) between the two products; accumulation is fp32.
+ *   n_groups          1 .. MOE_MAX_EXPERTS
+ *   rows              total rows (= offsets[n_groups] - offsets[0]); offsets
+ *                     must be non-decreasing with offsets[0] = 0
+ *   offsets [n_groups+1] (device)
+ *   x [rows][d]; w1, w3 [n_groups][d_ff_group][d]; w2 [n_groups][d][d_ff_group]
+ *   y [rows][d]       out
+ * Routed experts: n_groups = n, rows = T*k, d_ff_group = d_ff.  Shared
+ * experts as one dense SwiGLU (their sum): n_groups = 1, rows = T,
+ * d_ff_group = K_s*d_ff, offsets = {0, T}.
+ * d_ff_group must be a multiple of 32 with rows*d_ff_group fitting the
+ * workspace of moe_workspace_bytes(p).
+ */
+moe_status moe_grouped_ffn(const moe_problem *p, int32_t n_groups, int64_t rows,
+                           const int32_t *offsets, const void *x, const void *w1,
+                           const void *w3, const void *w2, int32_t d_ff_group, void *y,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Gate-weighted combine with residual ("Routing in a classic MoE layer"):
+ *   h[t] = residual[t] + shared_out[t] + sum_j topk_gate[t][j] * y_perm[slot_of[t][j]]
+ * summed in fp32 (j ascending, then shared, then residual), rounded once.
+ * residual and shared_out may be NULL (term omitted).
+ *   y_perm [T*k][d], slot_of [T][k], topk_gate [T][k], h [T][d]
+ */
+moe_status moe_combine(const moe_problem *p, const void *residual, const void *shared_out,
+                       const void *y_perm, const int32_t *slot_of, const float *topk_gate,
+                       void *h, void *stream);
+
+/*
+ * The whole layer: route, group, routed experts, shared experts, combine.
+ *   u [T][d], centroids [n][d]
+ *   w1, w3 [n][d_ff][d], w2 [n][d][d_ff]              routed experts
+ *   ws1, ws3 [K_s*d_ff][d], ws2 [d][K_s*d_ff]         shared experts (expert q
+ *                     owns rows / columns q*d_ff .. q*d_ff + d_ff - 1); NULL
+ *                     allowed when K_s = 0 or flags has MOE_NO_SHARED
+ *   h [T][d]          out
+ *   topk_idx, topk_gate, counts, f, P                 out, as moe_route
+ *   flags             MOE_NO_RESIDUAL drops +u, MOE_NO_SHARED drops the shared
+ *                     experts (component checks only)
+ */
+moe_status moe_layer_fwd(const moe_problem *p, const void *u, const void *centroids,
+                         const void *w1, const void *w3, const void *w2, const void *ws1,
+                         const void *ws3, const void *ws2, void *h, int32_t *topk_idx,
+                         float *topk_gate, int32_t *counts, float *f, float *P, int flags,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

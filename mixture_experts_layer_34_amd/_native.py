@@ -1,0 +1,144 @@
+"""ctypes binding of libmoe.so (include/moe.h): argument marshalling only.
+
+Every function has the name and argument order of the C entry point.  Tensor
+arguments may be torch tensors (their data_ptr is passed), plain integers
+(device addresses) or None (NULL).  A non-OK status raises MoeError.  The
+library must be built (mixture_experts_layer_34_amd.build); there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
+                4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_UNSUPPORTED",
+                7: "MOE_ERR_HIP"}
+MOE_F32, MOE_BF16 = 0, 1
+MOE_NO_RESIDUAL, MOE_NO_SHARED = 1, 2
+MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 64
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("K", ctypes.c_int32), ("K_s", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def problem(T, d, N, m, K, K_s, d_ff, dtype) -> moe_problem:
+    if isinstance(dtype, str):
+        dtype = {"f32": MOE_F32, "bf16": MOE_BF16}[dtype]
+    return moe_problem(T, d, N, m, K, K_s, d_ff, dtype)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run `python -m mixture_experts_layer_34_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, PP = ctypes.c_void_p, ctypes.POINTER(moe_problem)
+    sz, i32, i64, st = ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+    lib.moe_workspace_bytes.argtypes = [PP]
+    lib.moe_workspace_bytes.restype = sz
+    lib.moe_status_str.argtypes = [st]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_route.argtypes = [PP, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_route.restype = st
+    lib.moe_permute.argtypes = [PP, P, P, P, P, P, P, P, sz, P]
+    lib.moe_permute.restype = st
+    lib.moe_grouped_ffn.argtypes = [PP, i32, i64, P, P, P, P, P, i32, P, P, sz, P]
+    lib.moe_grouped_ffn.restype = st
+    lib.moe_combine.argtypes = [PP, P, P, P, P, P, P, P]
+    lib.moe_combine.restype = st
+    lib.moe_layer_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int,
+                                  P, sz, P]
+    lib.moe_layer_fwd.restype = st
+    return lib
+
+
+lib = _load()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _nbytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return ws_bytes
+    if ws is None or isinstance(ws, int):
+        return 0
+    return ws.numel() * ws.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status, lib.moe_status_str(status).decode())
+
+
+def moe_status_str(status: int) -> str:
+    return lib.moe_status_str(status).decode()
+
+
+def moe_workspace_bytes(p: moe_problem) -> int:
+    return int(lib.moe_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_route(p, u, centroids, topk_idx, topk_gate, counts, f, P, ws, ws_bytes=None,
+              stream=None):
+    _check("moe_route", lib.moe_route(
+        ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(topk_idx), _ptr(topk_gate),
+        _ptr(counts), _ptr(f), _ptr(P), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_permute(p, u, topk_idx, offsets, perm_token, slot_of, x_perm, ws, ws_bytes=None,
+                stream=None):
+    _check("moe_permute", lib.moe_permute(
+        ctypes.byref(p), _ptr(u), _ptr(topk_idx), _ptr(offsets), _ptr(perm_token),
+        _ptr(slot_of), _ptr(x_perm), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_grouped_ffn(p, n_groups, rows, offsets, x, w1, w3, w2, d_ff_group, y, ws,
+                    ws_bytes=None, stream=None):
+    _check("moe_grouped_ffn", lib.moe_grouped_ffn(
+        ctypes.byref(p), n_groups, rows, _ptr(offsets), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2),
+        d_ff_group, _ptr(y), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_combine(p, residual, shared_out, y_perm, slot_of, topk_gate, h, stream=None):
+    _check("moe_combine", lib.moe_combine(
+        ctypes.byref(p), _ptr(residual), _ptr(shared_out), _ptr(y_perm), _ptr(slot_of),
+        _ptr(topk_gate), _ptr(h), _stream(stream)))
+
+
+def moe_layer_fwd(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate, counts,
+                  f, P, flags, ws, ws_bytes=None, stream=None):
+    _check("moe_layer_fwd", lib.moe_layer_fwd(
+        ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
+        _ptr(ws3), _ptr(ws2), _ptr(h), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(f),
+        _ptr(P), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))

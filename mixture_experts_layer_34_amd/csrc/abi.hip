@@ -1,0 +1,314 @@
+// C ABI of the MoE layer: argument validation, workspace carving and the
+// launch sequence.  Every check runs on the host before any HIP call, so a
+// rejected call enqueues nothing.
+#include "../../include/moe.h"
+#include "kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace {
+
+using moe::kRouteTok;
+using moe::kTileM;
+
+struct Dims {
+  int64_t T;
+  int d, d_ff, n, k, K_s, esize;
+};
+
+moe_status check_problem(const moe_problem* p, Dims* out) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (p->T < 1 || p->d < 32 || p->d % 32 != 0 || p->d_ff < 32 || p->d_ff % 32 != 0)
+    return MOE_ERR_SHAPE;
+  if (p->N < 1 || p->m < 1 || p->K < 1 || p->K_s < 0) return MOE_ERR_SHAPE;
+  const int64_t n = (int64_t)p->m * p->N;
+  const int64_t k = (int64_t)p->m * p->K - p->K_s;
+  if (n > MOE_MAX_EXPERTS || k < 1 || k > n || k > MOE_MAX_TOPK) return MOE_ERR_SHAPE;
+  if (p->T * k >= (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if ((int64_t)p->K_s * p->d_ff > INT32_MAX / 2) return MOE_ERR_SHAPE;
+  out->T = p->T;
+  out->d = p->d;
+  out->d_ff = p->d_ff;
+  out->n = (int)n;
+  out->k = (int)k;
+  out->K_s = p->K_s;
+  out->esize = p->dtype == MOE_BF16 ? 2 : 4;
+  return MOE_OK;
+}
+
+bool aligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Workspace regions, each 256-byte aligned.
+struct Layout {
+  size_t blk_cnt, blk_P, blk_base, lrank, offsets, perm_token, slot_of;
+  size_t t_row0, t_rows, t_off, t_count;
+  size_t hbuf, ybuf, hsbuf, sbuf;
+  size_t total;
+  int max_tiles;
+  size_t hcap;  // elements of hbuf
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout layout(const Dims& d) {
+  Layout L{};
+  const size_t B = (size_t)((d.T + kRouteTok - 1) / kRouteTok);
+  const size_t R = (size_t)d.T * d.k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  L.blk_cnt = take(B * d.n * 4);
+  L.blk_P = take(B * d.n * 4);
+  L.blk_base = take(B * d.n * 4);
+  L.lrank = take(R * 4);
+  L.offsets = take((size_t)(d.n + 1) * 4);
+  L.perm_token = take(R * 4);
+  L.slot_of = take(R * 4);
+  L.max_tiles = (int)(R / kTileM) + MOE_MAX_EXPERTS;
+  L.t_row0 = take((size_t)L.max_tiles * 4);
+  L.t_rows = take((size_t)L.max_tiles * 4);
+  L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
+  L.t_count = take(4);
+  const size_t hs_el = (size_t)d.T * d.K_s * d.d_ff;
+  L.hcap = R * d.d_ff > hs_el ? R * d.d_ff : hs_el;
+  L.hbuf = take(L.hcap * d.esize);
+  L.ybuf = take(R * d.d * d.esize);
+  L.hsbuf = take(hs_el * d.esize);
+  L.sbuf = take((size_t)d.T * d.d * d.esize);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe::TileList tiles_of(void* ws, const Layout& L) {
+  return moe::TileList{at<int32_t>(ws, L.t_row0), at<int32_t>(ws, L.t_rows),
+                       at<int32_t>(ws, L.t_off), at<int32_t>(ws, L.t_count), L.max_tiles};
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                  \
+  do {                                                 \
+    const moe_status st_ = hip_status(expr);           \
+    if (st_ != MOE_OK) return st_;                     \
+  } while (0)
+
+moe_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_problem* p) {
+  Dims d;
+  if (check_problem(p, &d) != MOE_OK) return 0;
+  return layout(d).total;
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "problem sizes out of range";
+    case MOE_ERR_DTYPE: return "unknown element type";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_route(const moe_problem* p, const void* u, const void* centroids,
+                     int32_t* topk_idx, float* topk_gate, int32_t* counts, float* f, float* P,
+                     void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!u || !centroids || !topk_idx || !topk_gate || !counts || !f || !P) return MOE_ERR_NULL;
+  if (!aligned(u) || !aligned(centroids) || !aligned(topk_idx) || !aligned(topk_gate) ||
+      !aligned(counts) || !aligned(f) || !aligned(P))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
+                            at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
+                            at<int32_t>(ws, L.lrank), s));
+  MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
+                           counts, f, P, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.blk_base),
+                           nullptr, s));
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_problem* p, const void* u, const int32_t* topk_idx,
+                       int32_t* offsets, int32_t* perm_token, int32_t* slot_of, void* x_perm,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !offsets || !perm_token || !slot_of || (x_perm && !u)) return MOE_ERR_NULL;
+  if (!aligned(topk_idx) || !aligned(offsets) || !aligned(perm_token) || !aligned(slot_of) ||
+      (x_perm && (!aligned(x_perm) || !aligned(u))))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(moe::launch_hist(topk_idx, d.T, d.n, d.k, at<int32_t>(ws, L.blk_cnt),
+                           at<int32_t>(ws, L.lrank), s));
+  MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), nullptr, d.T, d.n, d.k, nullptr, nullptr,
+                           nullptr, offsets, at<int32_t>(ws, L.blk_base), nullptr, s));
+  MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
+                              d.T, d.n, d.k, perm_token, slot_of, u, x_perm, d.d * d.esize, s));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const moe_problem* p, int32_t n_groups, int64_t rows,
+                           const int32_t* offsets, const void* x, const void* w1,
+                           const void* w3, const void* w2, int32_t d_ff_group, void* y,
+                           void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (n_groups < 1 || n_groups > MOE_MAX_EXPERTS || rows < 1 || d_ff_group < 32 ||
+      d_ff_group % 32 != 0)
+    return MOE_ERR_SHAPE;
+  if (!offsets || !x || !w1 || !w3 || !w2 || !y) return MOE_ERR_NULL;
+  if (!aligned(offsets) || !aligned(x) || !aligned(w1) || !aligned(w3) || !aligned(w2) ||
+      !aligned(y))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  if (rows > d.T * d.k || (size_t)rows * d_ff_group > L.hcap) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::TileList tl = tiles_of(ws, L);
+  if (p->dtype == MOE_BF16) MOE_TRY(moe::launch_tiles(offsets, n_groups, rows, tl, s));
+  moe::FfnArgs a{};
+  a.dtype = p->dtype;
+  a.x = x;
+  a.x_rows = nullptr;
+  a.ldx = d.d;
+  a.w1 = w1;
+  a.w3 = w3;
+  a.w2 = w2;
+  a.n_groups = n_groups;
+  a.d = d.d;
+  a.d_ff_g = d_ff_group;
+  a.rows = rows;
+  a.offsets = offsets;
+  a.tiles = &tl;
+  a.hbuf = at<char>(ws, L.hbuf);
+  a.y = y;
+  MOE_TRY(moe::launch_grouped_ffn(a, s));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_problem* p, const void* residual, const void* shared_out,
+                       const void* y_perm, const int32_t* slot_of, const float* topk_gate,
+                       void* h, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !slot_of || !topk_gate || !h) return MOE_ERR_NULL;
+  if (!aligned(y_perm) || !aligned(slot_of) || !aligned(topk_gate) || !aligned(h) ||
+      (residual && !aligned(residual)) || (shared_out && !aligned(shared_out)))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(moe::launch_combine(p->dtype, residual, shared_out, y_perm, slot_of, topk_gate, h, d.T,
+                              d.d, d.k, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centroids,
+                         const void* w1, const void* w3, const void* w2, const void* ws1,
+                         const void* ws3, const void* ws2, void* h, int32_t* topk_idx,
+                         float* topk_gate, int32_t* counts, float* f, float* P, int flags,
+                         void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED)) return MOE_ERR_SHAPE;
+  const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
+  if (!u || !centroids || !w1 || !w3 || !w2 || !h || !topk_idx || !topk_gate || !counts || !f ||
+      !P)
+    return MOE_ERR_NULL;
+  if (shared && (!ws1 || !ws3 || !ws2)) return MOE_ERR_NULL;
+  if (!aligned(u) || !aligned(centroids) || !aligned(w1) || !aligned(w3) || !aligned(w2) ||
+      !aligned(h) || !aligned(topk_idx) || !aligned(topk_gate) || !aligned(counts) ||
+      !aligned(f) || !aligned(P))
+    return MOE_ERR_ALIGN;
+  if (shared && (!aligned(ws1) || !aligned(ws3) || !aligned(ws2))) return MOE_ERR_ALIGN;
+  const Layout L = layout(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::TileList tl = tiles_of(ws, L);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm_token = at<int32_t>(ws, L.perm_token);
+  int32_t* slot_of = at<int32_t>(ws, L.slot_of);
+
+  MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
+                            at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
+                            at<int32_t>(ws, L.lrank), s));
+  MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
+                           counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+  MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
+                              d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
+  // routed experts: rows gathered from u through perm_token
+  moe::FfnArgs a{};
+  a.dtype = p->dtype;
+  a.x = u;
+  a.x_rows = perm_token;
+  a.ldx = d.d;
+  a.w1 = w1;
+  a.w3 = w3;
+  a.w2 = w2;
+  a.n_groups = d.n;
+  a.d = d.d;
+  a.d_ff_g = d.d_ff;
+  a.rows = d.T * d.k;
+  a.offsets = offsets;
+  a.tiles = &tl;
+  a.hbuf = at<char>(ws, L.hbuf);
+  a.y = at<char>(ws, L.ybuf);
+  MOE_TRY(moe::launch_grouped_ffn(a, s));
+  // shared experts: one dense SwiGLU of width K_s*d_ff over all tokens
+  void* sbuf = nullptr;
+  if (shared) {
+    moe::FfnArgs b{};
+    b.dtype = p->dtype;
+    b.x = u;
+    b.x_rows = nullptr;
+    b.ldx = d.d;
+    b.w1 = ws1;
+    b.w3 = ws3;
+    b.w2 = ws2;
+    b.n_groups = 1;
+    b.d = d.d;
+    b.d_ff_g = d.K_s * d.d_ff;
+    b.rows = d.T;
+    b.offsets = nullptr;
+    b.tiles = nullptr;
+    b.hbuf = at<char>(ws, L.hsbuf);
+    b.y = at<char>(ws, L.sbuf);
+    MOE_TRY(moe::launch_grouped_ffn(b, s));
+    sbuf = b.y;
+  }
+  MOE_TRY(moe::launch_combine(p->dtype, (flags & MOE_NO_RESIDUAL) ? nullptr : u, sbuf,
+                              at<char>(ws, L.ybuf), slot_of, topk_gate, h, d.T, d.d, d.k, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// bf16 storage is handled as raw 16-bit patterns.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Element type traits: storage type and its conversion to fp32.
+template <int DT> struct Elem;
+template <> struct Elem<0> {  // fp32
+  typedef float T;
+  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ float cvt(float x) { return x; }
+  static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<1> {  // bf16 bits
+  typedef uint16_t T;
+  static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Map a linear workgroup id to a logical tile so that each XCD (workgroups
+// are dealt round-robin over the 8 XCDs) processes one contiguous range of
+// logical tiles: neighbouring tiles then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+  constexpr int kXcd = 8;
+  const int q = G / kXcd, r = G % kXcd;
+  const int x = w % kXcd, i = w / kXcd;
+  return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace moe

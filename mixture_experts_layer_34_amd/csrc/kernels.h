@@ -1,0 +1,70 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouteTok = 64;   // tokens per route block: one wave ballot covers them
+constexpr int kTileM = 128;     // rows per grouped-GEMM M-tile
+constexpr int kMaxExperts = 256;
+
+// Device tile list of a grouped problem (built by the scan / tile kernels).
+struct TileList {
+  int32_t* row0;    // [max_tiles] first grouped row of each M-tile
+  int32_t* rows;    // [max_tiles] rows in the tile (1..kTileM)
+  int32_t* off;     // [n_groups+1] first M-tile of each group
+  int32_t* count;   // [1] number of M-tiles
+  int max_tiles;    // capacity (host bound)
+};
+
+// Router: logits, softmax, top-k, per-block P partial sums, per-block
+// histogram and per-(token, slot) rank inside its block.
+hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, int d, int n,
+                        int k, int32_t* topk_idx, float* topk_gate, int32_t* blk_cnt,
+                        float* blk_P, int32_t* lrank, hipStream_t s);
+
+// Histogram and ranks from a given topk_idx (standalone grouping).
+hipError_t launch_hist(const int32_t* topk_idx, int64_t T, int n, int k, int32_t* blk_cnt,
+                       int32_t* lrank, hipStream_t s);
+
+// Column scan of the block histograms: counts, f, P (when blk_P), offsets,
+// per-block bases, and the M-tile list (when tiles != nullptr).
+hipError_t launch_scan(const int32_t* blk_cnt, const float* blk_P, int64_t T, int n, int k,
+                       int32_t* counts, float* f, float* P, int32_t* offsets,
+                       int32_t* blk_base, const TileList* tiles, hipStream_t s);
+
+// Scatter to grouped order (+ optional row gather of u into x_perm).
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank,
+                          const int32_t* blk_base, int64_t T, int n, int k,
+                          int32_t* perm_token, int32_t* slot_of, const void* u, void* x_perm,
+                          int row_bytes, hipStream_t s);
+
+// M-tile list from device offsets (standalone grouped FFN).
+hipError_t launch_tiles(const int32_t* offsets, int n_groups, int64_t rows,
+                        const TileList& tiles, hipStream_t s);
+
+struct FfnArgs {
+  int dtype;
+  const void* x;           // activations
+  const int32_t* x_rows;   // nullable: source row of x for each grouped row
+  int64_t ldx;             // row stride of x (elements)
+  const void* w1;          // [G][d_ff_g][d]
+  const void* w3;
+  const void* w2;          // [G][d][d_ff_g]
+  int n_groups;
+  int d;
+  int d_ff_g;
+  int64_t rows;            // total grouped rows
+  const int32_t* offsets;  // [G+1] device (fp32 path and tile-less launches use it)
+  const TileList* tiles;   // nullptr: single group of `rows` rows
+  void* hbuf;              // [rows][d_ff_g] intermediate
+  void* y;                 // [rows][d]
+};
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(int dtype, const void* residual, const void* shared_out,
+                          const void* y_perm, const int32_t* slot_of, const float* gate,
+                          void* h, int64_t T, int d, int k, hipStream_t s);
+
+}  // namespace moe

@@ -45,6 +45,7 @@ def _load():
     lib.oracle_balance_loss.restype = ctypes.c_float
     lib.oracle_permute.argtypes = [i64, i32, i32, P, P, P, P]
     lib.oracle_expert.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_combine.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_layer.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32,
                                  P, P, P, P, P, P, P, P, P, i64,
                                  P, P, P, P, P, P, P, P, P]
@@ -160,3 +161,22 @@ def layer(inp: dict, N: int, m: int, K: int, K_s: int, toks=None) -> dict:
     if rc != 0:
         raise RuntimeError(f"oracle_layer failed ({rc})")
     return out
+
+
+def combine(y_perm: np.ndarray, slot_of: np.ndarray, gate: np.ndarray, shared=None,
+            residual=None) -> np.ndarray:
+    """h = sum_j gate * y_perm[slot_of] + shared + residual (fp32 result)."""
+    y_perm = _c(y_perm)
+    slot_of = np.ascontiguousarray(slot_of, np.int32)
+    gate = np.ascontiguousarray(gate, np.float32)
+    T, k = slot_of.shape
+    d = y_perm.shape[1]
+    dt = _dt(y_perm)
+    for a in (shared, residual):
+        assert a is None or (_dt(a) == dt and a.shape == (T, d))
+    h = np.empty((T, d), np.float32)
+    rc = _load().oracle_combine(T, d, k, dt, _p(_c(residual)), _p(_c(shared)), _p(y_perm),
+                                _p(slot_of), _p(gate), _p(h))
+    if rc != 0:
+        raise RuntimeError(f"oracle_combine failed ({rc})")
+    return h

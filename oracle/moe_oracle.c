@@ -315,3 +315,26 @@ int oracle_layer(int64_t T, int d, int N, int m, int K, int K_s, int d_ff, int d
   }
   return fail ? ORC_ERR_MEM : ORC_OK;
 }
+
+/*
+ * Combine alone (section "Routing in a classic MoE layer"):
+ *   h[t] = sum_j gate[t][j] * y_perm[slot_of[t][j]] + shared[t] + residual[t]
+ * summed in fp32 (j ascending, then shared, then residual).  residual and
+ * shared may be NULL.  y_perm [T*k][d] and the others in dtype storage; h fp32.
+ */
+int oracle_combine(int64_t T, int d, int k, int dtype, const void *residual, const void *shared,
+                   const void *y_perm, const int32_t *slot_of, const float *gate, float *h) {
+  if (T < 1 || d < 1 || k < 1) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int i = 0; i < d; ++i) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j)
+        acc += gate[(size_t)t * k + j] *
+               orc_get(y_perm, (size_t)slot_of[(size_t)t * k + j] * d + i, dtype);
+      if (shared) acc += orc_get(shared, (size_t)t * d + i, dtype);
+      if (residual) acc += orc_get(residual, (size_t)t * d + i, dtype);
+      h[(size_t)t * d + i] = acc;
+    }
+  return ORC_OK;
+}

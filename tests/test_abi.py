@@ -1,0 +1,188 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/moe.h declares, and rejects bad arguments on the host before any HIP
+call (fake, never-dereferenced addresses are enough for that)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_34_amd as moe
+from mixture_experts_layer_34_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+A = 0x100000          # aligned fake device address
+MIS = 0x100001        # misaligned fake device address
+BIG = 1 << 40         # fake workspace size
+
+S = {v: k for k, v in _native.STATUS_NAMES.items()}
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
+                 "moe_workspace_bytes", "moe_status_str"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_native.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(moe_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def p16(**kw):
+    base = dict(T=4096, d=2048, N=16, m=4, K=2, K_s=2, d_ff=1408, dtype="bf16")
+    base.update(kw)
+    return moe.problem(**base)
+
+
+def status(fn, *args):
+    with pytest.raises(moe.MoeError) as ei:
+        fn(*args)
+    return _native.STATUS_NAMES[ei.value.status]
+
+
+def test_status_strings():
+    for code in range(8):
+        assert moe.moe_status_str(code)
+    assert moe.moe_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,why", [
+    (dict(T=0), "T < 1"),
+    (dict(d=48), "d not a multiple of 32"),
+    (dict(d=0), "d < 32"),
+    (dict(d_ff=100), "d_ff not a multiple of 32"),
+    (dict(N=0), "N < 1"),
+    (dict(m=0), "m < 1"),
+    (dict(K_s=-1), "K_s < 0"),
+    (dict(K=1, K_s=4), "k < 1"),
+    (dict(N=2, m=1, K=3, K_s=0), "k > n"),
+    (dict(N=257, m=1, K=1, K_s=0), "n > 256"),
+    (dict(N=128, m=1, K=65, K_s=0), "k > 64"),
+    (dict(T=1 << 29, N=64, m=1, K=8, K_s=0), "T*k overflows int32"),
+])
+def test_shape_validation(kw, why):
+    p = p16(**kw)
+    assert moe.moe_workspace_bytes(p) == 0, why
+    assert status(moe.moe_route, p, A, A, A, A, A, A, A, A, BIG) == "MOE_ERR_SHAPE", why
+    assert status(moe.moe_layer_fwd, p, A, A, A, A, A, A, A, A, A, A, A, A, A, A, 0, A,
+                  BIG) == "MOE_ERR_SHAPE", why
+
+
+def test_dtype_validation():
+    p = p16()
+    p.dtype = 7
+    assert moe.moe_workspace_bytes(p) == 0
+    assert status(moe.moe_combine, p, A, A, A, A, A, A) == "MOE_ERR_DTYPE"
+
+
+def test_null_problem():
+    r = _native.lib.moe_route(None, A, A, A, A, A, A, A, A, BIG, None)
+    assert _native.STATUS_NAMES[r] == "MOE_ERR_NULL"
+    assert _native.lib.moe_workspace_bytes(None) == 0
+
+
+def test_route_pointer_checks():
+    p = p16()
+    ws = moe.moe_workspace_bytes(p)
+    for i in range(7):
+        args = [A] * 7
+        args[i] = None
+        assert status(moe.moe_route, p, *args, A, ws) == "MOE_ERR_NULL", i
+        args[i] = MIS
+        assert status(moe.moe_route, p, *args, A, ws) == "MOE_ERR_ALIGN", i
+    assert status(moe.moe_route, p, *[A] * 7, None, ws) == "MOE_ERR_WORKSPACE"
+    assert status(moe.moe_route, p, *[A] * 7, A, ws - 1) == "MOE_ERR_WORKSPACE"
+    assert status(moe.moe_route, p, *[A] * 7, MIS, ws) == "MOE_ERR_ALIGN"
+
+
+def test_permute_pointer_checks():
+    p = p16()
+    ws = moe.moe_workspace_bytes(p)
+    # u may be NULL only when x_perm is NULL
+    assert status(moe.moe_permute, p, None, A, A, A, A, A, A, ws) == "MOE_ERR_NULL"
+    for i in (1, 2, 3, 4):
+        args = [A] * 6
+        args[i] = None
+        assert status(moe.moe_permute, p, *args, A, ws) == "MOE_ERR_NULL", i
+        args[i] = MIS
+        assert status(moe.moe_permute, p, *args, A, ws) == "MOE_ERR_ALIGN", i
+    assert status(moe.moe_permute, p, A, A, A, A, A, MIS, A, ws) == "MOE_ERR_ALIGN"
+    assert status(moe.moe_permute, p, A, A, A, A, A, A, A, 16) == "MOE_ERR_WORKSPACE"
+
+
+def test_grouped_ffn_checks():
+    p = p16()
+    ws = moe.moe_workspace_bytes(p)
+    R = p.T * 6
+    ok = [A] * 5
+    assert status(moe.moe_grouped_ffn, p, 0, R, *ok, 1408, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(moe.moe_grouped_ffn, p, 257, R, *ok, 1408, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(moe.moe_grouped_ffn, p, 64, 0, *ok, 1408, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(moe.moe_grouped_ffn, p, 64, R, *ok, 1400, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(moe.moe_grouped_ffn, p, 64, R + 1, *ok, 1408, A, A, ws) == "MOE_ERR_WORKSPACE"
+    assert status(moe.moe_grouped_ffn, p, 64, R, *ok, 1408 * 8, A, A,
+                  ws) == "MOE_ERR_WORKSPACE"
+    for i in range(5):
+        args = [A] * 5
+        args[i] = None
+        assert status(moe.moe_grouped_ffn, p, 64, R, *args, 1408, A, A, ws) == "MOE_ERR_NULL"
+        args[i] = MIS
+        assert status(moe.moe_grouped_ffn, p, 64, R, *args, 1408, A, A, ws) == "MOE_ERR_ALIGN"
+    assert status(moe.moe_grouped_ffn, p, 64, R, *ok, 1408, None, A, ws) == "MOE_ERR_NULL"
+
+
+def test_combine_checks():
+    p = p16()
+    for i in range(4):
+        args = [A] * 4
+        args[i] = None
+        assert status(moe.moe_combine, p, A, A, *args) == "MOE_ERR_NULL", i
+        args[i] = MIS
+        assert status(moe.moe_combine, p, A, A, *args) == "MOE_ERR_ALIGN", i
+    assert status(moe.moe_combine, p, MIS, None, A, A, A, A) == "MOE_ERR_ALIGN"
+    assert status(moe.moe_combine, p, None, MIS, A, A, A, A) == "MOE_ERR_ALIGN"
+
+
+def test_layer_fwd_checks():
+    p = p16()
+    ws = moe.moe_workspace_bytes(p)
+    full = [A] * 14
+    # bad flag bits
+    assert status(moe.moe_layer_fwd, p, *full, 4, A, ws) == "MOE_ERR_SHAPE"
+    # shared weights required when K_s > 0 ...
+    args = list(full)
+    args[5] = None
+    assert status(moe.moe_layer_fwd, p, *args, 0, A, ws) == "MOE_ERR_NULL"
+    # ... and misaligned ones rejected
+    args[5] = MIS
+    assert status(moe.moe_layer_fwd, p, *args, 0, A, ws) == "MOE_ERR_ALIGN"
+    for i in (0, 1, 2, 3, 4, 8, 9, 10, 11, 12, 13):
+        args = list(full)
+        args[i] = None
+        assert status(moe.moe_layer_fwd, p, *args, 0, A, ws) == "MOE_ERR_NULL", i
+        args[i] = MIS
+        assert status(moe.moe_layer_fwd, p, *args, 0, A, ws) == "MOE_ERR_ALIGN", i
+    assert status(moe.moe_layer_fwd, p, *full, 0, A, ws - 256) == "MOE_ERR_WORKSPACE"
+
+
+def test_workspace_grows_with_problem():
+    a = moe.moe_workspace_bytes(p16())
+    b = moe.moe_workspace_bytes(p16(T=8192))
+    assert 0 < a < b
+    assert a % 256 == 0

@@ -379,3 +379,30 @@ def test_bf16_storage_is_widened_exactly():
     b = oracle.layer(wide, cfg.N, cfg.m, cfg.K, cfg.K_s)
     for key in ("topk_idx", "topk_gate", "h"):
         assert (a[key] == b[key]).all()
+
+
+def test_combine_closed_form():
+    """h = sum_j g_j y[slot_j] + shared + residual with exact small values."""
+    y = f32([[2.0, 4.0], [8.0, -2.0], [1.0, 1.0]])
+    slot = np.array([[2, 0], [1, 2]], np.int32)
+    gate = f32([[0.5, 0.25], [0.125, 1.0]])
+    sh = f32([[1.0, 0.0], [0.0, 1.0]])
+    res = f32([[10.0, 20.0], [30.0, 40.0]])
+    h = oracle.combine(y, slot, gate, sh, res)
+    want = [[0.5 * 1 + 0.25 * 2 + 1 + 10, 0.5 * 1 + 0.25 * 4 + 0 + 20],
+            [0.125 * 8 + 1 * 1 + 0 + 30, 0.125 * -2 + 1 * 1 + 1 + 40]]
+    assert h.tolist() == want
+    h2 = oracle.combine(y, slot, gate)
+    assert h2.tolist() == (np.array(want) - sh - res).tolist()
+
+
+def test_combine_matches_layer():
+    """The combine entry reproduces the layer's h from its own Y and S."""
+    cfg = moe_synth.CONFIGS["tiny"]
+    inp = moe_synth.make_inputs(cfg)
+    o = oracle.layer(inp, cfg.N, cfg.m, cfg.K, cfg.K_s)
+    pm = oracle.permute(o["topk_idx"], cfg.n)
+    y_perm = np.empty((cfg.T * cfg.k, cfg.d), np.float32)
+    y_perm[pm["slot_of"].ravel()] = o["Y"].reshape(-1, cfg.d)
+    h = oracle.combine(y_perm, pm["slot_of"], o["topk_gate"], o["S"], inp["u"])
+    assert (h == o["h"]).all()
