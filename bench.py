@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeekMoE layer forward on one MI355X.
+
+Workload: the 16B-shaped layer (T = 4096 tokens, d = 2048, 64 routed
+fine-grained experts with 6 kept per token, 2 shared experts, SwiGLU
+intermediate 1408, bf16 storage, fp32 accumulation), synthetic seeded inputs.
+A step is one moe_layer_fwd call (route, grouping, routed experts, shared
+experts, combine) with inputs resident in HBM.  Two copies of every weight
+are rotated so the 256 MB last-level cache cannot serve a step from the
+previous one.
+
+Prints one JSON line with tokens/s, the roofline of the dominant kernel
+(timed live with HIP events recorded on the launch stream), per-kernel
+times, the 64-token decode regime's HBM rate, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+METRIC = "MoE layer fwd tokens/s + MFMA util % (16B-shaped, 4096 tok); HBM GB/s @64 tok"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent calls through ctypes (events are recorded by libmoe itself)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return out.value
+
+    def destroy(self, e: int):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_work(cfg, n_active: int, es: int = 2) -> dict:
+    """Algorithmic FLOPs and HBM bytes of each kernel of one layer call.
+    Weights count once and only for experts that receive tokens."""
+    T, d, f, n, k, ks = cfg.T, cfg.d, cfg.d_ff, cfg.n, cfg.k, cfg.K_s
+    R = T * k
+    B = (T + 63) // 64
+    fs = ks * f
+    w = {}
+    w["route"] = dict(flop=2 * T * d * n, bytes=T * d * es + n * d * es + R * 12 + B * n * 12)
+    w["scan"] = dict(flop=0, bytes=B * n * 12 + n * 12)
+    w["scatter"] = dict(flop=0, bytes=R * 4 * 5 + B * n * 4)
+    w["routed_up_swiglu"] = dict(flop=4 * R * d * f,
+                                 bytes=n_active * 2 * f * d * es + R * d * es + R * f * es + R * 4)
+    w["routed_down"] = dict(flop=2 * R * f * d,
+                            bytes=n_active * d * f * es + R * f * es + R * d * es)
+    if ks:
+        w["shared_up_swiglu"] = dict(flop=4 * T * d * fs,
+                                     bytes=2 * fs * d * es + T * d * es + T * fs * es)
+        w["shared_down"] = dict(flop=2 * T * fs * d, bytes=fs * d * es + T * fs * es + T * d * es)
+    w["combine"] = dict(flop=2 * R * d, bytes=3 * T * d * es + R * d * es + R * 8)
+    return w
+
+
+def roofline(flop: float, nbytes: float, seconds: float) -> dict:
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if flop and t_mfma >= t_hbm:
+        ach = flop / seconds / 1e12
+        return dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4))
+    ach = nbytes / seconds / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(ach / PEAK_HBM_GBS, 4))
+
+
+class Layer:
+    """Device-resident inputs, outputs and workspace of one workload."""
+
+    def __init__(self, cfg, inp, weight_sets, moe, torch):
+        from mixture_experts_layer_34_amd.device import to_device, workspace
+        self.moe, self.torch, self.cfg = moe, torch, cfg
+        dev = "cuda"
+        self.p = moe.problem(cfg.T, cfg.d, cfg.N, cfg.m, cfg.K, cfg.K_s, cfg.d_ff, cfg.dtype)
+        self.u = to_device(inp["u"], dev)
+        self.c = to_device(inp["centroids"], dev)
+        self.weights = weight_sets
+        self.h = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
+        self.idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+        self.gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(cfg.n, dtype=torch.int32, device=dev)
+        self.f = torch.empty(cfg.n, dtype=torch.float32, device=dev)
+        self.P = torch.empty(cfg.n, dtype=torch.float32, device=dev)
+        self.ws = workspace(self.p, dev)
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def run(self, i: int, marks=None):
+        w = self.weights[i % len(self.weights)]
+        args = (self.p, self.u, self.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"],
+                self.h, self.idx, self.gate, self.counts, self.f, self.P, 0, self.ws)
+        if marks is None:
+            self.moe.moe_layer_fwd(*args, stream=self.stream)
+        else:
+            self.moe.moe_layer_fwd_marked(*args, marks, stream=self.stream)
+
+
+def time_layer(layer: Layer, hip: Hip, steps: int, warmup: int) -> dict:
+    torch = layer.torch
+    for i in range(warmup):
+        layer.run(i)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    rec(e0, layer.stream)
+    for i in range(steps):
+        layer.run(i)
+    rec(e1, layer.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hip.ms(e0, e1) / steps
+    # per-kernel times: the same number of steps with marks between kernels
+    names = layer.moe.moe_layer_kernels(layer.p, 0)
+    marks = [[hip.event() for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        layer.run(i, marks[i])
+    torch.cuda.synchronize()
+    per = {n: 0.0 for n in names}
+    marked_total = 0.0
+    for i in range(steps):
+        for j, n in enumerate(names):
+            per[n] += hip.ms(marks[i][j], marks[i][j + 1]) / steps
+        marked_total += hip.ms(marks[i][0], marks[i][-1]) / steps
+    for row in marks:
+        for e in row:
+            hip.destroy(e)
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, kernel_ms=per,
+                marked_ms_per_step=marked_total, kernels=names)
+
+
+def cpu_baseline(cfg, inp, seconds: float) -> dict:
+    """The oracle on the first T_s tokens of the workload as their own batch."""
+    import numpy as np
+
+    import oracle
+    sub = dict(inp)
+    probe = 16
+    sub["u"] = np.ascontiguousarray(inp["u"][:probe])
+    t0 = time.perf_counter()
+    oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
+    per_tok = (time.perf_counter() - t0) / probe
+    ts = int(max(probe, min(cfg.T, seconds / max(per_tok, 1e-9))))
+    sub["u"] = np.ascontiguousarray(inp["u"][:ts])
+    t0 = time.perf_counter()
+    oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
+    el = time.perf_counter() - t0
+    return dict(value=round(ts / el, 2), unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"first {ts} of {cfg.T} tokens as one batch (routing + all experts), "
+                       f"{el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=2, help="weight copies rotated per step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer is built and timed on a single "
+              "MI355X (no expert parallelism across GPUs in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_34_amd as moe
+    import moe_synth
+    from mixture_experts_layer_34_amd.device import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+    cfg = moe_synth.CONFIGS["16b"]
+    log(f"generating inputs for {cfg}")
+    inp = moe_synth.make_inputs(cfg, seed=0)
+    sets = []
+    for r in range(args.rotate):
+        s = {k: to_device(inp[k], "cuda") for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}
+        sets.append(s)
+    layer = Layer(cfg, inp, sets, moe, torch)
+    log("timing the 16B-shaped layer")
+    res = time_layer(layer, hip, args.steps, args.warmup)
+    counts = layer.counts.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    work = kernel_work(cfg, n_active)
+    kern = {}
+    for name, ms in res["kernel_ms"].items():
+        w = work[name]
+        kern[name] = dict(us=round(ms * 1e3, 2), **roofline(w["flop"], w["bytes"], ms * 1e-3))
+    dom = max(res["kernel_ms"], key=res["kernel_ms"].get)
+    dw = work[dom]
+    droof = roofline(dw["flop"], dw["bytes"], res["kernel_ms"][dom] * 1e-3)
+    droof["traffic"] = None
+    droof["kernel"] = dom
+    droof["us_per_launch"] = round(res["kernel_ms"][dom] * 1e3, 2)
+    routed_flop = work["routed_up_swiglu"]["flop"] + work["routed_down"]["flop"]
+    routed_s = (res["kernel_ms"]["routed_up_swiglu"] + res["kernel_ms"]["routed_down"]) * 1e-3
+    ms = res["ms_per_step"]
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "DeepSeekMoE 16B-shaped layer forward: T=4096 tokens, d=2048, "
+                               "64 routed experts (top-6), 2 shared, SwiGLU d_ff=1408",
+                   "T": cfg.T, "d": cfg.d, "n_routed": cfg.n, "top_k": cfg.k,
+                   "n_shared": cfg.K_s, "d_ff": cfg.d_ff, "N": cfg.N, "m": cfg.m, "K": cfg.K,
+                   "weight_copies_rotated": args.rotate, "parallelism": "single GPU"},
+        "roofline": droof,
+        "routed_grouped_gemm_mfma_frac": round(routed_flop / routed_s / 1e12 / PEAK_BF16_TFLOPS,
+                                               4),
+        "kernels": kern,
+        "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
+        "wall_ms_per_step": round(res["wall_ms_per_step"], 4),
+    }
+    del layer
+    if not args.no_decode:
+        dcfg = moe_synth.CONFIGS["16b_decode"]
+        log("timing the 64-token decode regime")
+        du, dc, _ = moe_synth.make_router_inputs(dcfg, seed=0)
+        dinp = dict(inp, u=du, centroids=dc)
+        dl = Layer(dcfg, dinp, sets, moe, torch)
+        dres = time_layer(dl, hip, max(args.steps, 20), args.warmup)
+        dcounts = dl.counts.cpu().numpy()
+        dwork = kernel_work(dcfg, int((dcounts > 0).sum()))
+        dbytes = sum(w["bytes"] for w in dwork.values())
+        dms = dres["ms_per_step"]
+        out["decode_64tok"] = {
+            "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
+            "ms_per_step": round(dms, 4),
+            "algorithmic_bytes": int(dbytes),
+            "hbm_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "experts_touched": int((dcounts > 0).sum()),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in dres["kernel_ms"].items()},
+        }
+        del dl
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

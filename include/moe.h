@@ -162,6 +162,27 @@ moe_status moe_layer_fwd(const moe_problem *p, const void *u, const void *centro
                          float *topk_gate, int32_t *counts, float *f, float *P, int flags,
                          void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * moe_layer_fwd with measurement marks, for callers that time the layer's
+ * kernels on the stream they run on.  `marks` holds hipEvent_t handles created
+ * by the caller, at least moe_layer_kernels(p, flags, NULL, 0) + 1 of them:
+ * marks[0] is recorded before the first kernel and marks[i] right after the
+ * i-th kernel launch, all on `stream`.  marks = NULL behaves as moe_layer_fwd.
+ */
+moe_status moe_layer_fwd_marked(const moe_problem *p, const void *u, const void *centroids,
+                                const void *w1, const void *w3, const void *w2,
+                                const void *ws1, const void *ws3, const void *ws2, void *h,
+                                int32_t *topk_idx, float *topk_gate, int32_t *counts, float *f,
+                                float *P, int flags, void *ws, size_t ws_bytes, void *stream,
+                                void *const *marks);
+
+/*
+ * Number of kernels moe_layer_fwd launches for (p, flags); when names is not
+ * NULL, up to max_names static kernel labels are stored.  Returns -1 for an
+ * invalid problem.
+ */
+int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int max_names);
+
 /* Static description of a status code. */
 const char *moe_status_str(moe_status s);
 

@@ -2,14 +2,21 @@
 
 The compute path is libmoe.so (hand-written HIP, C ABI in include/moe.h);
 this package is its ctypes binding plus device-memory plumbing with torch.
-Importing it fails when the library is not built.
+The binding loads on first use and raises ImportError when the library is
+not built (python -m mixture_experts_layer_34_amd.build); there is no
+fallback.
 """
-from ._native import (MOE_BF16, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_NO_RESIDUAL,
-                      MOE_NO_SHARED, MoeError, moe_combine, moe_grouped_ffn, moe_layer_fwd,
-                      moe_permute, moe_problem, moe_route, moe_status_str, moe_workspace_bytes,
-                      problem)
+import importlib
 
-__all__ = ["MOE_BF16", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_NO_RESIDUAL",
-           "MOE_NO_SHARED", "MoeError", "moe_combine", "moe_grouped_ffn", "moe_layer_fwd",
-           "moe_permute", "moe_problem", "moe_route", "moe_status_str", "moe_workspace_bytes",
-           "problem"]
+_EXPORTS = ("MOE_BF16", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_NO_RESIDUAL",
+            "MOE_NO_SHARED", "MoeError", "moe_combine", "moe_grouped_ffn", "moe_layer_fwd",
+            "moe_layer_fwd_marked", "moe_layer_kernels", "moe_permute", "moe_problem",
+            "moe_route", "moe_status_str", "moe_workspace_bytes", "problem")
+__all__ = list(_EXPORTS)
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        native = importlib.import_module("._native", __name__)
+        return getattr(native, name)
+    raise AttributeError(name)

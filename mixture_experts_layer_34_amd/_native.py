@@ -63,6 +63,11 @@ def _load():
     lib.moe_layer_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int,
                                   P, sz, P]
     lib.moe_layer_fwd.restype = st
+    lib.moe_layer_fwd_marked.argtypes = lib.moe_layer_fwd.argtypes + [P]
+    lib.moe_layer_fwd_marked.restype = st
+    lib.moe_layer_kernels.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                      ctypes.c_int]
+    lib.moe_layer_kernels.restype = ctypes.c_int
     return lib
 
 
@@ -142,3 +147,22 @@ def moe_layer_fwd(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_
         ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
         _ptr(ws3), _ptr(ws2), _ptr(h), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(f),
         _ptr(P), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_layer_kernels(p, flags=0) -> list:
+    n = lib.moe_layer_kernels(ctypes.byref(p), flags, None, 0)
+    if n < 0:
+        raise MoeError("moe_layer_kernels", 2, "invalid problem")
+    names = (ctypes.c_char_p * n)()
+    lib.moe_layer_kernels(ctypes.byref(p), flags, names, n)
+    return [x.decode() for x in names]
+
+
+def moe_layer_fwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate,
+                         counts, f, P, flags, ws, marks, ws_bytes=None, stream=None):
+    """marks: sequence of hipEvent_t handles (ints), len >= kernels + 1."""
+    arr = None if marks is None else (ctypes.c_void_p * len(marks))(*marks)
+    _check("moe_layer_fwd_marked", lib.moe_layer_fwd_marked(
+        ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
+        _ptr(ws3), _ptr(ws2), _ptr(h), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(f),
+        _ptr(P), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream), arr))

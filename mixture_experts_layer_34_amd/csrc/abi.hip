@@ -237,6 +237,37 @@ moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centro
                          const void* ws3, const void* ws2, void* h, int32_t* topk_idx,
                          float* topk_gate, int32_t* counts, float* f, float* P, int flags,
                          void* ws, size_t ws_bytes, void* stream) {
+  return moe_layer_fwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate,
+                              counts, f, P, flags, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_kernels(const moe_problem* p, int flags, const char** names, int max_names) {
+  Dims d;
+  if (check_problem(p, &d) != MOE_OK) return -1;
+  const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
+  const bool tiled = p->dtype == MOE_BF16;
+  const char* seq[8];
+  int c = 0;
+  seq[c++] = "route";
+  seq[c++] = "scan";
+  seq[c++] = "scatter";
+  seq[c++] = tiled ? "routed_up_swiglu" : "routed_up_swiglu_f32";
+  seq[c++] = tiled ? "routed_down" : "routed_down_f32";
+  if (shared) {
+    seq[c++] = tiled ? "shared_up_swiglu" : "shared_up_swiglu_f32";
+    seq[c++] = tiled ? "shared_down" : "shared_down_f32";
+  }
+  seq[c++] = "combine";
+  for (int i = 0; names && i < c && i < max_names; ++i) names[i] = seq[i];
+  return c;
+}
+
+moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void* centroids,
+                                const void* w1, const void* w3, const void* w2,
+                                const void* ws1, const void* ws3, const void* ws2, void* h,
+                                int32_t* topk_idx, float* topk_gate, int32_t* counts, float* f,
+                                float* P, int flags, void* ws, size_t ws_bytes, void* stream,
+                                void* const* marks) {
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
@@ -258,14 +289,23 @@ moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centro
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm_token = at<int32_t>(ws, L.perm_token);
   int32_t* slot_of = at<int32_t>(ws, L.slot_of);
+  int mark_i = 0;
+  auto mark = [&]() -> hipError_t {
+    if (!marks) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(marks[mark_i++]), s);
+  };
+  MOE_TRY(mark());
 
   MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
                             at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
                             at<int32_t>(ws, L.lrank), s));
+  MOE_TRY(mark());
   MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
                            counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+  MOE_TRY(mark());
   MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
                               d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
+  MOE_TRY(mark());
   // routed experts: rows gathered from u through perm_token
   moe::FfnArgs a{};
   a.dtype = p->dtype;
@@ -283,7 +323,10 @@ moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centro
   a.tiles = &tl;
   a.hbuf = at<char>(ws, L.hbuf);
   a.y = at<char>(ws, L.ybuf);
-  MOE_TRY(moe::launch_grouped_ffn(a, s));
+  MOE_TRY(moe::launch_ffn_up(a, s));
+  MOE_TRY(mark());
+  MOE_TRY(moe::launch_ffn_down(a, s));
+  MOE_TRY(mark());
   // shared experts: one dense SwiGLU of width K_s*d_ff over all tokens
   void* sbuf = nullptr;
   if (shared) {
@@ -303,11 +346,15 @@ moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centro
     b.tiles = nullptr;
     b.hbuf = at<char>(ws, L.hsbuf);
     b.y = at<char>(ws, L.sbuf);
-    MOE_TRY(moe::launch_grouped_ffn(b, s));
+    MOE_TRY(moe::launch_ffn_up(b, s));
+    MOE_TRY(mark());
+    MOE_TRY(moe::launch_ffn_down(b, s));
+    MOE_TRY(mark());
     sbuf = b.y;
   }
   MOE_TRY(moe::launch_combine(p->dtype, (flags & MOE_NO_RESIDUAL) ? nullptr : u, sbuf,
                               at<char>(ws, L.ybuf), slot_of, topk_gate, h, d.T, d.d, d.k, s));
+  MOE_TRY(mark());
   return MOE_OK;
 }
 

@@ -243,24 +243,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
 
 }  // namespace
 
-hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
-  if (a.dtype == 0) {
-    GemmF32Args up{(const float*)a.x, a.x_rows, a.ldx, (const float*)a.w1, (const float*)a.w3,
-                   (int64_t)a.d_ff_g * a.d, a.d, a.d_ff_g, (float*)a.hbuf, a.d_ff_g, a.rows,
-                   a.tiles ? a.offsets : nullptr, a.n_groups};
-    const int64_t n_up = a.rows * a.d_ff_g;
-    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)((n_up + 255) / 256)), dim3(256), 0,
-                       s, up);
-    GemmF32Args dn{(const float*)a.hbuf, nullptr, a.d_ff_g, (const float*)a.w2, nullptr,
-                   (int64_t)a.d * a.d_ff_g, a.d_ff_g, a.d, (float*)a.y, a.d, a.rows,
-                   a.tiles ? a.offsets : nullptr, a.n_groups};
-    const int64_t n_dn = a.rows * a.d;
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)((n_dn + 255) / 256)), dim3(256), 0,
-                       s, dn);
-    return hipGetLastError();
-  }
-  const int max_m = a.tiles ? a.tiles->max_tiles : (int)((a.rows + BM - 1) / BM);
+static GemmArgs up_args(const FfnArgs& a) {
   GemmArgs up{};
   up.A = (const uint16_t*)a.x;
   up.a_rows = a.x_rows;
@@ -281,9 +264,11 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   }
   up.n_groups = a.n_groups;
   up.single_rows = a.rows;
-  hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)(max_m * up.nN)), dim3(kThreads), 0,
-                     s, up);
-  GemmArgs dn = up;
+  return up;
+}
+
+static GemmArgs down_args(const FfnArgs& a) {
+  GemmArgs dn = up_args(a);
   dn.A = (const uint16_t*)a.hbuf;
   dn.a_rows = nullptr;
   dn.lda = a.d_ff_g;
@@ -295,9 +280,51 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   dn.C = (uint16_t*)a.y;
   dn.ldc = a.d;
   dn.nN = (a.d + BN - 1) / BN;
-  hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)(max_m * dn.nN)), dim3(kThreads), 0,
-                     s, dn);
+  return dn;
+}
+
+static int max_m_tiles(const FfnArgs& a) {
+  return a.tiles ? a.tiles->max_tiles : (int)((a.rows + BM - 1) / BM);
+}
+
+hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  if (a.dtype == 0) {
+    GemmF32Args up{(const float*)a.x, a.x_rows, a.ldx, (const float*)a.w1, (const float*)a.w3,
+                   (int64_t)a.d_ff_g * a.d, a.d, a.d_ff_g, (float*)a.hbuf, a.d_ff_g, a.rows,
+                   a.tiles ? a.offsets : nullptr, a.n_groups};
+    const int64_t n_up = a.rows * a.d_ff_g;
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)((n_up + 255) / 256)), dim3(256), 0,
+                       s, up);
+    return hipGetLastError();
+  }
+  const GemmArgs up = up_args(a);
+  hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)(max_m_tiles(a) * up.nN)),
+                     dim3(kThreads), 0, s, up);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  if (a.dtype == 0) {
+    GemmF32Args dn{(const float*)a.hbuf, nullptr, a.d_ff_g, (const float*)a.w2, nullptr,
+                   (int64_t)a.d * a.d_ff_g, a.d_ff_g, a.d, (float*)a.y, a.d, a.rows,
+                   a.tiles ? a.offsets : nullptr, a.n_groups};
+    const int64_t n_dn = a.rows * a.d;
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)((n_dn + 255) / 256)), dim3(256),
+                       0, s, dn);
+    return hipGetLastError();
+  }
+  const GemmArgs dn = down_args(a);
+  hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)(max_m_tiles(a) * dn.nN)),
+                     dim3(kThreads), 0, s, dn);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
+  const hipError_t e = launch_ffn_up(a, s);
+  if (e != hipSuccess) return e;
+  return launch_ffn_down(a, s);
 }
 
 }  // namespace moe

@@ -61,7 +61,9 @@ struct FfnArgs {
   void* hbuf;              // [rows][d_ff_g] intermediate
   void* y;                 // [rows][d]
 };
-hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);   // up then down
+hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);        // hbuf = SwiGLU(x W1, x W3)
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);      // y = hbuf W2
 
 hipError_t launch_combine(int dtype, const void* residual, const void* shared_out,
                           const void* y_perm, const int32_t* slot_of, const float* gate,

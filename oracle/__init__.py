@@ -45,6 +45,7 @@ def _load():
     lib.oracle_balance_loss.restype = ctypes.c_float
     lib.oracle_permute.argtypes = [i64, i32, i32, P, P, P, P]
     lib.oracle_expert.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_layer.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32,
                                  P, P, P, P, P, P, P, P, P, i64,
@@ -180,3 +181,8 @@ def combine(y_perm: np.ndarray, slot_of: np.ndarray, gate: np.ndarray, shared=No
     if rc != 0:
         raise RuntimeError(f"oracle_combine failed ({rc})")
     return h
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().oracle_threads())

@@ -338,3 +338,15 @@ int oracle_combine(int64_t T, int d, int k, int dtype, const void *residual, con
     }
   return ORC_OK;
 }
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+/* Threads the oracle's parallel loops use. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -8,16 +8,24 @@ import moe_synth
 # Parity bars.
 #   Expert outputs, shared outputs, combine and layer output: max relative
 #   error 2e-2, rel(a, b) = max|a - b| / max|b| per tensor.
-#   Gates and P: a logit rounding difference dl between two fp32 sums moves
-#   exp(dl) by ~dl; certified margins assume |dl| << 1e-4, so gates agree to
-#   1e-4 relative.  P adds two fp32 summations over T positive terms in
-#   different orders, each within (T - 1) 2^-24 relative.
+#   Gates: g_i = exp(l_i - max) / Z, so a difference dl in the fp32 logits of
+#   the two sides moves g_i by a relative ~2 dl.  Two fp32 dot products of
+#   length d summed in different orders differ by about eps sqrt(d) |l|
+#   (random-walk rounding, eps = 2^-24); the bound below takes four times
+#   that at the largest logit, and never less than 1e-4.
+#   P: the gate bound plus two fp32 summations over T positive terms in
+#   different orders, each within (T - 1) eps relative.
 REL_TOL = 2e-2
 GATE_TOL = 1e-4
+EPS = 2.0 ** -24
 
 
-def p_tol(T: int) -> float:
-    return GATE_TOL + 2.0 * T * 2.0 ** -24
+def gate_tol(d: int, max_abs_logit: float) -> float:
+    return max(GATE_TOL, 4.0 * EPS * d ** 0.5 * max_abs_logit * 2.0)
+
+
+def p_tol(T: int, d: int, max_abs_logit: float) -> float:
+    return gate_tol(d, max_abs_logit) + 2.0 * T * EPS
 
 
 def rel(a, b) -> float:
