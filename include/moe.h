@@ -59,7 +59,8 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /*
  * The pages' statement of the problem.  Valid when
- *   T >= 1, T*k < 2^31;  d, d_ff >= 32 and multiples of 32;
+ *   T >= 1;  T*k*d, T*k*d_ff and T*K_s*d_ff < 2^31;  d, d_ff >= 32 and
+ *   multiples of 32;
  *   N, m, K >= 1;  K_s >= 0;  n = m*N <= MOE_MAX_EXPERTS;
  *   1 <= k = m*K - K_s <= min(n, MOE_MAX_TOPK).
  * Only the products m*N and m*K enter the result.
@@ -75,8 +76,11 @@ typedef struct moe_problem {
   int32_t dtype; /* moe_dtype */
 } moe_problem;
 
-/* moe_layer_fwd flags (component checks). */
-enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2 };
+/* Flags.  MOE_NO_RESIDUAL / MOE_NO_SHARED (moe_layer_fwd only) drop a term
+ * for component checks.  MOE_PACKED_WEIGHTS (moe_layer_fwd, moe_grouped_ffn):
+ * every expert weight tensor is in the packed layout of moe_pack_weights
+ * instead of row-major; bf16 only. */
+enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2, MOE_PACKED_WEIGHTS = 4 };
 
 /* Bytes of workspace that suffice for every entry point on this problem;
  * 0 when the problem is invalid. */
@@ -126,12 +130,12 @@ moe_status moe_permute(const moe_problem *p, const void *u, const int32_t *topk_
  * experts as one dense SwiGLU (their sum): n_groups = 1, rows = T,
  * d_ff_group = K_s*d_ff, offsets = {0, T}.
  * d_ff_group must be a multiple of 32 with rows*d_ff_group fitting the
- * workspace of moe_workspace_bytes(p).
+ * workspace of moe_workspace_bytes(p).  flags: 0 or MOE_PACKED_WEIGHTS.
  */
 moe_status moe_grouped_ffn(const moe_problem *p, int32_t n_groups, int64_t rows,
                            const int32_t *offsets, const void *x, const void *w1,
-                           const void *w3, const void *w2, int32_t d_ff_group, void *y,
-                           void *ws, size_t ws_bytes, void *stream);
+                           const void *w3, const void *w2, int32_t d_ff_group, int flags,
+                           void *y, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Gate-weighted combine with residual ("Routing in a classic MoE layer"):
@@ -154,13 +158,29 @@ moe_status moe_combine(const moe_problem *p, const void *residual, const void *s
  *   h [T][d]          out
  *   topk_idx, topk_gate, counts, f, P                 out, as moe_route
  *   flags             MOE_NO_RESIDUAL drops +u, MOE_NO_SHARED drops the shared
- *                     experts (component checks only)
+ *                     experts (component checks only); MOE_PACKED_WEIGHTS: all
+ *                     six weight tensors come from moe_pack_weights
  */
 moe_status moe_layer_fwd(const moe_problem *p, const void *u, const void *centroids,
                          const void *w1, const void *w3, const void *w2, const void *ws1,
                          const void *ws3, const void *ws2, void *h, int32_t *topk_idx,
                          float *topk_gate, int32_t *counts, float *f, float *P, int flags,
                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Weight layout for the grouped FFN's fast path (an implementation choice,
+ * made once when weights are loaded; the layer's result does not depend on
+ * it).  src is a bf16 matrix [rows][K] row-major; dst (same size, must not
+ * overlap src) receives it as 32-row bands, each band a run of K/16 blocks
+ * of 32 rows x 16 columns, and each block stored in MFMA operand order:
+ * element (r, k) of block sits at ((r % 32) + 32 * ((k % 16) / 8)) * 8 + k % 8.
+ * Stacked expert tensors pack as one matrix: w1, w3 with rows = n*d_ff,
+ * K = d; w2 with rows = n*d, K = d_ff; ws1, ws3 with rows = K_s*d_ff, K = d;
+ * ws2 with rows = d, K = K_s*d_ff.  Requires p->dtype == MOE_BF16,
+ * rows % 32 == 0, K % 32 == 0.  Asynchronous on stream.
+ */
+moe_status moe_pack_weights(const moe_problem *p, int64_t rows, int32_t K, const void *src,
+                            void *dst, void *stream);
 
 /*
  * moe_layer_fwd with measurement marks, for callers that time the layer's

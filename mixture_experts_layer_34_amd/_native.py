@@ -19,7 +19,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_UNSUPPORTED",
                 7: "MOE_ERR_HIP"}
 MOE_F32, MOE_BF16 = 0, 1
-MOE_NO_RESIDUAL, MOE_NO_SHARED = 1, 2
+MOE_NO_RESIDUAL, MOE_NO_SHARED, MOE_PACKED_WEIGHTS = 1, 2, 4
 MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 64
 
 
@@ -56,8 +56,10 @@ def _load():
     lib.moe_route.restype = st
     lib.moe_permute.argtypes = [PP, P, P, P, P, P, P, P, sz, P]
     lib.moe_permute.restype = st
-    lib.moe_grouped_ffn.argtypes = [PP, i32, i64, P, P, P, P, P, i32, P, P, sz, P]
+    lib.moe_grouped_ffn.argtypes = [PP, i32, i64, P, P, P, P, P, i32, ctypes.c_int, P, P, sz, P]
     lib.moe_grouped_ffn.restype = st
+    lib.moe_pack_weights.argtypes = [PP, i64, i32, P, P, P]
+    lib.moe_pack_weights.restype = st
     lib.moe_combine.argtypes = [PP, P, P, P, P, P, P, P]
     lib.moe_combine.restype = st
     lib.moe_layer_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int,
@@ -128,11 +130,16 @@ def moe_permute(p, u, topk_idx, offsets, perm_token, slot_of, x_perm, ws, ws_byt
         _ptr(slot_of), _ptr(x_perm), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
 
 
-def moe_grouped_ffn(p, n_groups, rows, offsets, x, w1, w3, w2, d_ff_group, y, ws,
+def moe_grouped_ffn(p, n_groups, rows, offsets, x, w1, w3, w2, d_ff_group, flags, y, ws,
                     ws_bytes=None, stream=None):
     _check("moe_grouped_ffn", lib.moe_grouped_ffn(
         ctypes.byref(p), n_groups, rows, _ptr(offsets), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2),
-        d_ff_group, _ptr(y), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        d_ff_group, flags, _ptr(y), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_pack_weights(p, rows, K, src, dst, stream=None):
+    _check("moe_pack_weights", lib.moe_pack_weights(
+        ctypes.byref(p), rows, K, _ptr(src), _ptr(dst), _stream(stream)))
 
 
 def moe_combine(p, residual, shared_out, y_perm, slot_of, topk_gate, h, stream=None):

@@ -28,6 +28,13 @@ moe_status check_problem(const moe_problem* p, Dims* out) {
   const int64_t k = (int64_t)p->m * p->K - p->K_s;
   if (n > MOE_MAX_EXPERTS || k < 1 || k > n || k > MOE_MAX_TOPK) return MOE_ERR_SHAPE;
   if (p->T * k >= (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  // Kernels index rows with 32-bit element offsets: every activation tensor
+  // (u, x_perm, y_perm, h and the SwiGLU intermediates) stays below 2^31
+  // elements.
+  const int64_t big = (int64_t)1 << 31;
+  if (p->T * k * p->d >= big || p->T * k * p->d_ff >= big ||
+      p->T * (int64_t)p->K_s * p->d_ff >= big)
+    return MOE_ERR_SHAPE;
   if ((int64_t)p->K_s * p->d_ff > INT32_MAX / 2) return MOE_ERR_SHAPE;
   out->T = p->T;
   out->d = p->d;
@@ -179,11 +186,14 @@ moe_status moe_permute(const moe_problem* p, const void* u, const int32_t* topk_
 
 moe_status moe_grouped_ffn(const moe_problem* p, int32_t n_groups, int64_t rows,
                            const int32_t* offsets, const void* x, const void* w1,
-                           const void* w3, const void* w2, int32_t d_ff_group, void* y,
-                           void* ws, size_t ws_bytes, void* stream) {
+                           const void* w3, const void* w2, int32_t d_ff_group, int flags,
+                           void* y, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
+  if (flags & ~MOE_PACKED_WEIGHTS) return MOE_ERR_SHAPE;
+  const bool packed = (flags & MOE_PACKED_WEIGHTS) != 0;
+  if (packed && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (n_groups < 1 || n_groups > MOE_MAX_EXPERTS || rows < 1 || d_ff_group < 32 ||
       d_ff_group % 32 != 0)
     return MOE_ERR_SHAPE;
@@ -213,7 +223,26 @@ moe_status moe_grouped_ffn(const moe_problem* p, int32_t n_groups, int64_t rows,
   a.tiles = &tl;
   a.hbuf = at<char>(ws, L.hbuf);
   a.y = y;
+  a.packed = packed;
   MOE_TRY(moe::launch_grouped_ffn(a, s));
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_problem* p, int64_t rows, int32_t K, const void* src,
+                            void* dst, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows < 32 || rows % 32 != 0 || K < 32 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (rows * (int64_t)K >= ((int64_t)1 << 33)) return MOE_ERR_SHAPE;
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (!aligned(src) || !aligned(dst)) return MOE_ERR_ALIGN;
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  const int64_t nb = rows * K * 2;
+  if (s0 < d0 + nb && d0 < s0 + nb) return MOE_ERR_SHAPE;  // overlapping buffers
+  MOE_TRY(moe::launch_pack(src, dst, rows, K, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 
@@ -246,17 +275,16 @@ int moe_layer_kernels(const moe_problem* p, int flags, const char** names, int m
   if (check_problem(p, &d) != MOE_OK) return -1;
   const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
   const bool tiled = p->dtype == MOE_BF16;
-  const char* seq[8];
+  const char* seq[10];
   int c = 0;
   seq[c++] = "route";
   seq[c++] = "scan";
   seq[c++] = "scatter";
-  seq[c++] = tiled ? "routed_up_swiglu" : "routed_up_swiglu_f32";
-  seq[c++] = tiled ? "routed_down" : "routed_down_f32";
-  if (shared) {
-    seq[c++] = tiled ? "shared_up_swiglu" : "shared_up_swiglu_f32";
-    seq[c++] = tiled ? "shared_down" : "shared_down_f32";
-  }
+  // bf16: one launch per projection covers routed and shared experts; fp32
+  // runs the two groups back to back inside the same mark.
+  seq[c++] = tiled ? "up_swiglu" : "up_swiglu_f32";
+  seq[c++] = tiled ? "down" : "down_f32";
+  (void)shared;
   seq[c++] = "combine";
   for (int i = 0; names && i < c && i < max_names; ++i) names[i] = seq[i];
   return c;
@@ -271,8 +299,10 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
-  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED)) return MOE_ERR_SHAPE;
+  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS)) return MOE_ERR_SHAPE;
   const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
+  const bool packed = (flags & MOE_PACKED_WEIGHTS) != 0;
+  if (packed && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!u || !centroids || !w1 || !w3 || !w2 || !h || !topk_idx || !topk_gate || !counts || !f ||
       !P)
     return MOE_ERR_NULL;
@@ -306,8 +336,11 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
                               d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
   MOE_TRY(mark());
-  // routed experts: rows gathered from u through perm_token
-  moe::FfnArgs a{};
+  // Routed experts (rows gathered from u through perm_token) and the shared
+  // experts (one dense SwiGLU of width K_s*d_ff over all tokens) go through
+  // the same launches so their tiles fill the GPU together.
+  moe::FfnArgs segs[2] = {};
+  moe::FfnArgs& a = segs[0];
   a.dtype = p->dtype;
   a.x = u;
   a.x_rows = perm_token;
@@ -323,14 +356,11 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   a.tiles = &tl;
   a.hbuf = at<char>(ws, L.hbuf);
   a.y = at<char>(ws, L.ybuf);
-  MOE_TRY(moe::launch_ffn_up(a, s));
-  MOE_TRY(mark());
-  MOE_TRY(moe::launch_ffn_down(a, s));
-  MOE_TRY(mark());
-  // shared experts: one dense SwiGLU of width K_s*d_ff over all tokens
+  a.packed = packed;
   void* sbuf = nullptr;
+  int nseg = 1;
   if (shared) {
-    moe::FfnArgs b{};
+    moe::FfnArgs& b = segs[1];
     b.dtype = p->dtype;
     b.x = u;
     b.x_rows = nullptr;
@@ -346,12 +376,14 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
     b.tiles = nullptr;
     b.hbuf = at<char>(ws, L.hsbuf);
     b.y = at<char>(ws, L.sbuf);
-    MOE_TRY(moe::launch_ffn_up(b, s));
-    MOE_TRY(mark());
-    MOE_TRY(moe::launch_ffn_down(b, s));
-    MOE_TRY(mark());
+    b.packed = packed;
     sbuf = b.y;
+    nseg = 2;
   }
+  MOE_TRY(moe::launch_ffn_up(segs, nseg, s));
+  MOE_TRY(mark());
+  MOE_TRY(moe::launch_ffn_down(segs, nseg, s));
+  MOE_TRY(mark());
   MOE_TRY(moe::launch_combine(p->dtype, (flags & MOE_NO_RESIDUAL) ? nullptr : u, sbuf,
                               at<char>(ws, L.ybuf), slot_of, topk_gate, h, d.T, d.d, d.k, s));
   MOE_TRY(mark());

@@ -8,6 +8,7 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte register payload
 
 constexpr int kWave = 64;
 
@@ -48,6 +49,13 @@ template <> struct Elem<1> {  // bf16 bits
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Load through a wave-uniform base and a 32-bit byte offset, which maps to
+// the global_load form with an SGPR base, a VGPR offset and an immediate.
+template <typename V>
+__device__ __forceinline__ V ld_off(const void* __restrict__ base, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
+}
 
 // Map a linear workgroup id to a logical tile so that each XCD (workgroups
 // are dealt round-robin over the 8 XCDs) processes one contiguous range of

@@ -5,26 +5,37 @@
 // DeepSeekMoE card); grouping tokens per expert and fusing the weight
 // matrices is the page's note on production layers.
 //
-// bf16 path: 128x128 output tiles, 4 waves each owning 64x64 through
-// MFMA 32x32x16 (fp32 accumulate), K staged through LDS in 64-wide slices
-// with double buffering.  For the up projection a tile's 128 columns are 64
-// rows of W1 and the same 64 rows of W3, so gate and up values of one output
-// land in the same lane and the SwiGLU is applied in registers.
-// M-tiles come from a device tile list (rows of one expert), so no host
-// synchronisation is needed; workgroups beyond the live tile count exit.
+// bf16 path.  A workgroup of 4 waves computes a 128-row x 512-column tile;
+// each wave owns all 128 rows and 128 columns as 4 x 4 MFMA 32x32x16 blocks
+// (fp32 accumulators in AGPRs, one wave per SIMD).  K advances in 32-wide
+// slices through a software pipeline: while the MFMAs of slice s run, the
+// wave reads the operand fragments of slice s+1 from LDS, writes slice s+2
+// (staged in registers) into the LDS buffer slice s vacated, and issues the
+// global loads of slice s+3; the instruction groups are interleaved one
+// MFMA at a time so the LDS and the matrix cores work concurrently.
+// For the up projection a wave's 128 columns are 64 rows of W1 followed by
+// the same 64 rows of W3, so gate and up values of one output land in the
+// same lane and the SwiGLU is applied in registers.  Outputs leave through
+// an LDS staging tile as coalesced 16-byte stores.
+// One launch can hold two segments (routed experts from a device tile list,
+// then the shared experts as one group) so both fill the GPU together; no
+// host synchronisation is needed and workgroups beyond the live tile count
+// exit.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = kTileM;  // 128
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (elements): 144 B, conflict-free b128 reads
+constexpr int BM = kTileM;          // 128 rows (tokens)
+constexpr int WN = 128;             // weight rows per wave
+constexpr int BN = 4 * WN;          // 512 weight rows per tile
+constexpr int BK = 32;              // K slice
+constexpr int LDK = BK + 8;         // padded LDS row (elements): 80 B
 constexpr int kThreads = 256;
+constexpr int kUpCols = BN / 2;     // d_ff columns per up tile (64 per wave)
 
-struct GemmArgs {
+struct GemmSeg {
   const uint16_t* A;
   const int32_t* a_rows;  // nullable gather map
   int64_t lda;
@@ -38,26 +49,267 @@ struct GemmArgs {
   int nN;                 // column tiles
   const int32_t* tile_row0;
   const int32_t* tile_rows;
-  const int32_t* tile_off;  // nullable: single group
+  const int32_t* tile_off;  // nullable: single group of single_rows rows
   const int32_t* num_tiles;
   int n_groups;
   int64_t single_rows;
 };
 
+struct GemmArgs {
+  GemmSeg seg[2];
+  int nseg;
+};
+
+// Weight packing: [rows][K] row-major -> 32-row bands, each a run of 16-wide
+// k blocks of 512 elements in MFMA operand order (lane l holds row l % 32,
+// k 8*(l/32) .. +8 of the block).  One thread moves one 16-byte chunk.
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ src,
+                                                   uint16_t* __restrict__ dst, int64_t rows,
+                                                   int K) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t kc_per_row = K / 8;
+  if (c >= rows * kc_per_row) return;
+  const int64_t row = c / kc_per_row;
+  const int kc = (int)(c - row * kc_per_row);
+  const int64_t band = row >> 5;
+  const int r = (int)(row & 31);
+  const int kb = kc >> 1, h = kc & 1;
+  const int64_t o = ((band * (K / 16) + kb) * 64 + (r + 32 * h)) * 8;
+  *reinterpret_cast<u32x4*>(dst + o) = *reinterpret_cast<const u32x4*>(src + row * K + kc * 8);
+}
+
+__device__ __forceinline__ int seg_m_tiles(const GemmSeg& g) {
+  return g.tile_off ? *g.num_tiles : (int)((g.single_rows + BM - 1) / BM);
+}
+
+struct Stage {
+  u32x4 a[2], b[8];
+};
+template <int MB>
+struct Frag {
+  bf16x8 a[2][MB], b[2][4];
+};
+
+// Weights row-major: both operands staged through LDS.
+template <bool UP, int MB>
+struct PipeLds {
+  const GemmSeg& g;
+  const uint16_t* b0base;
+  const uint16_t* b1base;
+  uint32_t aoff[2], boff[8];
+  int ns, nr, lane, lc, lr;
+  uint16_t (*sA)[BM * LDK];
+  uint16_t (*sB)[BN * LDK];
+
+  // Slices past the end are clamped to the last one, so the pipeline body
+  // has no branches; those extra loads land in a buffer nobody reads.
+  __device__ __forceinline__ void gload(Stage& st, int s) const {
+    s = s < ns ? s : ns - 1;
+    const uint32_t k0 = (uint32_t)s * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st.a[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      st.b[i] = ld_off<u32x4>((UP && i >= 4) ? b1base : b0base, boff[i] + k0);
+  }
+  __device__ __forceinline__ void sstore(const Stage& st, int buf) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(&sA[buf][(lr + 64 * i) * LDK + lc * 8]) = st.a[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(&sB[buf][(lr + 64 * i) * LDK + lc * 8]) = st.b[i];
+  }
+  __device__ __forceinline__ void rfrag(Frag<MB>& f, int buf) const {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ko = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
+        f.a[kk][mi] =
+            *reinterpret_cast<const bf16x8*>(&sA[buf][(mi * 32 + (lane & 31)) * LDK + ko]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int brow = UP ? ((nb >> 1) * kUpCols + nr + (nb & 1) * 32) : nr + nb * 32;
+        f.b[kk][nb] = *reinterpret_cast<const bf16x8*>(&sB[buf][(brow + (lane & 31)) * LDK + ko]);
+      }
+    }
+  }
+  __device__ __forceinline__ void mma(const Frag<MB>& f, f32x16 (&acc)[4][4]) const {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mi][nb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][mi], f.b[kk][nb], acc[mi][nb], 0, 0, 0);
+  }
+  // One MFMA at a time, interleaved with the fragment reads of the next
+  // slice, then the LDS writes and global loads of later slices.
+  __device__ __forceinline__ static void schedule() {
+    constexpr int nm = 8 * MB, nrd = 2 * (MB + 4);
+#pragma unroll
+    for (int i = 0; i < nm; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      if (i >= nm - 12 && i < nm - 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      if (i >= nm - 10) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+  }
+  __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) const {
+    Stage R;
+    Frag<MB> F0, F1;
+    gload(R, 0);
+    sstore(R, 0);
+    gload(R, 1);
+    sstore(R, 1);
+    __syncthreads();
+    rfrag(F0, 0);
+    gload(R, 2);
+    int s = 0;
+    for (; s + 2 <= ns; s += 2) {
+      // F0 = slice s; LDS buffer 1 = slice s+1; R = slice s+2 in flight
+      mma(F0, acc);
+      rfrag(F1, 1);
+      sstore(R, 0);
+      gload(R, s + 3);
+      schedule();
+      __syncthreads();
+      // F1 = slice s+1; LDS buffer 0 = slice s+2; R = slice s+3 in flight
+      mma(F1, acc);
+      rfrag(F0, 0);
+      sstore(R, 1);
+      gload(R, s + 4);
+      schedule();
+      __syncthreads();
+    }
+    if (s < ns) mma(F0, acc);  // odd slice count
+  }
+};
+
+// Weights in the packed layout (see pack_kernel): each wave loads its own
+// weight fragments straight into registers with coalesced 1 KB loads, two
+// slices ahead; only the activations (shared by the 4 waves) go through LDS.
 template <bool UP>
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
+struct PipePacked {
+  const GemmSeg& g;
+  const uint16_t* bb[4];
+  uint32_t bo[4];
+  uint32_t aoff[2];
+  int ns, lane, lc, lr;
+  uint16_t (*sA)[BM * LDK];
+
+  struct StageA {
+    u32x4 a[2];
+  };
+  struct FragA {
+    bf16x8 a[2][4];
+  };
+  struct FragB {
+    bf16x8 b[2][4];
+  };
+
+  __device__ __forceinline__ int clampk(int s) const { return s < ns ? s : ns - 1; }
+  __device__ __forceinline__ void aload(StageA& st, int s) const {
+    const uint32_t k0 = (uint32_t)clampk(s) * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st.a[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
+  }
+  __device__ __forceinline__ void bload(FragB& f, int s) const {
+    const uint32_t kb = (uint32_t)clampk(s) * 2;  // 16-wide k blocks
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) f.b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + (kb + kk) * 1024u);
+  }
+  __device__ __forceinline__ void astore(const StageA& st, int buf) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(&sA[buf][(lr + 64 * i) * LDK + lc * 8]) = st.a[i];
+  }
+  __device__ __forceinline__ void rfrag(FragA& f, int buf) const {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ko = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        f.a[kk][mi] =
+            *reinterpret_cast<const bf16x8*>(&sA[buf][(mi * 32 + (lane & 31)) * LDK + ko]);
+    }
+  }
+  __device__ __forceinline__ static void mma(const FragA& fa, const FragB& fb,
+                                             f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mi][nb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa.a[kk][mi], fb.b[kk][nb], acc[mi][nb], 0, 0, 0);
+  }
+  __device__ __forceinline__ static void schedule() {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
+      if (i >= 8 && i < 10) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      if (i >= 12 && i < 22) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+    }
+  }
+  __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) const {
+    StageA R;
+    FragA A0, A1;
+    FragB B0, B1;
+    aload(R, 0);
+    astore(R, 0);
+    aload(R, 1);
+    astore(R, 1);
+    bload(B0, 0);
+    bload(B1, 1);
+    __syncthreads();
+    rfrag(A0, 0);
+    aload(R, 2);
+    int s = 0;
+    for (; s + 2 <= ns; s += 2) {
+      // A0, B0 = slice s; LDS buffer 1 = activations of slice s+1; B1 in
+      // flight for slice s+1; R = activations of slice s+2 in flight
+      mma(A0, B0, acc);
+      rfrag(A1, 1);
+      astore(R, 0);
+      aload(R, s + 3);
+      bload(B0, s + 2);
+      schedule();
+      __syncthreads();
+      mma(A1, B1, acc);
+      rfrag(A0, 0);
+      astore(R, 1);
+      aload(R, s + 4);
+      bload(B1, s + 3);
+      schedule();
+      __syncthreads();
+    }
+    if (s < ns) mma(A0, B0, acc);  // odd slice count
+  }
+};
+
+template <bool UP, bool PACKED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
 
-  int num_m;
-  if (g.tile_off)
-    num_m = *g.num_tiles;
-  else
-    num_m = (int)((g.single_rows + BM - 1) / BM);
-  const int G = num_m * g.nN;
+  const int G0 = seg_m_tiles(args.seg[0]) * args.seg[0].nN;
+  const int G1 = args.nseg > 1 ? seg_m_tiles(args.seg[1]) * args.seg[1].nN : 0;
+  const int G = G0 + G1;
   if ((int)blockIdx.x >= G) return;
-  const int L = xcd_remap((int)blockIdx.x, G);
+  int L = xcd_remap((int)blockIdx.x, G);
+  const int si = L < G0 ? 0 : 1;
+  if (si) L -= G0;
+  const GemmSeg& g = args.seg[si];
 
+  // Logical order within a segment: group, then column tile, then M-tile,
+  // so the M-tiles that share a weight tile run next to each other on one XCD.
   int e, nt, row0, rows;
   if (g.tile_off) {
     int lo = 0, hi = g.n_groups;
@@ -76,6 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
     row0 = g.tile_row0[mt];
     rows = g.tile_rows[mt];
   } else {
+    const int num_m = seg_m_tiles(g);
     e = 0;
     nt = L / num_m;
     const int mt = L - nt * num_m;
@@ -84,106 +337,101 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lc = tid & 7, lr = tid >> 3;
-  const uint16_t* ap[4];
-  const uint16_t* bp[4];
+  const int lc = tid & 3, lr = tid >> 2;  // 16-byte chunk of a 32-wide row; row 0..63
+  // 32-bit byte offsets from uniform bases (the ABI keeps every operand
+  // below 2^31 elements).
+  uint32_t aoff[2], boff[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 32 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int r = lr + 64 * i;
     const int rr = r < rows ? r : rows - 1;
     const int64_t grow = (int64_t)row0 + rr;
     const int64_t src = g.a_rows ? (int64_t)g.a_rows[grow] : grow;
-    ap[i] = g.A + src * g.lda + lc * 8;
-    const uint16_t* base;
-    int brow;
-    if (UP) {
-      brow = nt * 64 + (r & 63);
-      base = (r < 64 ? g.B0 : g.B1) + (int64_t)e * g.b_stride;
-    } else {
-      brow = nt * BN + r;
-      base = g.B0 + (int64_t)e * g.b_stride;
+    aoff[i] = ((uint32_t)(src * g.lda) + lc * 8) * 2u;
+  }
+  const uint16_t* b0base = g.B0 + (int64_t)e * g.b_stride;
+  const uint16_t* b1base = UP ? g.B1 + (int64_t)e * g.b_stride : b0base;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = lr + 64 * i;  // tile row 0..511
+    int brow = UP ? nt * kUpCols + (r & (kUpCols - 1)) : nt * BN + r;
+    if (brow > g.N - 1) brow = g.N - 1;  // clamped rows: outputs not stored
+    boff[i] = ((uint32_t)brow * (uint32_t)g.K + lc * 8) * 2u;
+  }
+  // This wave's weight rows inside the tile: up = 64 W1 rows (and the same
+  // 64 W3 rows at +kUpCols), down = 128 W2 rows.
+  const int nr = UP ? wave * 64 : wave * WN;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mi][nb][j] = 0.f;
+
+  // 32-row blocks holding at least one real row (uniform over the block).
+  // The main loop always computes all four: a second loop specialisation
+  // for shorter tiles would not fit the register budget next to this one.
+  const int mblocks = (rows + 31) >> 5;
+  const int ns = g.K / BK;  // K is a multiple of 32
+  if (PACKED) {
+    // Packed weights: 32-row bands of 16-wide k blocks (512 elements each).
+    const uint32_t KB = (uint32_t)(g.K / 16);
+    PipePacked<UP> pipe{g, {}, {}, {aoff[0], aoff[1]}, ns, lane, lc, lr, sA};
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      int brow = UP ? nt * kUpCols + nr + (nb & 1) * 32 : nt * BN + nr + nb * 32;
+      if (brow > g.N - 32) brow = g.N - 32;  // clamped bands: outputs not stored
+      pipe.bb[nb] = (UP && nb >= 2) ? b1base : b0base;
+      pipe.bo[nb] = ((uint32_t)(brow >> 5) * KB * 512u + lane * 8) * 2u;
     }
-    if (brow > g.N - 1) brow = g.N - 1;
-    bp[i] = base + (int64_t)brow * g.K + lc * 8;
+    pipe.run(acc);
+  } else {
+    PipeLds<UP, 4> pipe{g, b0base, b1base, {aoff[0], aoff[1]},
+                        {boff[0], boff[1], boff[2], boff[3], boff[4], boff[5], boff[6], boff[7]},
+                        ns, nr, lane, lc, lr, sA, sB};
+    pipe.run(acc);
   }
 
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[2][2];
+  // Epilogue in two passes of 64 rows through an LDS staging tile (in sB).
+  constexpr int OC = UP ? kUpCols : BN;  // output columns of the tile
+  constexpr int LDO = OC + 8;
+  constexpr int CPR = OC / 8;            // 16-byte chunks per row
+  uint16_t* stile = &sB[0][0];
+  const int cbase = nt * OC;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
-
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-    const bool in = k0 + lc * 8 < g.K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = in ? *reinterpret_cast<const uint4*>(ap[i] + k0) : uint4{0, 0, 0, 0};
-      rb[i] = in ? *reinterpret_cast<const uint4*>(bp[i] + k0) : uint4{0, 0, 0, 0};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lr + 32 * i;
-      *reinterpret_cast<uint4*>(&sA[buf][r * LDK + lc * 8]) = ra[i];
-      *reinterpret_cast<uint4*>(&sB[buf][r * LDK + lc * 8]) = rb[i];
-    }
-  };
-
-  const int nk = (g.K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ko = kk * 16 + (lane >> 5) * 8;
-      bf16x8 af[2], bfv[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(
-            &sA[buf][(wm * 64 + mi * 32 + (lane & 31)) * LDK + ko]);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int nr = UP ? (ni * 64 + wn * 32) : (wn * 64 + ni * 32);
-        bfv[ni] = *reinterpret_cast<const bf16x8*>(&sB[buf][(nr + (lane & 31)) * LDK + ko]);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfv[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
-  }
-
-  // C layout of MFMA 32x32: lane holds column lane % 32 and rows
-  // 8*(j/4) + 4*(lane/32) + j%4 for register j.
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+    for (int mh = 0; mh < 2; ++mh) {
+      const int mi = pass * 2 + mh;
+      if (mi >= mblocks) continue;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int rit = wm * 64 + mi * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-      if (rit >= rows) continue;
-      uint16_t* crow = g.C + ((int64_t)row0 + rit) * g.ldc;
-      if (UP) {
-        const int col = nt * 64 + wn * 32 + (lane & 31);
-        if (col < g.N) crow[col] = f32_to_bf16(silu(acc[mi][0][j]) * acc[mi][1][j]);
-      } else {
+      for (int j = 0; j < 16; ++j) {
+        const int rl = mh * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        if (UP) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = nt * BN + wn * 64 + ni * 32 + (lane & 31);
-          if (col < g.N) crow[col] = f32_to_bf16(acc[mi][ni][j]);
+          for (int nb = 0; nb < 2; ++nb) {
+            const float x = acc[mi][nb][j];
+            const float gate = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+            stile[rl * LDO + nr + nb * 32 + (lane & 31)] = f32_to_bf16(gate * acc[mi][nb + 2][j]);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            stile[rl * LDO + nr + nb * 32 + (lane & 31)] = f32_to_bf16(acc[mi][nb][j]);
         }
       }
+    }
+    __syncthreads();
+    for (int c = tid; c < 64 * CPR; c += kThreads) {
+      const int rl = c / CPR, ch = c - rl * CPR;
+      const int r = pass * 64 + rl;
+      const int col = cbase + ch * 8;
+      if (r < rows && col < g.N)
+        *reinterpret_cast<u32x4*>(g.C + ((int64_t)row0 + r) * g.ldc + col) =
+            *reinterpret_cast<const u32x4*>(&stile[rl * LDO + ch * 8]);
     }
   }
 }
@@ -243,8 +491,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
 
 }  // namespace
 
-static GemmArgs up_args(const FfnArgs& a) {
-  GemmArgs up{};
+static GemmSeg up_seg(const FfnArgs& a) {
+  GemmSeg up{};
   up.A = (const uint16_t*)a.x;
   up.a_rows = a.x_rows;
   up.lda = a.ldx;
@@ -255,7 +503,7 @@ static GemmArgs up_args(const FfnArgs& a) {
   up.N = a.d_ff_g;
   up.C = (uint16_t*)a.hbuf;
   up.ldc = a.d_ff_g;
-  up.nN = (a.d_ff_g + 63) / 64;
+  up.nN = (a.d_ff_g + kUpCols - 1) / kUpCols;
   if (a.tiles) {
     up.tile_row0 = a.tiles->row0;
     up.tile_rows = a.tiles->rows;
@@ -267,8 +515,8 @@ static GemmArgs up_args(const FfnArgs& a) {
   return up;
 }
 
-static GemmArgs down_args(const FfnArgs& a) {
-  GemmArgs dn = up_args(a);
+static GemmSeg down_seg(const FfnArgs& a) {
+  GemmSeg dn = up_seg(a);
   dn.A = (const uint16_t*)a.hbuf;
   dn.a_rows = nullptr;
   dn.lda = a.d_ff_g;
@@ -287,44 +535,81 @@ static int max_m_tiles(const FfnArgs& a) {
   return a.tiles ? a.tiles->max_tiles : (int)((a.rows + BM - 1) / BM);
 }
 
-hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
-  if (a.dtype == 0) {
-    GemmF32Args up{(const float*)a.x, a.x_rows, a.ldx, (const float*)a.w1, (const float*)a.w3,
-                   (int64_t)a.d_ff_g * a.d, a.d, a.d_ff_g, (float*)a.hbuf, a.d_ff_g, a.rows,
-                   a.tiles ? a.offsets : nullptr, a.n_groups};
-    const int64_t n_up = a.rows * a.d_ff_g;
-    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)((n_up + 255) / 256)), dim3(256), 0,
-                       s, up);
-    return hipGetLastError();
+template <bool UP>
+static hipError_t launch_bf16(const FfnArgs* segs, int nseg, bool packed, hipStream_t s) {
+  GemmArgs args{};
+  int grid = 0;
+  args.nseg = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].rows == 0) continue;
+    args.seg[args.nseg] = UP ? up_seg(segs[i]) : down_seg(segs[i]);
+    grid += max_m_tiles(segs[i]) * args.seg[args.nseg].nN;
+    ++args.nseg;
   }
-  const GemmArgs up = up_args(a);
-  hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)(max_m_tiles(a) * up.nN)),
-                     dim3(kThreads), 0, s, up);
+  if (args.nseg == 0) return hipSuccess;
+  if (packed)
+    hipLaunchKernelGGL((gemm_bf16_kernel<UP, true>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       args);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<UP, false>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       args);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) {
+static hipError_t launch_f32(const FfnArgs& a, bool up, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  if (a.dtype == 0) {
-    GemmF32Args dn{(const float*)a.hbuf, nullptr, a.d_ff_g, (const float*)a.w2, nullptr,
-                   (int64_t)a.d * a.d_ff_g, a.d_ff_g, a.d, (float*)a.y, a.d, a.rows,
-                   a.tiles ? a.offsets : nullptr, a.n_groups};
-    const int64_t n_dn = a.rows * a.d;
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)((n_dn + 255) / 256)), dim3(256),
-                       0, s, dn);
-    return hipGetLastError();
+  if (up) {
+    GemmF32Args g{(const float*)a.x, a.x_rows, a.ldx, (const float*)a.w1, (const float*)a.w3,
+                  (int64_t)a.d_ff_g * a.d, a.d, a.d_ff_g, (float*)a.hbuf, a.d_ff_g, a.rows,
+                  a.tiles ? a.offsets : nullptr, a.n_groups};
+    const int64_t n = a.rows * a.d_ff_g;
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       s, g);
+  } else {
+    GemmF32Args g{(const float*)a.hbuf, nullptr, a.d_ff_g, (const float*)a.w2, nullptr,
+                  (int64_t)a.d * a.d_ff_g, a.d_ff_g, a.d, (float*)a.y, a.d, a.rows,
+                  a.tiles ? a.offsets : nullptr, a.n_groups};
+    const int64_t n = a.rows * a.d;
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       s, g);
   }
-  const GemmArgs dn = down_args(a);
-  hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)(max_m_tiles(a) * dn.nN)),
-                     dim3(kThreads), 0, s, dn);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_up(const FfnArgs* segs, int nseg, hipStream_t s) {
+  if (segs[0].dtype == 0) {
+    for (int i = 0; i < nseg; ++i) {
+      const hipError_t e = launch_f32(segs[i], true, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return launch_bf16<true>(segs, nseg, segs[0].packed, s);
+}
+
+hipError_t launch_ffn_down(const FfnArgs* segs, int nseg, hipStream_t s) {
+  if (segs[0].dtype == 0) {
+    for (int i = 0; i < nseg; ++i) {
+      const hipError_t e = launch_f32(segs[i], false, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return launch_bf16<false>(segs, nseg, segs[0].packed, s);
+}
+
+hipError_t launch_pack(const void* src, void* dst, int64_t rows, int K, hipStream_t s) {
+  const int64_t n = rows * (K / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const uint16_t*)src, (uint16_t*)dst, rows, K);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
-  const hipError_t e = launch_ffn_up(a, s);
+  const hipError_t e = launch_ffn_up(&a, 1, s);
   if (e != hipSuccess) return e;
-  return launch_ffn_down(a, s);
+  return launch_ffn_down(&a, 1, s);
 }
 
 }  // namespace moe

@@ -5,7 +5,7 @@
 
 namespace moe {
 
-constexpr int kRouteTok = 64;   // tokens per route block: one wave ballot covers them
+constexpr int kRouteTok = 16;   // tokens per route block (one ballot histogram each)
 constexpr int kTileM = 128;     // rows per grouped-GEMM M-tile
 constexpr int kMaxExperts = 256;
 
@@ -60,10 +60,16 @@ struct FfnArgs {
   const TileList* tiles;   // nullptr: single group of `rows` rows
   void* hbuf;              // [rows][d_ff_g] intermediate
   void* y;                 // [rows][d]
+  bool packed;             // weights in the packed layout (bf16 only)
 };
-hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);   // up then down
-hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);        // hbuf = SwiGLU(x W1, x W3)
-hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);      // y = hbuf W2
+
+// Packs a [rows][K] bf16 matrix (rows % 32 == 0, K % 16 == 0) into the
+// MFMA-block layout the packed grouped FFN reads.
+hipError_t launch_pack(const void* src, void* dst, int64_t rows, int K, hipStream_t s);
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);  // up then down
+// One launch over 1 or 2 segments (e.g. routed experts and shared experts).
+hipError_t launch_ffn_up(const FfnArgs* segs, int nseg, hipStream_t s);    // hbuf = SwiGLU(x W1, x W3)
+hipError_t launch_ffn_down(const FfnArgs* segs, int nseg, hipStream_t s);  // y = hbuf W2
 
 hipError_t launch_combine(int dtype, const void* residual, const void* shared_out,
                           const void* y_perm, const int32_t* slot_of, const float* gate,

@@ -41,12 +41,12 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   const int nch = row_bytes / 16;
-  const uint4* src = reinterpret_cast<const uint4*>(u + t * row_bytes);
+  const u32x4* src = reinterpret_cast<const u32x4*>(u + t * row_bytes);
   for (int c = lane; c < nch; c += 64) {
-    const uint4 v = src[c];
+    const u32x4 v = src[c];
     for (int j = 0; j < k; ++j) {
       const int64_t pj = spos[wave][j];
-      if (pj >= 0) reinterpret_cast<uint4*>(x_perm + pj * row_bytes)[c] = v;
+      if (pj >= 0) reinterpret_cast<u32x4*>(x_perm + pj * row_bytes)[c] = v;
     }
   }
 }

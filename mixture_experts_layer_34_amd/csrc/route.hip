@@ -2,11 +2,13 @@
 // a classic MoE layer"; selection rule of "Top-k routing, from affinities to
 // gates"; statistics of "Expert-level balance loss").
 //
-// One workgroup (4 waves) routes a block of 64 tokens:
-//   1. logits u^T e_i: bf16 MFMA 16x16x32 (fp32 accumulate), each wave owns
-//      16 tokens and all experts; fp32 storage uses plain FMA dot products;
-//   2. a quad of lanes per token does the softmax (max-subtracted) and the
-//      top-k selection on the fp32 logits (descending, ties to the lower
+// One workgroup (8 waves) routes a block of 16 tokens:
+//   1. logits u^T e_i: bf16 MFMA 16x16x32 (fp32 accumulate); the 8 waves
+//      split the hidden dimension so each issues its loads in one batch,
+//      and their partial logits are added in a fixed order; fp32 storage
+//      uses plain FMA dot products;
+//   2. one 16-lane DPP row per token does the softmax (max-subtracted) and
+//      the top-k selection on the fp32 logits (descending, ties to the lower
 //      index), writing indices and gates s_i;
 //   3. per-block partial sums of s_i (ascending token) for P;
 //   4. a wave ballot per expert gives the block histogram and each
@@ -20,50 +22,99 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr size_t kDefaultLds = 64 * 1024;  // dynamic LDS allowed without an attribute
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTailThreads = kRouteTok * 16;  // 16 lanes (one DPP row) per token
+constexpr size_t kDefaultLds = 64 * 1024;    // dynamic LDS allowed without an attribute
 
 struct RouteSmem {
-  float* lg;     // [64][ldl] logits; later reused as int ranks
-  float* mz;     // [64][2] max and softmax denominator
-  int* sidx;     // [64][k] kept experts (-1 for tokens past T)
+  float* part;   // [4][16][ldl] partial logits (waves w and w+4 share slot w)
+  float* lg;     // [16][ldl] logits; later reused as int ranks
+  float* sv;     // [16][ldl] softmax values
+  int* sidx;     // [16][k] kept experts (-1 for tokens past T)
   int ldl;
 };
 
 __device__ __forceinline__ RouteSmem carve(char* smem, int n, int k) {
   RouteSmem s;
   s.ldl = n + 1;
-  s.lg = reinterpret_cast<float*>(smem);
-  s.mz = s.lg + kRouteTok * s.ldl;
-  s.sidx = reinterpret_cast<int*>(s.mz + 2 * kRouteTok);
+  s.part = reinterpret_cast<float*>(smem);
+  s.lg = s.part + 4 * kRouteTok * s.ldl;
+  s.sv = s.lg + kRouteTok * s.ldl;
+  s.sidx = reinterpret_cast<int*>(s.sv + kRouteTok * s.ldl);
   return s;
 }
 
 size_t route_smem_bytes(int n, int k) {
-  return sizeof(float) * (size_t)kRouteTok * (n + 1) + sizeof(float) * 2 * kRouteTok +
-         sizeof(int) * (size_t)kRouteTok * k;
+  return sizeof(float) * (size_t)6 * kRouteTok * (n + 1) + sizeof(int) * (size_t)kRouteTok * k;
 }
 
-// Block histogram and in-block ranks.  Every wave sees all 64 tokens (lane =
-// token) and handles the experts e = wave, wave + 4, ...
+// Cross-lane moves inside a 16-lane DPP row (VALU latency, no LDS crossbar).
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+// Butterfly over a row: xor 1, xor 2 (quad permutes), then the half-row and
+// row mirrors pair the quads and the half-rows; every lane ends with the
+// reduction of all 16.
+constexpr int kQuadX1 = 0xB1, kQuadX2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dppf<kQuadX1>(v));
+  v = fmaxf(v, dppf<kQuadX2>(v));
+  v = fmaxf(v, dppf<kHalfMirror>(v));
+  return fmaxf(v, dppf<kMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dppf<kQuadX1>(v);
+  v += dppf<kQuadX2>(v);
+  v += dppf<kHalfMirror>(v);
+  return v + dppf<kMirror>(v);
+}
+// Arg-max with ties to the lower index (a total order, so the butterfly
+// gives every lane the same winner).
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dppf<CTRL>(v);
+  const int oi = dpp<CTRL>(i);
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ __forceinline__ void row_argmax(float& v, int& i) {
+  argmax_step<kQuadX1>(v, i);
+  argmax_step<kQuadX2>(v, i);
+  argmax_step<kHalfMirror>(v, i);
+  argmax_step<kMirror>(v, i);
+}
+
+// Block histogram and in-block ranks.  Lanes 0..15 of every wave stand for
+// the block's 16 tokens; wave w handles the experts e = w, w + 8, ...
 __device__ void block_hist_rank(const RouteSmem& s, int n, int k, int64_t blk, int64_t T,
                                 int32_t* blk_cnt, int32_t* lrank) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;
-  for (int j = 0; j < k; ++j) {
-    const int e = s.sidx[lane * k + j];
-    if (e < 0) continue;
-    const uint64_t b = 1ull << (e & 63);
-    switch (e >> 6) {
-      case 0: bits0 |= b; break;
-      case 1: bits1 |= b; break;
-      case 2: bits2 |= b; break;
-      default: bits3 |= b; break;
+  if (lane < kRouteTok) {
+    for (int j = 0; j < k; ++j) {
+      const int e = s.sidx[lane * k + j];
+      if (e < 0) continue;
+      const uint64_t b = 1ull << (e & 63);
+      switch (e >> 6) {
+        case 0: bits0 |= b; break;
+        case 1: bits1 |= b; break;
+        case 2: bits2 |= b; break;
+        default: bits3 |= b; break;
+      }
     }
   }
   int* rk = reinterpret_cast<int*>(s.lg);
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int e = wave; e < n; e += 4) {
+  for (int e = wave; e < n; e += kWaves) {
     const int w = e >> 6;
     const uint64_t word = w == 0 ? bits0 : (w == 1 ? bits1 : (w == 2 ? bits2 : bits3));
     const bool has = (word >> (e & 63)) & 1ull;
@@ -81,12 +132,14 @@ __device__ void block_hist_rank(const RouteSmem& s, int n, int k, int64_t blk, i
 }
 
 // bf16 logits with MFMA 16x16x32.  NB = expert blocks of 16 (compile time).
+// Wave w accumulates the 32-wide hidden slices [w*S/8, (w+1)*S/8), loading a
+// chunk of U slices before its MFMAs.
 template <int NB>
 __device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __restrict__ cent,
                             int64_t T, int d, int n, int64_t blk, const RouteSmem& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  int64_t ta = blk * kRouteTok + wave * 16 + r16;
+  int64_t ta = blk * kRouteTok + r16;
   if (ta > T - 1) ta = T - 1;
   const uint16_t* ap = u + ta * d + kq;
   const uint16_t* cp[NB];
@@ -99,26 +152,67 @@ __device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __re
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap + k0);
+  const int S = d / 32;
+  const int s0 = wave * S / kWaves, s1 = (wave + 1) * S / kWaves;
+  constexpr int U = NB <= 4 ? 8 : (NB <= 8 ? 4 : 2);
+  int st = s0;
+  for (; st + U <= s1; st += U) {
+    bf16x8 a[U], b[U][NB];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      a[uu] = *reinterpret_cast<const bf16x8*>(ap + (st + uu) * 32);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        b[uu][nb] = *reinterpret_cast<const bf16x8*>(cp[nb] + (st + uu) * 32);
+    }
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[uu], b[uu][nb], acc[nb], 0, 0, 0);
+  }
+  for (; st < s1; ++st) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap + st * 32);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(cp[nb] + k0);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(cp[nb] + st * 32);
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
     }
   }
-  // C layout: lane holds rows 4*(lane/16) + j, column lane % 16.
+  // C layout: lane holds rows 4*(lane/16) + j, column lane % 16.  Waves 4..7
+  // store first, waves 0..3 add theirs on top, then the four slots are added
+  // in a fixed order.
+  const int stride = kRouteTok * s.ldl;
+  float* part = s.part + (wave & 3) * stride;
+  if (wave >= 4) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = nb * 16 + r16;
-    if (col < n) {
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = nb * 16 + r16;
+      if (col < n) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wave * 16 + (lane >> 4) * 4 + j;
-        s.lg[row * s.ldl + col] = acc[nb][j];
+        for (int j = 0; j < 4; ++j) part[((lane >> 4) * 4 + j) * s.ldl + col] = acc[nb][j];
       }
     }
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = nb * 16 + r16;
+      if (col < n) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float* q = part + ((lane >> 4) * 4 + j) * s.ldl + col;
+          *q = acc[nb][j] + *q;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < kRouteTok * n; p += kThreads) {
+    const int tl = p / n, e = p - tl * n;
+    const int o = tl * s.ldl + e;
+    s.lg[o] = ((s.part[o] + s.part[stride + o]) + s.part[2 * stride + o]) + s.part[3 * stride + o];
   }
 }
 
@@ -142,54 +236,46 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
                            int32_t* __restrict__ blk_cnt, float* __restrict__ blk_P,
                            int32_t* __restrict__ lrank) {
   const int tid = threadIdx.x;
-  {
-    const int tl = tid >> 2, q = tid & 3;
+  if (tid < kTailThreads) {  // whole waves
+    const int tl = tid >> 4, q = tid & 15;
     const int64_t t = blk * kRouteTok + tl;
     const bool valid = t < T;
     const float* row = s.lg + tl * s.ldl;
+    float* srow = s.sv + tl * s.ldl;
     float mx = -INFINITY;
-    for (int i = q; i < n; i += 4) mx = fmaxf(mx, row[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    for (int i = q; i < n; i += 16) mx = fmaxf(mx, row[i]);
+    mx = row_max(mx);
     float z = 0.f;
-    for (int i = q; i < n; i += 4) z += expf(row[i] - mx);
-    z += __shfl_xor(z, 1);
-    z += __shfl_xor(z, 2);
-    if (q == 0) {
-      s.mz[2 * tl] = mx;
-      s.mz[2 * tl + 1] = z;
+    for (int i = q; i < n; i += 16) {
+      const float ev = expf(row[i] - mx);
+      srow[i] = ev;
+      z += ev;
     }
-    // k rounds of a quad arg-max over the experts not taken yet; each lane
-    // scans its experts q, q+4, ... in ascending order, so a strict '>'
+    z = row_sum(z);
+    for (int i = q; i < n; i += 16) srow[i] = srow[i] / z;
+    // k rounds of a row arg-max over the experts not taken yet; each lane
+    // scans its experts q, q+16, ... in ascending order, so a strict '>'
     // keeps the lower index among equal logits.
-    uint64_t taken = 0;
+    uint32_t taken = 0;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
       int r = 0;
-      for (int i = q; i < n; i += 4, ++r) {
-        if ((taken >> r) & 1ull) continue;
+      for (int i = q; i < n; i += 16, ++r) {
+        if ((taken >> r) & 1u) continue;
         const float v = row[i];
         if (v > bv) {
           bv = v;
           bi = i;
         }
       }
-#pragma unroll
-      for (int off = 1; off <= 2; off <<= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 3) == q) taken |= 1ull << (bi >> 2);
+      row_argmax(bv, bi);
+      if ((bi & 15) == q) taken |= 1u << (bi >> 4);
       if (q == 0) {
         s.sidx[tl * k + j] = valid ? bi : -1;
         if (valid) {
           topk_idx[t * k + j] = bi;
-          topk_gate[t * k + j] = expf(bv - mx) / z;
+          topk_gate[t * k + j] = srow[bi];
         }
       }
     }
@@ -200,11 +286,10 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
     float acc = 0.f;
     for (int tl = 0; tl < kRouteTok; ++tl) {
       if (blk * kRouteTok + tl >= T) break;
-      acc += expf(s.lg[tl * s.ldl + i] - s.mz[2 * tl]) / s.mz[2 * tl + 1];
+      acc += s.sv[tl * s.ldl + i];
     }
     blk_P[blk * n + i] = acc;
   }
-  __syncthreads();
   block_hist_rank(s, n, k, blk, T, blk_cnt, lrank);
 }
 
@@ -252,27 +337,29 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
 
 // ---------------------------------------------------------------- scans
 
-// Exclusive scan of v[0..cnt) in LDS by the first `cnt` threads' values;
-// returns the exclusive prefix for this thread and stores the total.
-// All threads of the block must call it.  buf holds >= 1024 ints.
-__device__ int block_exclusive_scan(int v, int cnt, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  const int nt = blockDim.x;
-  buf[tid] = tid < cnt ? v : 0;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+// Exclusive scan over the first 256 threads (4 whole waves) of one value
+// each; every thread of the block must call it.  wsum holds >= 4 ints.
+__device__ int scan256(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+  if (tid < 256) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
   }
-  const int incl = buf[tid];
-  if (tid == nt - 1) *total = incl;
   __syncthreads();
-  return incl - (tid < cnt ? v : 0);
+  int pre = 0;
+  if (tid < 256)
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+  if (tid == 255) *total = pre + incl;
+  __syncthreads();
+  return pre + incl - v;
 }
 
-// Writes the M-tiles of group g (rows cnt starting at grouped row first).
+// Writes the M-tiles of one group (rows cnt starting at grouped row first).
 __device__ __forceinline__ void emit_tiles(const TileList& tl, int first_tile, int first_row,
                                            int cnt) {
   int tile = first_tile;
@@ -283,16 +370,19 @@ __device__ __forceinline__ void emit_tiles(const TileList& tl, int first_tile, i
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 32;  // block counts a thread keeps in registers
 
+// Column scan of the [B][n] block histograms.  Thread (e, c) owns expert e
+// and a chunk of consecutive blocks; its counts stay in registers between
+// the sum and the write of the per-block bases.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_cnt, const float* __restrict__ blk_P, int B, int64_t T,
     int n, int k, int32_t* __restrict__ counts, float* __restrict__ f, float* __restrict__ P,
     int32_t* __restrict__ offsets, int32_t* __restrict__ blk_base, TileList tl, int has_tiles) {
   __shared__ int csum[kScanThreads];
   __shared__ float psum[kScanThreads];
-  __shared__ int sbuf[kScanThreads];
-  __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts];
+  __shared__ int wsum[4];
   __shared__ int s_total;
   const int tid = threadIdx.x;
   int C = kScanThreads / n;
@@ -302,43 +392,55 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   const int e = tid % n, c = tid / n;
   const bool act = c < C;
   const int b0 = c * per, b1 = (c + 1) * per < B ? (c + 1) * per : B;
+  const bool cached = per <= kScanPer;
+  int v[kScanPer];
+  int cs = 0;
+  float ps = 0.f;
   if (act) {
-    int cs = 0;
-    float ps = 0.f;
-    for (int b = b0; b < b1; ++b) {
-      cs += blk_cnt[(int64_t)b * n + e];
-      if (blk_P) ps += blk_P[(int64_t)b * n + e];
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) {
+        v[i] = b0 + i < b1 ? blk_cnt[(int64_t)(b0 + i) * n + e] : 0;
+        cs += v[i];
+      }
+      if (blk_P) {
+#pragma unroll
+        for (int i = 0; i < kScanPer; ++i)
+          if (b0 + i < b1) ps += blk_P[(int64_t)(b0 + i) * n + e];
+      }
+    } else {
+      for (int b = b0; b < b1; ++b) {
+        cs += blk_cnt[(int64_t)b * n + e];
+        if (blk_P) ps += blk_P[(int64_t)b * n + e];
+      }
     }
     csum[c * n + e] = cs;
     psum[c * n + e] = ps;
   }
   __syncthreads();
+  int pre = 0;  // rows of this expert in earlier chunks
+  if (act)
+    for (int cc = 0; cc < c; ++cc) pre += csum[cc * n + e];
+  int cnt_e = 0;
   if (tid < n) {
-    int run = 0;
     float pr = 0.f;
     for (int cc = 0; cc < C; ++cc) {
-      const int v = csum[cc * n + tid];
-      csum[cc * n + tid] = run;
-      run += v;
+      cnt_e += csum[cc * n + tid];
       pr += psum[cc * n + tid];
     }
-    s_cnt[tid] = run;
-    if (counts) counts[tid] = run;
-    if (f) f[tid] = (float)((int64_t)run * n) / (float)((int64_t)k * T);
+    if (counts) counts[tid] = cnt_e;
+    if (f) f[tid] = (float)((int64_t)cnt_e * n) / (float)((int64_t)k * T);
     if (P && blk_P) P[tid] = pr / (float)T;
   }
-  __syncthreads();
-  const int cnt_e = tid < n ? s_cnt[tid] : 0;
-  const int off_e = block_exclusive_scan(cnt_e, n, sbuf, &s_total);
+  const int off_e = scan256(cnt_e, wsum, &s_total);
   if (tid < n) {
     s_off[tid] = off_e;
     offsets[tid] = off_e;
   }
   if (tid == 0) offsets[n] = s_total;
-  __syncthreads();
   if (has_tiles) {
     const int nt_e = tid < n ? (cnt_e + kTileM - 1) / kTileM : 0;
-    const int toff = block_exclusive_scan(nt_e, n, sbuf, &s_total);
+    const int toff = scan256(nt_e, wsum, &s_total);
     if (tid < n) {
       tl.off[tid] = toff;
       emit_tiles(tl, toff, off_e, cnt_e);
@@ -347,12 +449,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
       tl.off[n] = s_total;
       *tl.count = s_total;
     }
+  } else {
+    __syncthreads();
   }
   if (act) {
-    int base = s_off[e] + csum[c * n + e];
-    for (int b = b0; b < b1; ++b) {
-      blk_base[(int64_t)b * n + e] = base;
-      base += blk_cnt[(int64_t)b * n + e];
+    int base = s_off[e] + pre;
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) {
+        if (b0 + i < b1) blk_base[(int64_t)(b0 + i) * n + e] = base;
+        base += v[i];
+      }
+    } else {
+      for (int b = b0; b < b1; ++b) {
+        blk_base[(int64_t)b * n + e] = base;
+        base += blk_cnt[(int64_t)b * n + e];
+      }
     }
   }
 }
@@ -364,7 +476,7 @@ constexpr int kTileThreads = 256;
 // the tile capacity.
 __global__ __launch_bounds__(kTileThreads) void tiles_kernel(const int32_t* __restrict__ offsets,
                                                              int G, int64_t rows, TileList tl) {
-  __shared__ int sbuf[kTileThreads];
+  __shared__ int wsum[4];
   __shared__ int s_total;
   const int tid = threadIdx.x;
   int first = 0, cnt = 0;
@@ -376,7 +488,7 @@ __global__ __launch_bounds__(kTileThreads) void tiles_kernel(const int32_t* __re
     cnt = (int)(hi - lo);
   }
   const int nt_g = (cnt + kTileM - 1) / kTileM;
-  const int toff = block_exclusive_scan(nt_g, G, sbuf, &s_total);
+  const int toff = scan256(nt_g, wsum, &s_total);
   if (tid < G) {
     tl.off[tid] = toff;
     emit_tiles(tl, toff, first, cnt);

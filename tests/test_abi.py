@@ -75,6 +75,8 @@ def test_status_strings():
     (dict(N=257, m=1, K=1, K_s=0), "n > 256"),
     (dict(N=128, m=1, K=65, K_s=0), "k > 64"),
     (dict(T=1 << 29, N=64, m=1, K=8, K_s=0), "T*k overflows int32"),
+    (dict(T=1 << 17, d=4096), "T*k*d reaches 2^31 elements"),
+    (dict(T=1 << 18, d=64, d_ff=1408), "T*k*d_ff reaches 2^31 elements"),
 ])
 def test_shape_validation(kw, why):
     p = p16(**kw)
@@ -131,20 +133,37 @@ def test_grouped_ffn_checks():
     ws = moe.moe_workspace_bytes(p)
     R = p.T * 6
     ok = [A] * 5
-    assert status(moe.moe_grouped_ffn, p, 0, R, *ok, 1408, A, A, ws) == "MOE_ERR_SHAPE"
-    assert status(moe.moe_grouped_ffn, p, 257, R, *ok, 1408, A, A, ws) == "MOE_ERR_SHAPE"
-    assert status(moe.moe_grouped_ffn, p, 64, 0, *ok, 1408, A, A, ws) == "MOE_ERR_SHAPE"
-    assert status(moe.moe_grouped_ffn, p, 64, R, *ok, 1400, A, A, ws) == "MOE_ERR_SHAPE"
-    assert status(moe.moe_grouped_ffn, p, 64, R + 1, *ok, 1408, A, A, ws) == "MOE_ERR_WORKSPACE"
-    assert status(moe.moe_grouped_ffn, p, 64, R, *ok, 1408 * 8, A, A,
-                  ws) == "MOE_ERR_WORKSPACE"
+    st = moe.moe_grouped_ffn
+    assert status(st, p, 0, R, *ok, 1408, 0, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(st, p, 257, R, *ok, 1408, 0, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(st, p, 64, 0, *ok, 1408, 0, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(st, p, 64, R, *ok, 1400, 0, A, A, ws) == "MOE_ERR_SHAPE"
+    assert status(st, p, 64, R, *ok, 1408, 8, A, A, ws) == "MOE_ERR_SHAPE"   # unknown flag
+    assert status(st, p, 64, R + 1, *ok, 1408, 0, A, A, ws) == "MOE_ERR_WORKSPACE"
+    assert status(st, p, 64, R, *ok, 1408 * 8, 0, A, A, ws) == "MOE_ERR_WORKSPACE"
     for i in range(5):
         args = [A] * 5
         args[i] = None
-        assert status(moe.moe_grouped_ffn, p, 64, R, *args, 1408, A, A, ws) == "MOE_ERR_NULL"
+        assert status(st, p, 64, R, *args, 1408, 0, A, A, ws) == "MOE_ERR_NULL"
         args[i] = MIS
-        assert status(moe.moe_grouped_ffn, p, 64, R, *args, 1408, A, A, ws) == "MOE_ERR_ALIGN"
-    assert status(moe.moe_grouped_ffn, p, 64, R, *ok, 1408, None, A, ws) == "MOE_ERR_NULL"
+        assert status(st, p, 64, R, *args, 1408, 0, A, A, ws) == "MOE_ERR_ALIGN"
+    assert status(st, p, 64, R, *ok, 1408, 0, None, A, ws) == "MOE_ERR_NULL"
+    pf = p16(dtype="f32")
+    assert status(st, pf, 64, R, *ok, 1408, moe.MOE_PACKED_WEIGHTS, A, A,
+                  moe.moe_workspace_bytes(pf)) == "MOE_ERR_UNSUPPORTED"
+
+
+def test_pack_weights_checks():
+    p = p16()
+    pk = moe.moe_pack_weights
+    assert status(pk, p16(dtype="f32"), 64, 64, A, A + (1 << 20)) == "MOE_ERR_UNSUPPORTED"
+    assert status(pk, p, 48, 64, A, A + (1 << 20)) == "MOE_ERR_SHAPE"     # rows % 32
+    assert status(pk, p, 64, 48, A, A + (1 << 20)) == "MOE_ERR_SHAPE"     # K % 32
+    assert status(pk, p, 64, 64, A, A + 4096) == "MOE_ERR_SHAPE"          # overlap
+    assert status(pk, p, 64, 64, None, A) == "MOE_ERR_NULL"
+    assert status(pk, p, 64, 64, MIS, A + (1 << 20)) == "MOE_ERR_ALIGN"
+    bad = p16(T=0)
+    assert status(pk, bad, 64, 64, A, A + (1 << 20)) == "MOE_ERR_SHAPE"
 
 
 def test_combine_checks():
@@ -164,7 +183,10 @@ def test_layer_fwd_checks():
     ws = moe.moe_workspace_bytes(p)
     full = [A] * 14
     # bad flag bits
-    assert status(moe.moe_layer_fwd, p, *full, 4, A, ws) == "MOE_ERR_SHAPE"
+    assert status(moe.moe_layer_fwd, p, *full, 8, A, ws) == "MOE_ERR_SHAPE"
+    pf = p16(dtype="f32")
+    assert status(moe.moe_layer_fwd, pf, *full, moe.MOE_PACKED_WEIGHTS, A,
+                  moe.moe_workspace_bytes(pf)) == "MOE_ERR_UNSUPPORTED"
     # shared weights required when K_s > 0 ...
     args = list(full)
     args[5] = None

@@ -63,6 +63,31 @@ class Case:
         self.layer = oracle.layer(self.inp, cfg.N, cfg.m, cfg.K, cfg.K_s, toks=self.toks)
         self.dev = {k: to_device(self.inp[k], "cuda")
                     for k in ("u", "centroids", "w1", "w3", "w2", "ws1", "ws3", "ws2")}
+        self._packed = None
+
+    def weights(self, packed):
+        """Row-major weights, or their packed copies (bf16 only)."""
+        if not packed:
+            return self.dev
+        if self._packed is None:
+            self._packed = dict(self.dev)
+            p = prob(self.cfg)
+            for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2"):
+                t = self.dev[k]
+                if t is None:
+                    continue
+                rows, K = t.numel() // t.shape[-1], t.shape[-1]
+                out = torch.empty_like(t)
+                moe.moe_pack_weights(p, rows, K, t, out)
+                self._packed[k] = out
+            torch.cuda.synchronize()
+        return self._packed
+
+
+def packed_flag(case, packed):
+    if packed and case.cfg.dtype != "bf16":
+        pytest.skip("packed weights are a bf16 layout")
+    return moe.MOE_PACKED_WEIGHTS if packed else 0
 
 
 @pytest.fixture(scope="module", params=NAMES)
@@ -114,16 +139,19 @@ def test_permute(case, gather):
         assert torch.equal(xp, u[want])
 
 
-def test_grouped_ffn_routed(case):
+@pytest.mark.parametrize("packed", [False, True])
+def test_grouped_ffn_routed(case, packed):
     """y_perm[slot_of[t, j]] = FFN_{idx[t, j]}(u_t), ungated."""
     cfg, p, d = case.cfg, prob(case.cfg), "cuda"
+    fl = packed_flag(case, packed)
+    w = case.weights(packed)
     pm = case.perm
     R = cfg.T * cfg.k
     x = case.dev["u"][torch.from_numpy(pm["perm_token"].astype(np.int64)).to(d)].contiguous()
     y = torch.empty((R, cfg.d), dtype=torch_dtype(p), device=d)
     offs = torch.from_numpy(pm["offsets"]).to(d)
-    moe.moe_grouped_ffn(p, cfg.n, R, offs, x, case.dev["w1"], case.dev["w3"], case.dev["w2"],
-                        cfg.d_ff, y, workspace(p, d))
+    moe.moe_grouped_ffn(p, cfg.n, R, offs, x, w["w1"], w["w3"], w["w2"], cfg.d_ff, fl, y,
+                        workspace(p, d))
     torch.cuda.synchronize()
     rows = torch.from_numpy(pm["slot_of"][case.toks].ravel().astype(np.int64)).to(d)
     got = host(y[rows]).reshape(len(case.toks), cfg.k, cfg.d)
@@ -133,19 +161,38 @@ def test_grouped_ffn_routed(case):
         assert rel(got[:, j], want[:, j]) <= exact_tol(cfg), j
 
 
-def test_grouped_ffn_shared(case):
+@pytest.mark.parametrize("packed", [False, True])
+def test_grouped_ffn_shared(case, packed):
     """The K_s shared experts as one dense group of width K_s*d_ff equal the
     oracle's expert-by-expert shared sum."""
     cfg, p, d = case.cfg, prob(case.cfg), "cuda"
     if cfg.K_s == 0:
         pytest.skip("no shared experts")
+    fl = packed_flag(case, packed)
+    w = case.weights(packed)
     s = torch.empty((cfg.T, cfg.d), dtype=torch_dtype(p), device=d)
     offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=d)
-    moe.moe_grouped_ffn(p, 1, cfg.T, offs, case.dev["u"], case.dev["ws1"], case.dev["ws3"],
-                        case.dev["ws2"], cfg.K_s * cfg.d_ff, s, workspace(p, d))
+    moe.moe_grouped_ffn(p, 1, cfg.T, offs, case.dev["u"], w["ws1"], w["ws3"], w["ws2"],
+                        cfg.K_s * cfg.d_ff, fl, s, workspace(p, d))
     torch.cuda.synchronize()
     got = host(s[torch.from_numpy(case.toks).to(d)])
     assert rel(got, case.layer["S"]) <= exact_tol(cfg)
+
+
+def test_pack_layout(case):
+    """moe_pack_weights places element (r, k) of a [rows][K] matrix at
+    band r/32, block k/16, offset ((r%32) + 32*((k%16)/8))*8 + k%8."""
+    cfg = case.cfg
+    if cfg.dtype != "bf16":
+        pytest.skip("bf16 layout")
+    src = case.inp["w2"]
+    rows, K = src.shape[0] * src.shape[1], src.shape[2]
+    a = src.reshape(rows, K)
+    want = (a.reshape(rows // 32, 32, K // 16, 2, 8)      # band, r, kb, h, e
+             .transpose(0, 2, 3, 1, 4)                     # band, kb, h, r, e
+             .reshape(-1))
+    got = case.weights(True)["w2"].view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("terms", ["all", "no_residual", "experts_only"])
@@ -174,7 +221,7 @@ def test_combine(case, terms):
 
 def run_layer(case, flags=0, ws=None):
     cfg, p, d = case.cfg, prob(case.cfg), "cuda"
-    t = case.dev
+    t = case.weights(bool(flags & moe.MOE_PACKED_WEIGHTS))
     h = torch.empty((cfg.T, cfg.d), dtype=torch_dtype(p), device=d)
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=d)
     gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=d)
@@ -188,9 +235,10 @@ def run_layer(case, flags=0, ws=None):
     return dict(h=h, topk_idx=idx, topk_gate=gate, counts=counts, f=f, P=P)
 
 
-def test_layer(case):
+@pytest.mark.parametrize("packed", [False, True])
+def test_layer(case, packed):
     cfg = case.cfg
-    out = run_layer(case)
+    out = run_layer(case, packed_flag(case, packed))
     o = case.layer
     assert np.array_equal(out["topk_idx"].cpu().numpy(), o["topk_idx"])
     assert np.array_equal(out["counts"].cpu().numpy(), o["counts"])
@@ -202,13 +250,14 @@ def test_layer(case):
     assert rel(got, o["h"]) <= exact_tol(cfg)
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("flags", ["no_residual", "no_shared_no_residual"])
-def test_layer_components(case, flags):
+def test_layer_components(case, flags, packed):
     """The residual u and the shared experts dominate |h|; dropping them checks
     the routed sum and the shared sum at their own scale."""
     cfg = case.cfg
     fl = moe.MOE_NO_RESIDUAL | (moe.MOE_NO_SHARED if flags == "no_shared_no_residual" else 0)
-    out = run_layer(case, fl)
+    out = run_layer(case, fl | packed_flag(case, packed))
     o = case.layer
     want = o["ysum"] if flags == "no_residual" else o["ysum"] - o["S"]
     got = host(out["h"][torch.from_numpy(case.toks).to("cuda")])
@@ -217,9 +266,10 @@ def test_layer_components(case, flags):
 
 def test_layer_bitwise_deterministic(case):
     """Two runs (the second on a workspace filled with junk) give identical bits."""
-    a = run_layer(case)
+    fl = moe.MOE_PACKED_WEIGHTS if case.cfg.dtype == "bf16" else 0
+    a = run_layer(case, fl)
     ws = workspace(prob(case.cfg), "cuda")
     ws.fill_(0xA5)
-    b = run_layer(case, ws=ws)
+    b = run_layer(case, fl, ws=ws)
     for k in a:
         assert torch.equal(a[k], b[k]), k
