@@ -206,6 +206,11 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
 /* Static description of a status code. */
 const char *moe_status_str(moe_status s);
 
+/* The hipError_t behind the most recent MOE_ERR_HIP returned on the calling
+ * host thread (0 if none yet).  If text is not NULL, *text receives the HIP
+ * runtime's static description of it.  Diagnostic only; never fails. */
+int moe_last_hip_error(const char **text);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,8 @@ import importlib
 _EXPORTS = ("MOE_BF16", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_NO_RESIDUAL",
             "MOE_NO_SHARED", "MOE_PACKED_WEIGHTS", "MoeError", "moe_combine",
             "moe_grouped_ffn", "moe_layer_fwd", "moe_layer_fwd_marked", "moe_layer_kernels",
-            "moe_pack_weights", "moe_permute", "moe_problem", "moe_route", "moe_status_str",
+            "moe_last_hip_error", "moe_pack_weights", "moe_permute", "moe_problem", "moe_route",
+            "moe_status_str",
             "moe_workspace_bytes", "problem")
 __all__ = list(_EXPORTS)
 

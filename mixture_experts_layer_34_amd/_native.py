@@ -45,6 +45,14 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built: run `python -m mixture_experts_layer_34_amd.build`")
+    # torch ships its own HIP runtime.  Loading it first lets libmoe.so bind
+    # to that same runtime; loading libmoe.so first would pull in a second
+    # one from /opt/rocm, and whichever of the two initialises second finds
+    # no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, PP = ctypes.c_void_p, ctypes.POINTER(moe_problem)
     sz, i32, i64, st = ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
@@ -52,6 +60,8 @@ def _load():
     lib.moe_workspace_bytes.restype = sz
     lib.moe_status_str.argtypes = [st]
     lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
+    lib.moe_last_hip_error.restype = ctypes.c_int
     lib.moe_route.argtypes = [PP, P, P, P, P, P, P, P, P, sz, P]
     lib.moe_route.restype = st
     lib.moe_permute.argtypes = [PP, P, P, P, P, P, P, P, sz, P]
@@ -105,7 +115,18 @@ def _stream(stream):
 
 def _check(fn, status):
     if status != MOE_OK:
-        raise MoeError(fn, status, lib.moe_status_str(status).decode())
+        msg = lib.moe_status_str(status).decode()
+        if STATUS_NAMES.get(status) == "MOE_ERR_HIP":
+            code, text = moe_last_hip_error()
+            msg += f" {code}: {text}"
+        raise MoeError(fn, status, msg)
+
+
+def moe_last_hip_error():
+    """(hipError_t code, description) of the last MOE_ERR_HIP on this thread."""
+    text = ctypes.c_char_p()
+    code = lib.moe_last_hip_error(ctypes.byref(text))
+    return int(code), (text.value or b"").decode()
 
 
 def moe_status_str(status: int) -> str:

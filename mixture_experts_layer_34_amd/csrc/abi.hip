@@ -102,7 +102,14 @@ moe::TileList tiles_of(void* ws, const Layout& L) {
                        at<int32_t>(ws, L.t_off), at<int32_t>(ws, L.t_count), L.max_tiles};
 }
 
-moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+// Last HIP error an entry point hit on this host thread.
+thread_local hipError_t g_last_hip = hipSuccess;
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = e;
+  return MOE_ERR_HIP;
+}
 
 #define MOE_TRY(expr)                                  \
   do {                                                 \
@@ -138,6 +145,11 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
+}
+
+int moe_last_hip_error(const char** text) {
+  if (text) *text = hipGetErrorString(g_last_hip);
+  return (int)g_last_hip;
 }
 
 moe_status moe_route(const moe_problem* p, const void* u, const void* centroids,

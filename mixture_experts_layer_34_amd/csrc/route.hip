@@ -165,6 +165,9 @@ __device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __re
       for (int nb = 0; nb < NB; ++nb)
         b[uu][nb] = *reinterpret_cast<const bf16x8*>(cp[nb] + (st + uu) * 32);
     }
+    // Keep the whole batch in flight: without this fence the scheduler trades
+    // it for a short sliding window to save registers.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int uu = 0; uu < U; ++uu)
 #pragma unroll
@@ -231,6 +234,9 @@ __device__ void logits_f32(const float* __restrict__ u, const float* __restrict_
 }
 
 // Softmax, top-k, P partials, histogram.  Logits are already in s.lg.
+// Lane q of a token's DPP row keeps the logits of experts q, q+16, ... (NB
+// of them) in registers, so the k selection rounds touch no memory.
+template <int NB>
 __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem& s,
                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
                            int32_t* __restrict__ blk_cnt, float* __restrict__ blk_P,
@@ -242,35 +248,47 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
     const bool valid = t < T;
     const float* row = s.lg + tl * s.ldl;
     float* srow = s.sv + tl * s.ldl;
-    float mx = -INFINITY;
-    for (int i = q; i < n; i += 16) mx = fmaxf(mx, row[i]);
+    float v[NB];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int i = q + 16 * r;
+      v[r] = i < n ? row[i] : -INFINITY;
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int r = 1; r < NB; ++r) mx = fmaxf(mx, v[r]);
     mx = row_max(mx);
+    float ev[NB];
     float z = 0.f;
-    for (int i = q; i < n; i += 16) {
-      const float ev = expf(row[i] - mx);
-      srow[i] = ev;
-      z += ev;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      ev[r] = q + 16 * r < n ? expf(v[r] - mx) : 0.f;
+      z += ev[r];
     }
     z = row_sum(z);
-    for (int i = q; i < n; i += 16) srow[i] = srow[i] / z;
-    // k rounds of a row arg-max over the experts not taken yet; each lane
-    // scans its experts q, q+16, ... in ascending order, so a strict '>'
-    // keeps the lower index among equal logits.
-    uint32_t taken = 0;
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+      if (q + 16 * r < n) srow[q + 16 * r] = ev[r] / z;
+    // k rounds of a row arg-max; each lane scans its experts in ascending
+    // order, so a strict '>' keeps the lower index among equal logits, and a
+    // taken expert's logit becomes -inf.
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      int r = 0;
-      for (int i = q; i < n; i += 16, ++r) {
-        if ((taken >> r) & 1u) continue;
-        const float v = row[i];
-        if (v > bv) {
-          bv = v;
-          bi = i;
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        if (v[r] > bv) {
+          bv = v[r];
+          bi = q + 16 * r;
         }
       }
       row_argmax(bv, bi);
-      if ((bi & 15) == q) taken |= 1u << (bi >> 4);
+      if ((bi & 15) == q) {
+        const int rr = bi >> 4;
+#pragma unroll
+        for (int r = 0; r < NB; ++r)
+          if (r == rr) v[r] = -INFINITY;
+      }
       if (q == 0) {
         s.sidx[tl * k + j] = valid ? bi : -1;
         if (valid) {
@@ -283,11 +301,13 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
   __syncthreads();
   // P partial of this block, tokens ascending.
   for (int i = tid; i < n; i += kThreads) {
+    float vals[kRouteTok];
+#pragma unroll
+    for (int tl = 0; tl < kRouteTok; ++tl)
+      vals[tl] = blk * kRouteTok + tl < T ? s.sv[tl * s.ldl + i] : 0.f;
     float acc = 0.f;
-    for (int tl = 0; tl < kRouteTok; ++tl) {
-      if (blk * kRouteTok + tl >= T) break;
-      acc += s.sv[tl * s.ldl + i];
-    }
+#pragma unroll
+    for (int tl = 0; tl < kRouteTok; ++tl) acc += vals[tl];
     blk_P[blk * n + i] = acc;
   }
   block_hist_rank(s, n, k, blk, T, blk_cnt, lrank);
@@ -303,9 +323,10 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
   const int64_t blk = blockIdx.x;
   logits_bf16<NB>(u, cent, T, d, n, blk, s);
   __syncthreads();
-  route_tail(T, n, k, blk, s, topk_idx, topk_gate, blk_cnt, blk_P, lrank);
+  route_tail<NB>(T, n, k, blk, s, topk_idx, topk_gate, blk_cnt, blk_P, lrank);
 }
 
+template <int NB>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     const float* __restrict__ u, const float* __restrict__ cent, int64_t T, int d, int n, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
@@ -315,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
   const int64_t blk = blockIdx.x;
   logits_f32(u, cent, T, d, n, blk, s);
   __syncthreads();
-  route_tail(T, n, k, blk, s, topk_idx, topk_gate, blk_cnt, blk_P, lrank);
+  route_tail<NB>(T, n, k, blk, s, topk_idx, topk_gate, blk_cnt, blk_P, lrank);
 }
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ topk_idx,
@@ -507,18 +528,28 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
                         float* blk_P, int32_t* lrank, hipStream_t s) {
   const int B = (int)((T + kRouteTok - 1) / kRouteTok);
   const size_t sm = route_smem_bytes(n, k);
+  const int nb = (n + 15) / 16;
   if (dtype == 0) {
-    if (sm > kDefaultLds) {
-      const hipError_t e = hipFuncSetAttribute((const void*)route_f32_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(route_f32_kernel, dim3(B), dim3(kThreads), sm, s, (const float*)u,
-                       (const float*)cent, T, d, n, k, topk_idx, topk_gate, blk_cnt, blk_P,
-                       lrank);
+#define MOE_ROUTE_F32(NBV)                                                                     \
+  {                                                                                            \
+    if (sm > kDefaultLds) {                                                                    \
+      const hipError_t e = hipFuncSetAttribute((const void*)route_f32_kernel<NBV>,             \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                                               (int)sm);                                       \
+      if (e != hipSuccess) return e;                                                           \
+    }                                                                                          \
+    hipLaunchKernelGGL(route_f32_kernel<NBV>, dim3(B), dim3(kThreads), sm, s,                  \
+                       (const float*)u, (const float*)cent, T, d, n, k, topk_idx, topk_gate,   \
+                       blk_cnt, blk_P, lrank);                                                 \
+  }
+    if (nb <= 1) MOE_ROUTE_F32(1)
+    else if (nb <= 2) MOE_ROUTE_F32(2)
+    else if (nb <= 4) MOE_ROUTE_F32(4)
+    else if (nb <= 8) MOE_ROUTE_F32(8)
+    else MOE_ROUTE_F32(16)
+#undef MOE_ROUTE_F32
     return hipGetLastError();
   }
-  const int nb = (n + 15) / 16;
 #define MOE_ROUTE_CASE(NBV)                                                                    \
   {                                                                                            \
     if (sm > kDefaultLds) {                                                                    \

@@ -62,6 +62,14 @@ def test_status_strings():
     assert moe.moe_status_str(99) == "unknown status"
 
 
+def test_last_hip_error_starts_clear():
+    # host-side validation failures never touch the HIP error slot
+    p = p16(T=0)
+    assert status(moe.moe_route, p, A, A, A, A, A, A, A, A, BIG) == "MOE_ERR_SHAPE"
+    code, text = moe.moe_last_hip_error()
+    assert code == 0 and text
+
+
 @pytest.mark.parametrize("kw,why", [
     (dict(T=0), "T < 1"),
     (dict(d=48), "d not a multiple of 32"),
@@ -208,3 +216,13 @@ def test_workspace_grows_with_problem():
     b = moe.moe_workspace_bytes(p16(T=8192))
     assert 0 < a < b
     assert a % 256 == 0
+
+
+def test_one_hip_runtime_per_process():
+    # The binding loads torch's HIP runtime before libmoe.so, so the process
+    # maps exactly one libamdhip64 whichever module was imported first.
+    code = ("import mixture_experts_layer_34_amd as m; m.moe_status_str(0); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout
+    assert out.count("libamdhip64") == 1, out
