@@ -67,4 +67,24 @@ __device__ __forceinline__ int xcd_remap(int w, int G) {
   return x * q + (x < r ? x : r) + i;
 }
 
+// Two segments of tiles in one launch: each XCD first takes an even share of
+// segment 1's tiles (the longer ones, so they start early), then a
+// contiguous range of segment 0's tiles.  The shares add up to the number of
+// live workgroups (w < G0 + G1) the round-robin deal gives each XCD.
+__device__ __forceinline__ void xcd_remap2(int w, int G0, int G1, int& seg, int& L) {
+  constexpr int kXcd = 8;
+  const int G = G0 + G1;
+  const int x = w % kXcd, i = w / kXcd;
+  const int q = G / kXcd, r = G % kXcd;
+  const int q1 = G1 / kXcd, r1 = G1 % kXcd;
+  const int s1 = q1 + (x < r1 ? 1 : 0);
+  if (i < s1) {
+    seg = 1;
+    L = x * q1 + (x < r1 ? x : r1) + i;
+  } else {
+    seg = 0;
+    L = (x * q + (x < r ? x : r)) - (x * q1 + (x < r1 ? x : r1)) + (i - s1);
+  }
+}
+
 }  // namespace moe

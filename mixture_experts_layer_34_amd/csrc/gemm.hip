@@ -15,8 +15,11 @@
 // MFMA at a time so the LDS and the matrix cores work concurrently.
 // For the up projection a wave's 128 columns are 64 rows of W1 followed by
 // the same 64 rows of W3, so gate and up values of one output land in the
-// same lane and the SwiGLU is applied in registers.  Outputs leave through
-// an LDS staging tile as coalesced 16-byte stores.
+// same lane and the SwiGLU is applied in registers.  The MFMAs take the
+// weights as their first operand, so each accumulator holds the transposed
+// block: a lane owns one token and four consecutive output columns per
+// register group, which leave as one packed 8-byte LDS write, then through
+// the staging tile as coalesced 16-byte stores.
 // One launch can hold two segments (routed experts from a device tile list,
 // then the shared experts as one group) so both fill the GPU together; no
 // host synchronisation is needed and workgroups beyond the live tile count
@@ -34,6 +37,8 @@ constexpr int BK = 32;              // K slice
 constexpr int LDK = BK + 8;         // padded LDS row (elements): 80 B
 constexpr int kThreads = 256;
 constexpr int kUpCols = BN / 2;     // d_ff columns per up tile (64 per wave)
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 struct GemmSeg {
   const uint16_t* A;
@@ -143,7 +148,7 @@ struct PipeLds {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[mi][nb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][mi], f.b[kk][nb], acc[mi][nb], 0, 0, 0);
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][nb], f.a[kk][mi], acc[mi][nb], 0, 0, 0);
   }
   // One MFMA at a time, interleaved with the fragment reads of the next
   // slice, then the LDS writes and global loads of later slices.
@@ -191,6 +196,13 @@ struct PipeLds {
 // Weights in the packed layout (see pack_kernel): each wave loads its own
 // weight fragments straight into registers with coalesced 1 KB loads, two
 // slices ahead; only the activations (shared by the 4 waves) go through LDS.
+// Every slice is 32 steps, one MFMA each, fenced so the compiler keeps this
+// order: MFMA i covers weight block nb = i/8, k half kk = (i/4)%2, row block
+// mi = i%4 (an accumulator is reused 4 MFMAs later, never back to back).
+//   steps 0-7   read the next slice's activation fragments from LDS
+//   step 8nb+7  reload the two weight fragments of block nb (slice s+2)
+//   step 20     store the staged activations of slice s+2 into LDS
+//   step 22     load the activations of slice s+4 into that staging set
 template <bool UP>
 struct PipePacked {
   const GemmSeg& g;
@@ -200,97 +212,85 @@ struct PipePacked {
   int ns, lane, lc, lr;
   uint16_t (*sA)[BM * LDK];
 
-  struct StageA {
-    u32x4 a[2];
-  };
-  struct FragA {
-    bf16x8 a[2][4];
-  };
-  struct FragB {
-    bf16x8 b[2][4];
-  };
-
   __device__ __forceinline__ int clampk(int s) const { return s < ns ? s : ns - 1; }
-  __device__ __forceinline__ void aload(StageA& st, int s) const {
+  __device__ __forceinline__ void aload(u32x4 (&r)[2], int s) const {
     const uint32_t k0 = (uint32_t)clampk(s) * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) st.a[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
+    for (int i = 0; i < 2; ++i) r[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
   }
-  __device__ __forceinline__ void bload(FragB& f, int s) const {
+  __device__ __forceinline__ void bload(bf16x8 (&b)[2][4], int nb, int s) const {
     const uint32_t kb = (uint32_t)clampk(s) * 2;  // 16-wide k blocks
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) f.b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + (kb + kk) * 1024u);
+    for (int kk = 0; kk < 2; ++kk) b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + (kb + kk) * 1024u);
   }
-  __device__ __forceinline__ void astore(const StageA& st, int buf) const {
+  __device__ __forceinline__ void astore(const u32x4 (&r)[2], int buf) const {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&sA[buf][(lr + 64 * i) * LDK + lc * 8]) = st.a[i];
+      *reinterpret_cast<u32x4*>(&sA[buf][(lr + 64 * i) * LDK + lc * 8]) = r[i];
   }
-  __device__ __forceinline__ void rfrag(FragA& f, int buf) const {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ko = kk * 16 + (lane >> 5) * 8;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        f.a[kk][mi] =
-            *reinterpret_cast<const bf16x8*>(&sA[buf][(mi * 32 + (lane & 31)) * LDK + ko]);
-    }
+  __device__ __forceinline__ void rfrag(bf16x8 (&a)[2][4], int kk, int mi, int buf) const {
+    const int ko = kk * 16 + (lane >> 5) * 8;
+    a[kk][mi] = *reinterpret_cast<const bf16x8*>(&sA[buf][(mi * 32 + (lane & 31)) * LDK + ko]);
   }
-  __device__ __forceinline__ static void mma(const FragA& fa, const FragB& fb,
-                                             f32x16 (&acc)[4][4]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mi][nb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa.a[kk][mi], fb.b[kk][nb], acc[mi][nb], 0, 0, 0);
-  }
-  __device__ __forceinline__ static void schedule() {
+  // One slice: MFMAs on (ac, bc); next slice's fragments into an; weights
+  // of slice s+2 into bc; staged activations rs (slice s+2) into LDS buffer
+  // `buf`, then slice s+4 into rs.
+  __device__ __forceinline__ void slice(int s, int buf, const bf16x8 (&ac)[2][4],
+                                        bf16x8 (&an)[2][4], bf16x8 (&bc)[2][4], u32x4 (&rs)[2],
+                                        f32x16 (&acc)[4][4]) const {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
-      if (i >= 8 && i < 10) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      if (i >= 12 && i < 22) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+      const int nb = i >> 3, kk = (i >> 2) & 1, mi = i & 3;
+      acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[kk][nb], ac[kk][mi], acc[mi][nb],
+                                                            0, 0, 0);
+      if (i < 8) rfrag(an, i >> 2, i & 3, buf ^ 1);
+      if (i == 20) astore(rs, buf);
+      if (i == 22) aload(rs, s + 4);
+      if ((i & 7) == 7) bload(bc, nb, s + 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) const {
-    StageA R;
-    FragA A0, A1;
-    FragB B0, B1;
-    aload(R, 0);
-    astore(R, 0);
-    aload(R, 1);
-    astore(R, 1);
-    bload(B0, 0);
-    bload(B1, 1);
+    u32x4 R0[2], R1[2];
+    bf16x8 A0[2][4], A1[2][4], B0[2][4], B1[2][4];
+    // Issue order mirrors two steady-state slices so the wait counts the
+    // compiler derives at the loop head are the steady-state ones.
+    aload(R0, 0);
+    aload(R1, 1);
+    astore(R0, 0);
+    astore(R1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    bload(B0, 0, 0);
+    bload(B0, 1, 0);
+    aload(R0, 2);
+    bload(B0, 2, 0);
+    bload(B0, 3, 0);
+    bload(B1, 0, 1);
+    bload(B1, 1, 1);
+    aload(R1, 3);
+    bload(B1, 2, 1);
+    bload(B1, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    rfrag(A0, 0);
-    aload(R, 2);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) rfrag(A0, kk, mi, 0);
     int s = 0;
     for (; s + 2 <= ns; s += 2) {
-      // A0, B0 = slice s; LDS buffer 1 = activations of slice s+1; B1 in
-      // flight for slice s+1; R = activations of slice s+2 in flight
-      mma(A0, B0, acc);
-      rfrag(A1, 1);
-      astore(R, 0);
-      aload(R, s + 3);
-      bload(B0, s + 2);
-      schedule();
+      slice(s, 0, A0, A1, B0, R0, acc);
       __syncthreads();
-      mma(A1, B1, acc);
-      rfrag(A0, 0);
-      astore(R, 1);
-      aload(R, s + 4);
-      bload(B1, s + 3);
-      schedule();
+      slice(s + 1, 1, A1, A0, B1, R1, acc);
       __syncthreads();
     }
-    if (s < ns) mma(A0, B0, acc);  // odd slice count
+    if (s < ns) {  // odd slice count: MFMAs only
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int nb = i >> 3, kk = (i >> 2) & 1, mi = i & 3;
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B0[kk][nb], A0[kk][mi],
+                                                              acc[mi][nb], 0, 0, 0);
+      }
+    }
   }
 };
 
@@ -303,9 +303,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   const int G1 = args.nseg > 1 ? seg_m_tiles(args.seg[1]) * args.seg[1].nN : 0;
   const int G = G0 + G1;
   if ((int)blockIdx.x >= G) return;
-  int L = xcd_remap((int)blockIdx.x, G);
-  const int si = L < G0 ? 0 : 1;
-  if (si) L -= G0;
+  int si, L;
+  xcd_remap2((int)blockIdx.x, G0, G1, si, L);
   const GemmSeg& g = args.seg[si];
 
   // Logical order within a segment: group, then column tile, then M-tile,
@@ -395,8 +394,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   }
 
   // Epilogue in two passes of 64 rows through an LDS staging tile (in sB).
+  // The MFMAs computed the transposed tile (weights as the first operand),
+  // so lane l holds token l % 32 of each 32-row block and, per group of four
+  // accumulator registers, four consecutive output columns: one 8-byte LDS
+  // write per group.  The staging row pitch (in 4-byte words) is 2 mod 64,
+  // so the 32 tokens of a write land in distinct bank pairs.
   constexpr int OC = UP ? kUpCols : BN;  // output columns of the tile
-  constexpr int LDO = OC + 8;
+  constexpr int LDO = OC + 4;
   constexpr int CPR = OC / 8;            // 16-byte chunks per row
   uint16_t* stile = &sB[0][0];
   const int cbase = nt * OC;
@@ -407,20 +411,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
     for (int mh = 0; mh < 2; ++mh) {
       const int mi = pass * 2 + mh;
       if (mi >= mblocks) continue;
+      const int tl = mh * 32 + (lane & 31);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int rl = mh * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-        if (UP) {
+      for (int nb = 0; nb < (UP ? 2 : 4); ++nb) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const float x = acc[mi][nb][j];
-            const float gate = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-            stile[rl * LDO + nr + nb * 32 + (lane & 31)] = f32_to_bf16(gate * acc[mi][nb + 2][j]);
+        for (int q = 0; q < 4; ++q) {
+          const int col = nr + nb * 32 + 8 * q + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[mi][nb][4 * q + e];
+            if (UP) {
+              const float gate = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+              v[e] = gate * acc[mi][nb + 2][4 * q + e];
+            } else {
+              v[e] = x;
+            }
           }
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            stile[rl * LDO + nr + nb * 32 + (lane & 31)] = f32_to_bf16(acc[mi][nb][j]);
+          bf16x4 pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          *reinterpret_cast<bf16x4*>(&stile[tl * LDO + col]) = pk;
         }
       }
     }
@@ -429,9 +438,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
       const int rl = c / CPR, ch = c - rl * CPR;
       const int r = pass * 64 + rl;
       const int col = cbase + ch * 8;
-      if (r < rows && col < g.N)
+      if (r < rows && col < g.N) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(&stile[rl * LDO + ch * 8]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&stile[rl * LDO + ch * 8 + 4]);
         *reinterpret_cast<u32x4*>(g.C + ((int64_t)row0 + r) * g.ldc + col) =
-            *reinterpret_cast<const u32x4*>(&stile[rl * LDO + ch * 8]);
+            u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
     }
   }
 }
