@@ -27,12 +27,56 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_16b_T4096.md")
+KERNEL_SOURCES = ("mixture_experts_layer_34_amd/csrc/gemm.hip",
+                  "mixture_experts_layer_34_amd/csrc/common.h",
+                  "mixture_experts_layer_34_amd/csrc/kernels.h")
+COPY_PROBE_BYTES = 512 << 20
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 METRIC = "MoE layer fwd tokens/s + MFMA util % (16B-shaped, 4096 tok); HBM GB/s @64 tok"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter record
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
+    there is no record for it or the GEMM sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            lines = [ln for ln in f if ln.startswith("traffic-record: ")]
+    except OSError:
+        return None
+    sha = kernel_sources_sha256()
+    for ln in lines:
+        rec = json.loads(ln[len("traffic-record: "):])
+        if rec.get("kernel") == kernel and rec.get("sources_sha256") == sha:
+            return rec
+    return None
+
+
+def copy_probe(torch) -> None:
+    """A plain device-to-device copy of known size, for calibrating the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) against a kernel whose traffic
+    is exactly known."""
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 5}), flush=True)
 
 
 class Hip:
@@ -170,12 +214,15 @@ def time_layer(layer: Layer, hip: Hip, steps: int, warmup: int) -> dict:
 
 
 def cpu_baseline(cfg, inp, seconds: float) -> dict:
-    """The oracle on the first T_s tokens of the workload as their own batch."""
+    """The oracle on the first T_s tokens of the workload as their own batch
+    (the whole batch when it fits the time budget).  The probe is large
+    enough to keep every host thread busy, so its per-token cost holds for
+    the sample."""
     import numpy as np
 
     import oracle
     sub = dict(inp)
-    probe = 16
+    probe = min(cfg.T, 256)
     sub["u"] = np.ascontiguousarray(inp["u"][:probe])
     t0 = time.perf_counter()
     oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
@@ -199,6 +246,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is built and timed on a single "
@@ -213,6 +262,9 @@ def main():
     from mixture_experts_layer_34_amd.device import to_device
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     hip = Hip()
     cfg = moe_synth.CONFIGS["16b"]
     log(f"generating inputs for {cfg}")
@@ -251,7 +303,11 @@ def main():
     dom = max(res["kernel_ms"], key=res["kernel_ms"].get)
     dw = work[dom]
     droof = roofline(dw["flop"], dw["bytes"], res["kernel_ms"][dom] * 1e-3)
-    droof["traffic"] = None
+    rec = measured_traffic(dom)
+    droof["traffic"] = rec["bytes_per_launch"] if rec else None
+    if rec:
+        droof["traffic_detail"] = {k: rec[k] for k in ("fetch_bytes", "write_bytes",
+                                                       "copy_scale_fetch", "copy_scale_write")}
     droof["kernel"] = dom
     droof["us_per_launch"] = round(res["kernel_ms"][dom] * 1e3, 2)
     gemm_flop = work["up_swiglu"]["flop"] + work["down"]["flop"]
