@@ -70,9 +70,10 @@ Layout layout(const Dims& d) {
     o += up256(bytes);
     return at;
   };
-  L.blk_cnt = take(B * d.n * 4);
-  L.blk_P = take(B * d.n * 4);
-  L.blk_base = take(B * d.n * 4);
+  const size_t ldn = (size_t)moe::blk_ld(d.n);
+  L.blk_cnt = take(B * ldn * 4);
+  L.blk_P = take(B * ldn * 4);
+  L.blk_base = take(B * ldn * 4);
   L.lrank = take(R * 4);
   L.offsets = take((size_t)(d.n + 1) * 4);
   L.perm_token = take(R * 4);
@@ -104,6 +105,13 @@ moe::TileList tiles_of(void* ws, const Layout& L) {
 
 // Last HIP error an entry point hit on this host thread.
 thread_local hipError_t g_last_hip = hipSuccess;
+
+// Few rows per group (the decode regime): the weight-streaming kernels.
+// The layer also needs few tokens, since the shared experts' weights are
+// streamed once per 32 tokens there.
+bool use_skinny(bool packed, int64_t rows, int n_groups) {
+  return packed && rows <= 16 * (int64_t)n_groups;
+}
 
 moe_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
@@ -218,7 +226,9 @@ moe_status moe_grouped_ffn(const moe_problem* p, int32_t n_groups, int64_t rows,
   if (rows > d.T * d.k || (size_t)rows * d_ff_group > L.hcap) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe::TileList tl = tiles_of(ws, L);
-  if (p->dtype == MOE_BF16) MOE_TRY(moe::launch_tiles(offsets, n_groups, rows, tl, s));
+  const bool skinny = use_skinny(packed, rows, n_groups);
+  if (p->dtype == MOE_BF16 && !skinny)
+    MOE_TRY(moe::launch_tiles(offsets, n_groups, rows, tl, s));
   moe::FfnArgs a{};
   a.dtype = p->dtype;
   a.x = x;
@@ -236,7 +246,12 @@ moe_status moe_grouped_ffn(const moe_problem* p, int32_t n_groups, int64_t rows,
   a.hbuf = at<char>(ws, L.hbuf);
   a.y = y;
   a.packed = packed;
-  MOE_TRY(moe::launch_grouped_ffn(a, s));
+  if (skinny) {
+    MOE_TRY(moe::launch_ffn_skinny(&a, 1, true, s));
+    MOE_TRY(moe::launch_ffn_skinny(&a, 1, false, s));
+  } else {
+    MOE_TRY(moe::launch_grouped_ffn(a, s));
+  }
   return MOE_OK;
 }
 
@@ -392,9 +407,16 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
     sbuf = b.y;
     nseg = 2;
   }
-  MOE_TRY(moe::launch_ffn_up(segs, nseg, s));
-  MOE_TRY(mark());
-  MOE_TRY(moe::launch_ffn_down(segs, nseg, s));
+  const bool skinny = d.T <= 64 && use_skinny(packed, d.T * d.k, d.n);
+  if (skinny) {
+    MOE_TRY(moe::launch_ffn_skinny(segs, nseg, true, s));
+    MOE_TRY(mark());
+    MOE_TRY(moe::launch_ffn_skinny(segs, nseg, false, s));
+  } else {
+    MOE_TRY(moe::launch_ffn_up(segs, nseg, s));
+    MOE_TRY(mark());
+    MOE_TRY(moe::launch_ffn_down(segs, nseg, s));
+  }
   MOE_TRY(mark());
   MOE_TRY(moe::launch_combine(p->dtype, (flags & MOE_NO_RESIDUAL) ? nullptr : u, sbuf,
                               at<char>(ws, L.ybuf), slot_of, topk_gate, h, d.T, d.d, d.k, s));

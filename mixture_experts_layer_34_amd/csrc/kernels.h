@@ -9,6 +9,11 @@ constexpr int kRouteTok = 16;   // tokens per route block (one ballot histogram 
 constexpr int kTileM = 128;     // rows per grouped-GEMM M-tile
 constexpr int kMaxExperts = 256;
 
+// Row pitch (elements) of the per-route-block arrays (block histograms,
+// P partials, per-block bases): n rounded up to 4 so rows hold whole
+// 16-byte vectors; the padding columns hold zeros.
+__host__ __device__ inline int blk_ld(int n) { return (n + 3) & ~3; }
+
 // Device tile list of a grouped problem (built by the scan / tile kernels).
 struct TileList {
   int32_t* row0;    // [max_tiles] first grouped row of each M-tile
@@ -70,6 +75,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);  // up then down
 // One launch over 1 or 2 segments (e.g. routed experts and shared experts).
 hipError_t launch_ffn_up(const FfnArgs* segs, int nseg, hipStream_t s);    // hbuf = SwiGLU(x W1, x W3)
 hipError_t launch_ffn_down(const FfnArgs* segs, int nseg, hipStream_t s);  // y = hbuf W2
+// Same two projections for groups of few rows (packed bf16 weights only):
+// weight streaming with no row tiles; any row count is correct, more than
+// 32 rows in a group re-stream its weights per 32 rows.
+hipError_t launch_ffn_skinny(const FfnArgs* segs, int nseg, bool up, hipStream_t s);
 
 hipError_t launch_combine(int dtype, const void* residual, const void* shared_out,
                           const void* y_perm, const int32_t* slot_of, const float* gate,

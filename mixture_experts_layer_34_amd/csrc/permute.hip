@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
     const int e = topk_idx[t * k + lane];
     int pos = -1;
     if (e >= 0 && e < n) {
-      pos = blk_base[(t / kRouteTok) * n + e] + lrank[t * k + lane];
+      pos = blk_base[(t / kRouteTok) * blk_ld(n) + e] + lrank[t * k + lane];
       if (pos < 0 || pos >= R) pos = -1;
     }
     slot_of[t * k + lane] = pos;

@@ -114,14 +114,16 @@ __device__ void block_hist_rank(const RouteSmem& s, int n, int k, int64_t blk, i
   }
   int* rk = reinterpret_cast<int*>(s.lg);
   const uint64_t below = (1ull << lane) - 1ull;
+  const int ldn = blk_ld(n);
   for (int e = wave; e < n; e += kWaves) {
     const int w = e >> 6;
     const uint64_t word = w == 0 ? bits0 : (w == 1 ? bits1 : (w == 2 ? bits2 : bits3));
     const bool has = (word >> (e & 63)) & 1ull;
     const uint64_t mask = __ballot(has);
-    if (lane == 0) blk_cnt[blk * n + e] = __popcll(mask);
+    if (lane == 0) blk_cnt[blk * ldn + e] = __popcll(mask);
     if (has) rk[lane * s.ldl + e] = __popcll(mask & below);
   }
+  if (tid < ldn - n) blk_cnt[blk * ldn + n + tid] = 0;
   __syncthreads();
   for (int p = tid; p < kRouteTok * k; p += kThreads) {
     const int tl = p / k, j = p - tl * k;
@@ -308,8 +310,9 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
     float acc = 0.f;
 #pragma unroll
     for (int tl = 0; tl < kRouteTok; ++tl) acc += vals[tl];
-    blk_P[blk * n + i] = acc;
+    blk_P[blk * blk_ld(n) + i] = acc;
   }
+  if (tid < blk_ld(n) - n) blk_P[blk * blk_ld(n) + n + tid] = 0.f;
   block_hist_rank(s, n, k, blk, T, blk_cnt, lrank);
 }
 
@@ -391,100 +394,158 @@ __device__ __forceinline__ void emit_tiles(const TileList& tl, int first_tile, i
 }
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanPer = 32;  // block counts a thread keeps in registers
+constexpr int kScanRows = 8;  // 16-byte rows a thread keeps in registers
 
-// Column scan of the [B][n] block histograms.  Thread (e, c) owns expert e
-// and a chunk of consecutive blocks; its counts stay in registers between
-// the sum and the write of the per-block bases.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 shfl_up4(i32x4 v, int off, int width) {
+  return i32x4{__shfl_up(v.x, off, width), __shfl_up(v.y, off, width), __shfl_up(v.z, off, width),
+               __shfl_up(v.w, off, width)};
+}
+__device__ __forceinline__ f32x4v shfl_xor4(f32x4v v, int m, int width) {
+  return f32x4v{__shfl_xor(v.x, m, width), __shfl_xor(v.y, m, width), __shfl_xor(v.z, m, width),
+                __shfl_xor(v.w, m, width)};
+}
+
+// Column scan of the [B][ldn] block histograms.  Thread (e4, c) owns the
+// four experts 4*e4 .. 4*e4+3 (one 16-byte column) over a chunk of
+// consecutive blocks; the C chunks of a column are C consecutive lanes
+// (C a power of two dividing 64), so the prefix over chunks and the column
+// totals are lane shuffles.  Counts stay in registers between the sum and
+// the write of the per-block bases.  Integer sums are exact in any order;
+// the P sums run rows ascending inside a chunk, then a fixed butterfly.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_cnt, const float* __restrict__ blk_P, int B, int64_t T,
     int n, int k, int32_t* __restrict__ counts, float* __restrict__ f, float* __restrict__ P,
     int32_t* __restrict__ offsets, int32_t* __restrict__ blk_base, TileList tl, int has_tiles) {
-  __shared__ int csum[kScanThreads];
-  __shared__ float psum[kScanThreads];
-  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ float s_P[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_toff[kMaxExperts + 1];
   __shared__ int wsum[4];
   __shared__ int s_total;
   const int tid = threadIdx.x;
-  int C = kScanThreads / n;
-  if (C > B) C = B;
-  if (C < 1) C = 1;
+  const int ldn = blk_ld(n), n4 = ldn >> 2;
+  int cmax = kScanThreads / n4;
+  if (cmax > 64) cmax = 64;
+  if (cmax > B) cmax = B;
+  int C = 1;
+  while (C * 2 <= cmax) C *= 2;
   const int per = (B + C - 1) / C;
-  const int e = tid % n, c = tid / n;
-  const bool act = c < C;
-  const int b0 = c * per, b1 = (c + 1) * per < B ? (c + 1) * per : B;
-  const bool cached = per <= kScanPer;
-  int v[kScanPer];
-  int cs = 0;
-  float ps = 0.f;
+  const int e4 = tid / C, c = tid - (tid / C) * C;
+  const bool act = e4 < n4;
+  const int b0 = c * per < B ? c * per : B;
+  const int b1 = b0 + per < B ? b0 + per : B;
+  const bool cached = per <= kScanRows;
+  const int64_t col = 4 * e4;
+  i32x4 v[kScanRows];
+  i32x4 cs = {0, 0, 0, 0};
+  f32x4v ps = {0.f, 0.f, 0.f, 0.f};
   if (act) {
     if (cached) {
 #pragma unroll
-      for (int i = 0; i < kScanPer; ++i) {
-        v[i] = b0 + i < b1 ? blk_cnt[(int64_t)(b0 + i) * n + e] : 0;
+      for (int i = 0; i < kScanRows; ++i) {
+        v[i] = b0 + i < b1 ? *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)(b0 + i) * ldn + col)
+                           : i32x4{0, 0, 0, 0};
         cs += v[i];
       }
       if (blk_P) {
+        f32x4v pv[kScanRows];
 #pragma unroll
-        for (int i = 0; i < kScanPer; ++i)
-          if (b0 + i < b1) ps += blk_P[(int64_t)(b0 + i) * n + e];
+        for (int i = 0; i < kScanRows; ++i)
+          pv[i] = b0 + i < b1
+                      ? *reinterpret_cast<const f32x4v*>(blk_P + (int64_t)(b0 + i) * ldn + col)
+                      : f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kScanRows; ++i) ps += pv[i];
       }
     } else {
       for (int b = b0; b < b1; ++b) {
-        cs += blk_cnt[(int64_t)b * n + e];
-        if (blk_P) ps += blk_P[(int64_t)b * n + e];
+        cs += *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)b * ldn + col);
+        if (blk_P) ps += *reinterpret_cast<const f32x4v*>(blk_P + (int64_t)b * ldn + col);
       }
     }
-    csum[c * n + e] = cs;
-    psum[c * n + e] = ps;
+  }
+  i32x4 incl = cs;
+  for (int off = 1; off < C; off <<= 1) {
+    const i32x4 o = shfl_up4(incl, off, C);
+    if (c >= off) incl += o;
+  }
+  for (int m = C >> 1; m >= 1; m >>= 1) ps += shfl_xor4(ps, m, C);
+  const i32x4 pre = incl - cs;  // rows of these experts in earlier chunks
+  if (act && c == C - 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (col + q < n) s_cnt[col + q] = incl[q];
+  }
+  if (act && c == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (col + q < n) s_P[col + q] = ps[q];
   }
   __syncthreads();
-  int pre = 0;  // rows of this expert in earlier chunks
-  if (act)
-    for (int cc = 0; cc < c; ++cc) pre += csum[cc * n + e];
   int cnt_e = 0;
   if (tid < n) {
-    float pr = 0.f;
-    for (int cc = 0; cc < C; ++cc) {
-      cnt_e += csum[cc * n + tid];
-      pr += psum[cc * n + tid];
-    }
+    cnt_e = s_cnt[tid];
     if (counts) counts[tid] = cnt_e;
     if (f) f[tid] = (float)((int64_t)cnt_e * n) / (float)((int64_t)k * T);
-    if (P && blk_P) P[tid] = pr / (float)T;
+    if (P && blk_P) P[tid] = s_P[tid] / (float)T;
   }
   const int off_e = scan256(cnt_e, wsum, &s_total);
   if (tid < n) {
     s_off[tid] = off_e;
     offsets[tid] = off_e;
   }
-  if (tid == 0) offsets[n] = s_total;
+  if (tid == 0) {
+    s_off[n] = s_total;
+    offsets[n] = s_total;
+  }
   if (has_tiles) {
     const int nt_e = tid < n ? (cnt_e + kTileM - 1) / kTileM : 0;
     const int toff = scan256(nt_e, wsum, &s_total);
     if (tid < n) {
+      s_toff[tid] = toff;
       tl.off[tid] = toff;
-      emit_tiles(tl, toff, off_e, cnt_e);
     }
     if (tid == 0) {
+      s_toff[n] = s_total;
       tl.off[n] = s_total;
       *tl.count = s_total;
     }
-  } else {
-    __syncthreads();
+  }
+  __syncthreads();
+  if (has_tiles) {
+    // Tile t belongs to the last expert whose first tile is <= t.
+    const int total = s_toff[n];
+    for (int t = tid; t < total && t < tl.max_tiles; t += kScanThreads) {
+      int lo = 0, hi = n;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_toff[mid] <= t)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      const int r = (t - s_toff[lo]) * kTileM;
+      tl.row0[t] = s_off[lo] + r;
+      tl.rows[t] = s_cnt[lo] - r < kTileM ? s_cnt[lo] - r : kTileM;
+    }
   }
   if (act) {
-    int base = s_off[e] + pre;
+    i32x4 base;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) base[q] = (col + q < n ? s_off[col + q] : 0) + pre[q];
     if (cached) {
 #pragma unroll
-      for (int i = 0; i < kScanPer; ++i) {
-        if (b0 + i < b1) blk_base[(int64_t)(b0 + i) * n + e] = base;
+      for (int i = 0; i < kScanRows; ++i) {
+        if (b0 + i < b1) *reinterpret_cast<i32x4*>(blk_base + (int64_t)(b0 + i) * ldn + col) = base;
         base += v[i];
       }
     } else {
       for (int b = b0; b < b1; ++b) {
-        blk_base[(int64_t)b * n + e] = base;
-        base += blk_cnt[(int64_t)b * n + e];
+        *reinterpret_cast<i32x4*>(blk_base + (int64_t)b * ldn + col) = base;
+        base += *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)b * ldn + col);
       }
     }
   }

@@ -51,6 +51,15 @@ SMALL = {
     "ragged_f32": moe_synth.MoEConfig("ragged_f32", T=300, d=224, N=16, m=1, K=4, K_s=1,
                                       d_ff=160, dtype="f32"),
     "tiny": moe_synth.CONFIGS["tiny"],
+    # Few rows per expert: the layer and the grouped FFN take the
+    # weight-streaming kernels (K tail: d_ff = 160 is 10 k blocks of 16;
+    # column tails in both projections).
+    "decode_bf16": moe_synth.MoEConfig("decode_bf16", T=40, d=256, N=16, m=2, K=3, K_s=1,
+                                       d_ff=160, dtype="bf16"),
+    # Skewed popularity, no shared experts: some expert gets more than 32
+    # rows, so its weights are streamed once per 32 rows.
+    "decode_skew_bf16": moe_synth.MoEConfig("decode_skew_bf16", T=64, d=128, N=8, m=1, K=2,
+                                            K_s=0, d_ff=96, dtype="bf16", zipf_s=3.0),
 }
 FULL = {k: v for k, v in moe_synth.CONFIGS.items() if k != "tiny"}
 ALL = dict(SMALL, **FULL)

@@ -118,6 +118,18 @@ def test_route(case):
     assert elem_rel(got["P"], ref["P"]) <= p_tol(cfg.T, cfg.d, case.max_abs_logit)
 
 
+def test_decode_cases_cover_their_paths(case):
+    """The few-rows workloads really are few rows per expert, and the skewed
+    one has an expert above 32 rows (several passes over its weights)."""
+    cfg = case.cfg
+    if not cfg.name.startswith("decode"):
+        pytest.skip("not a decode workload")
+    counts = case.route["counts"]
+    assert cfg.T <= 64 and cfg.T * cfg.k <= 16 * cfg.n
+    if cfg.name == "decode_skew_bf16":
+        assert counts.max() > 32
+
+
 @pytest.mark.parametrize("gather", [True, False])
 def test_permute(case, gather):
     cfg, p, d = case.cfg, prob(case.cfg), "cuda"
