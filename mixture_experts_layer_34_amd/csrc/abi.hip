@@ -178,7 +178,7 @@ moe_status moe_route(const moe_problem* p, const void* u, const void* centroids,
                             at<int32_t>(ws, L.lrank), s));
   MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
                            counts, f, P, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.blk_base),
-                           nullptr, s));
+                           nullptr, nullptr, s));
   return MOE_OK;
 }
 
@@ -198,7 +198,7 @@ moe_status moe_permute(const moe_problem* p, const void* u, const int32_t* topk_
   MOE_TRY(moe::launch_hist(topk_idx, d.T, d.n, d.k, at<int32_t>(ws, L.blk_cnt),
                            at<int32_t>(ws, L.lrank), s));
   MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), nullptr, d.T, d.n, d.k, nullptr, nullptr,
-                           nullptr, offsets, at<int32_t>(ws, L.blk_base), nullptr, s));
+                           nullptr, offsets, at<int32_t>(ws, L.blk_base), nullptr, nullptr, s));
   MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
                               d.T, d.n, d.k, perm_token, slot_of, u, x_perm, d.d * d.esize, s));
   return MOE_OK;
@@ -305,8 +305,12 @@ int moe_layer_kernels(const moe_problem* p, int flags, const char** names, int m
   const char* seq[10];
   int c = 0;
   seq[c++] = "route";
-  seq[c++] = "scan";
-  seq[c++] = "scatter";
+  if (moe::scan_fuses_scatter(d.T, d.n, d.k)) {
+    seq[c++] = "scan_scatter";
+  } else {
+    seq[c++] = "scan";
+    seq[c++] = "scatter";
+  }
   // bf16: one launch per projection covers routed and shared experts; fp32
   // runs the two groups back to back inside the same mark.
   seq[c++] = tiled ? "up_swiglu" : "up_swiglu_f32";
@@ -357,12 +361,18 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
                             at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
                             at<int32_t>(ws, L.lrank), s));
   MOE_TRY(mark());
+  // Few (token, slot) pairs: the scan workgroup also scatters them.
+  const bool fuse = moe::scan_fuses_scatter(d.T, d.n, d.k);
+  const moe::ScatterFuse sf{topk_idx, at<int32_t>(ws, L.lrank), perm_token, slot_of};
   MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
-                           counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+                           counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl,
+                           fuse ? &sf : nullptr, s));
   MOE_TRY(mark());
-  MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
-                              d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
-  MOE_TRY(mark());
+  if (!fuse) {
+    MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
+                                d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
+    MOE_TRY(mark());
+  }
   // Routed experts (rows gathered from u through perm_token) and the shared
   // experts (one dense SwiGLU of width K_s*d_ff over all tokens) go through
   // the same launches so their tiles fill the GPU together.

@@ -418,7 +418,9 @@ __device__ __forceinline__ f32x4v shfl_xor4(f32x4v v, int m, int width) {
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_cnt, const float* __restrict__ blk_P, int B, int64_t T,
     int n, int k, int32_t* __restrict__ counts, float* __restrict__ f, float* __restrict__ P,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ blk_base, TileList tl, int has_tiles) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ blk_base, TileList tl, int has_tiles,
+    ScatterFuse sf) {
+  extern __shared__ __attribute__((aligned(16))) int s_base[];  // [B][ldn] when fused
   __shared__ int s_cnt[kMaxExperts];
   __shared__ float s_P[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
@@ -536,18 +538,36 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     i32x4 base;
 #pragma unroll
     for (int q = 0; q < 4; ++q) base[q] = (col + q < n ? s_off[col + q] : 0) + pre[q];
+    int32_t* dst = sf.topk_idx ? s_base : blk_base;
     if (cached) {
 #pragma unroll
       for (int i = 0; i < kScanRows; ++i) {
-        if (b0 + i < b1) *reinterpret_cast<i32x4*>(blk_base + (int64_t)(b0 + i) * ldn + col) = base;
+        if (b0 + i < b1) *reinterpret_cast<i32x4*>(dst + (int64_t)(b0 + i) * ldn + col) = base;
         base += v[i];
       }
     } else {
       for (int b = b0; b < b1; ++b) {
-        *reinterpret_cast<i32x4*>(blk_base + (int64_t)b * ldn + col) = base;
+        *reinterpret_cast<i32x4*>(dst + (int64_t)b * ldn + col) = base;
         base += *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)b * ldn + col);
       }
     }
+  }
+  if (!sf.topk_idx) return;
+  // Scatter to grouped order: (t, j) goes to its block's base for expert e
+  // plus its rank inside the block.  Ids outside [0, n) and positions
+  // outside [0, T*k) break the contract; such slots get slot_of = -1.
+  __syncthreads();
+  const int64_t R = T * k;
+  for (int64_t q = tid; q < R; q += kScanThreads) {
+    const int64_t t = q / k;
+    const int e = sf.topk_idx[q];
+    int pos = -1;
+    if (e >= 0 && e < n) {
+      pos = s_base[(t / kRouteTok) * ldn + e] + sf.lrank[q];
+      if (pos < 0 || pos >= R) pos = -1;
+    }
+    sf.slot_of[q] = pos;
+    if (pos >= 0) sf.perm_token[pos] = (int32_t)t;
   }
 }
 
@@ -646,13 +666,20 @@ hipError_t launch_hist(const int32_t* topk_idx, int64_t T, int n, int k, int32_t
   return hipGetLastError();
 }
 
+bool scan_fuses_scatter(int64_t T, int n, int k) {
+  const int64_t B = (T + kRouteTok - 1) / kRouteTok;
+  return T * k <= 8192 && B * blk_ld(n) * 4 <= (int64_t)kDefaultLds;
+}
+
 hipError_t launch_scan(const int32_t* blk_cnt, const float* blk_P, int64_t T, int n, int k,
                        int32_t* counts, float* f, float* P, int32_t* offsets, int32_t* blk_base,
-                       const TileList* tiles, hipStream_t s) {
+                       const TileList* tiles, const ScatterFuse* fuse, hipStream_t s) {
   const int B = (int)((T + kRouteTok - 1) / kRouteTok);
   TileList tl = tiles ? *tiles : TileList{nullptr, nullptr, nullptr, nullptr, 0};
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_cnt, blk_P, B, T, n, k,
-                     counts, f, P, offsets, blk_base, tl, tiles ? 1 : 0);
+  const ScatterFuse sf = fuse ? *fuse : ScatterFuse{nullptr, nullptr, nullptr, nullptr};
+  const size_t sm = fuse ? (size_t)B * blk_ld(n) * 4 : 0;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), sm, s, blk_cnt, blk_P, B, T, n,
+                     k, counts, f, P, offsets, blk_base, tl, tiles ? 1 : 0, sf);
   return hipGetLastError();
 }
 
