@@ -116,8 +116,8 @@ def kernel_work(cfg, n_active: int, es: int = 2) -> dict:
     w["route"] = dict(flop=2 * T * d * n, bytes=T * d * es + n * d * es + R * 12 + B * n * 12)
     w["scan"] = dict(flop=0, bytes=B * n * 12 + n * 12)
     w["scatter"] = dict(flop=0, bytes=R * 4 * 5 + B * n * 4)
-    # few (token, slot) pairs: one workgroup scans and scatters
-    w["scan_scatter"] = dict(flop=0, bytes=w["scan"]["bytes"] + R * 4 * 4)
+    # scan + scatter in one pass (every workgroup reads the histogram table)
+    w["group"] = dict(flop=0, bytes=B * B * n * 4 + B * n * 4 + R * 4 * 4)
     routed_up = dict(flop=4 * R * d * f,
                      bytes=n_active * 2 * f * d * es + R * d * es + R * f * es + R * 4)
     routed_dn = dict(flop=2 * R * f * d, bytes=n_active * d * f * es + R * f * es + R * d * es)

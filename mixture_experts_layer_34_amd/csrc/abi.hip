@@ -178,7 +178,7 @@ moe_status moe_route(const moe_problem* p, const void* u, const void* centroids,
                             at<int32_t>(ws, L.lrank), s));
   MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
                            counts, f, P, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.blk_base),
-                           nullptr, nullptr, s));
+                           nullptr, s));
   return MOE_OK;
 }
 
@@ -198,7 +198,7 @@ moe_status moe_permute(const moe_problem* p, const void* u, const int32_t* topk_
   MOE_TRY(moe::launch_hist(topk_idx, d.T, d.n, d.k, at<int32_t>(ws, L.blk_cnt),
                            at<int32_t>(ws, L.lrank), s));
   MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), nullptr, d.T, d.n, d.k, nullptr, nullptr,
-                           nullptr, offsets, at<int32_t>(ws, L.blk_base), nullptr, nullptr, s));
+                           nullptr, offsets, at<int32_t>(ws, L.blk_base), nullptr, s));
   MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
                               d.T, d.n, d.k, perm_token, slot_of, u, x_perm, d.d * d.esize, s));
   return MOE_OK;
@@ -305,8 +305,8 @@ int moe_layer_kernels(const moe_problem* p, int flags, const char** names, int m
   const char* seq[10];
   int c = 0;
   seq[c++] = "route";
-  if (moe::scan_fuses_scatter(d.T, d.n, d.k)) {
-    seq[c++] = "scan_scatter";
+  if (moe::group_in_one_pass(d.T, d.n)) {
+    seq[c++] = "group";
   } else {
     seq[c++] = "scan";
     seq[c++] = "scatter";
@@ -361,14 +361,15 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
                             at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
                             at<int32_t>(ws, L.lrank), s));
   MOE_TRY(mark());
-  // Few (token, slot) pairs: the scan workgroup also scatters them.
-  const bool fuse = moe::scan_fuses_scatter(d.T, d.n, d.k);
-  const moe::ScatterFuse sf{topk_idx, at<int32_t>(ws, L.lrank), perm_token, slot_of};
-  MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
-                           counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl,
-                           fuse ? &sf : nullptr, s));
-  MOE_TRY(mark());
-  if (!fuse) {
+  if (moe::group_in_one_pass(d.T, d.n)) {
+    MOE_TRY(moe::launch_group(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
+                              topk_idx, at<int32_t>(ws, L.lrank), counts, f, P, offsets,
+                              perm_token, slot_of, &tl, s));
+    MOE_TRY(mark());
+  } else {
+    MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
+                             counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+    MOE_TRY(mark());
     MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
                                 d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
     MOE_TRY(mark());

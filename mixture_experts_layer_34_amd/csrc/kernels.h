@@ -33,25 +33,19 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
 hipError_t launch_hist(const int32_t* topk_idx, int64_t T, int n, int k, int32_t* blk_cnt,
                        int32_t* lrank, hipStream_t s);
 
-// Scatter done by the scan workgroup itself (few (token, slot) pairs): the
-// per-block bases stay in LDS and perm_token / slot_of are written directly.
-struct ScatterFuse {
-  const int32_t* topk_idx;
-  const int32_t* lrank;
-  int32_t* perm_token;
-  int32_t* slot_of;
-};
-// Whether the scan can carry the scatter for this problem (pair count and
-// LDS for the bases).
-bool scan_fuses_scatter(int64_t T, int n, int k);
-
 // Column scan of the block histograms: counts, f, P (when blk_P), offsets,
-// per-block bases (global blk_base, or used in place for `fuse`), and the
-// M-tile list (when tiles != nullptr).
+// per-block bases, and the M-tile list (when tiles != nullptr).
 hipError_t launch_scan(const int32_t* blk_cnt, const float* blk_P, int64_t T, int n, int k,
                        int32_t* counts, float* f, float* P, int32_t* offsets,
-                       int32_t* blk_base, const TileList* tiles, const ScatterFuse* fuse,
-                       hipStream_t s);
+                       int32_t* blk_base, const TileList* tiles, hipStream_t s);
+
+// Scan and scatter in one pass of one workgroup per route block, for tables
+// small enough that every workgroup reads all of it (group_in_one_pass).
+bool group_in_one_pass(int64_t T, int n);
+hipError_t launch_group(const int32_t* blk_cnt, const float* blk_P, int64_t T, int n, int k,
+                        const int32_t* topk_idx, const int32_t* lrank, int32_t* counts,
+                        float* f, float* P, int32_t* offsets, int32_t* perm_token,
+                        int32_t* slot_of, const TileList* tiles, hipStream_t s);
 
 // Scatter to grouped order (+ optional row gather of u into x_perm).
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank,

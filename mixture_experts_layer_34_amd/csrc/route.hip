@@ -418,9 +418,7 @@ __device__ __forceinline__ f32x4v shfl_xor4(f32x4v v, int m, int width) {
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_cnt, const float* __restrict__ blk_P, int B, int64_t T,
     int n, int k, int32_t* __restrict__ counts, float* __restrict__ f, float* __restrict__ P,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ blk_base, TileList tl, int has_tiles,
-    ScatterFuse sf) {
-  extern __shared__ __attribute__((aligned(16))) int s_base[];  // [B][ldn] when fused
+    int32_t* __restrict__ offsets, int32_t* __restrict__ blk_base, TileList tl, int has_tiles) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ float s_P[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
@@ -538,36 +536,164 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     i32x4 base;
 #pragma unroll
     for (int q = 0; q < 4; ++q) base[q] = (col + q < n ? s_off[col + q] : 0) + pre[q];
-    int32_t* dst = sf.topk_idx ? s_base : blk_base;
     if (cached) {
 #pragma unroll
       for (int i = 0; i < kScanRows; ++i) {
-        if (b0 + i < b1) *reinterpret_cast<i32x4*>(dst + (int64_t)(b0 + i) * ldn + col) = base;
+        if (b0 + i < b1) *reinterpret_cast<i32x4*>(blk_base + (int64_t)(b0 + i) * ldn + col) = base;
         base += v[i];
       }
     } else {
       for (int b = b0; b < b1; ++b) {
-        *reinterpret_cast<i32x4*>(dst + (int64_t)b * ldn + col) = base;
+        *reinterpret_cast<i32x4*>(blk_base + (int64_t)b * ldn + col) = base;
         base += *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)b * ldn + col);
       }
     }
   }
-  if (!sf.topk_idx) return;
-  // Scatter to grouped order: (t, j) goes to its block's base for expert e
-  // plus its rank inside the block.  Ids outside [0, n) and positions
-  // outside [0, T*k) break the contract; such slots get slot_of = -1.
+}
+
+// Grouping in one pass of B workgroups, one per route block: every
+// workgroup reads the whole [B][ldn] histogram table (small: a few tens of
+// KB), forms the per-expert totals and its own block's prefix, hence the
+// expert offsets and its block's bases, and scatters its tokens' (t, j)
+// pairs.  Workgroup 0 also writes counts, f, P, offsets and the M-tile list.
+// Every workgroup derives the same totals (exact integer sums), so no
+// workgroup waits for another.
+constexpr int kGroupThreads = 256;
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(
+    const int32_t* __restrict__ blk_cnt, const float* __restrict__ blk_P, int B, int64_t T,
+    int n, int k, const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
+    int32_t* __restrict__ counts, float* __restrict__ f, float* __restrict__ P,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ slot_of, TileList tl) {
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_toff[kMaxExperts + 1];
+  __shared__ int wsum[4];
+  __shared__ int s_total;
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int ldn = blk_ld(n), n4 = ldn >> 2;
+  int C = 1;  // row chunks per column: a power of two, n4 * C <= 256
+  while (C * 2 * n4 <= kGroupThreads && C * 2 <= 64) C *= 2;
+  const int per = (B + C - 1) / C;
+  const int e4 = tid / C, c = tid - (tid / C) * C;
+  const bool act = e4 < n4;
+  const int r0 = c * per < B ? c * per : B;
+  const int r1 = r0 + per < B ? r0 + per : B;
+  const int64_t col = 4 * e4;
+  i32x4 tot = {0, 0, 0, 0}, pre = {0, 0, 0, 0};
+  if (act) {
+    // eight rows in flight at a time
+    for (int rb = r0; rb < r1; rb += 8) {
+      i32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = rb + i < r1 ? *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)(rb + i) * ldn + col)
+                           : i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tot += v[i];
+        if (rb + i < blk) pre += v[i];
+      }
+    }
+  }
+  for (int m = C >> 1; m >= 1; m >>= 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tot[q] += __shfl_xor(tot[q], m, C);
+      pre[q] += __shfl_xor(pre[q], m, C);
+    }
+  }
+  if (act && c == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (col + q < n) {
+        s_tot[col + q] = tot[q];
+        s_base[col + q] = pre[q];
+      }
+  }
+  // P: workgroup 0 sums the block partials, rows ascending inside a chunk,
+  // then a fixed butterfly over chunks.
+  if (blk == 0 && blk_P) {
+    f32x4v ps = {0.f, 0.f, 0.f, 0.f};
+    if (act)
+      for (int rb = r0; rb < r1; rb += 8) {
+        f32x4v v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          v[i] = rb + i < r1 ? *reinterpret_cast<const f32x4v*>(blk_P + (int64_t)(rb + i) * ldn + col)
+                             : f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ps += v[i];  // rows ascending
+      }
+    for (int m = C >> 1; m >= 1; m >>= 1) ps += shfl_xor4(ps, m, C);
+    if (act && c == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (col + q < n && P) P[col + q] = ps[q] / (float)T;
+    }
+  }
   __syncthreads();
+  const int cnt_e = tid < n ? s_tot[tid] : 0;
+  const int off_e = scan256(cnt_e, wsum, &s_total);
+  if (tid < n) {
+    s_off[tid] = off_e;
+    s_base[tid] += off_e;
+  }
+  if (blk == 0) {
+    if (tid < n) {
+      offsets[tid] = off_e;
+      if (counts) counts[tid] = cnt_e;
+      if (f) f[tid] = (float)((int64_t)cnt_e * n) / (float)((int64_t)k * T);
+    }
+    if (tid == 0) offsets[n] = s_total;
+  }
+  if (tid == 0) s_off[n] = s_total;
+  __syncthreads();
+  // This block's (token, slot) pairs.  Ids outside [0, n) and positions
+  // outside [0, T*k) break the contract; such slots get slot_of = -1.
   const int64_t R = T * k;
-  for (int64_t q = tid; q < R; q += kScanThreads) {
-    const int64_t t = q / k;
-    const int e = sf.topk_idx[q];
+  for (int q = tid; q < kRouteTok * k; q += kGroupThreads) {
+    const int64_t t = (int64_t)blk * kRouteTok + q / k;
+    if (t >= T) break;
+    const int64_t p = t * k + q % k;
+    const int e = topk_idx[p];
     int pos = -1;
     if (e >= 0 && e < n) {
-      pos = s_base[(t / kRouteTok) * ldn + e] + sf.lrank[q];
+      pos = s_base[e] + lrank[p];
       if (pos < 0 || pos >= R) pos = -1;
     }
-    sf.slot_of[q] = pos;
-    if (pos >= 0) sf.perm_token[pos] = (int32_t)t;
+    slot_of[p] = pos;
+    if (pos >= 0) perm_token[pos] = (int32_t)t;
+  }
+  if (blk != 0 || !tl.off) return;
+  // M-tile list (workgroup 0).
+  const int nt_e = tid < n ? (cnt_e + kTileM - 1) / kTileM : 0;
+  const int toff = scan256(nt_e, wsum, &s_total);
+  if (tid < n) {
+    s_toff[tid] = toff;
+    tl.off[tid] = toff;
+  }
+  if (tid == 0) {
+    s_toff[n] = s_total;
+    tl.off[n] = s_total;
+    *tl.count = s_total;
+  }
+  __syncthreads();
+  const int total = s_toff[n];
+  for (int t = tid; t < total && t < tl.max_tiles; t += kGroupThreads) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= t)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int r = (t - s_toff[lo]) * kTileM;
+    tl.row0[t] = s_off[lo] + r;
+    tl.rows[t] = s_tot[lo] - r < kTileM ? s_tot[lo] - r : kTileM;
   }
 }
 
@@ -666,20 +792,29 @@ hipError_t launch_hist(const int32_t* topk_idx, int64_t T, int n, int k, int32_t
   return hipGetLastError();
 }
 
-bool scan_fuses_scatter(int64_t T, int n, int k) {
-  const int64_t B = (T + kRouteTok - 1) / kRouteTok;
-  return T * k <= 8192 && B * blk_ld(n) * 4 <= (int64_t)kDefaultLds;
-}
-
 hipError_t launch_scan(const int32_t* blk_cnt, const float* blk_P, int64_t T, int n, int k,
                        int32_t* counts, float* f, float* P, int32_t* offsets, int32_t* blk_base,
-                       const TileList* tiles, const ScatterFuse* fuse, hipStream_t s) {
+                       const TileList* tiles, hipStream_t s) {
   const int B = (int)((T + kRouteTok - 1) / kRouteTok);
   TileList tl = tiles ? *tiles : TileList{nullptr, nullptr, nullptr, nullptr, 0};
-  const ScatterFuse sf = fuse ? *fuse : ScatterFuse{nullptr, nullptr, nullptr, nullptr};
-  const size_t sm = fuse ? (size_t)B * blk_ld(n) * 4 : 0;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), sm, s, blk_cnt, blk_P, B, T, n,
-                     k, counts, f, P, offsets, blk_base, tl, tiles ? 1 : 0, sf);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_cnt, blk_P, B, T, n, k,
+                     counts, f, P, offsets, blk_base, tl, tiles ? 1 : 0);
+  return hipGetLastError();
+}
+
+bool group_in_one_pass(int64_t T, int n) {
+  const int64_t B = (T + kRouteTok - 1) / kRouteTok;
+  return B * blk_ld(n) <= 32768;  // each workgroup reads the table: at most 128 KB
+}
+
+hipError_t launch_group(const int32_t* blk_cnt, const float* blk_P, int64_t T, int n, int k,
+                        const int32_t* topk_idx, const int32_t* lrank, int32_t* counts,
+                        float* f, float* P, int32_t* offsets, int32_t* perm_token,
+                        int32_t* slot_of, const TileList* tiles, hipStream_t s) {
+  const int B = (int)((T + kRouteTok - 1) / kRouteTok);
+  TileList tl = tiles ? *tiles : TileList{nullptr, nullptr, nullptr, nullptr, 0};
+  hipLaunchKernelGGL(group_kernel, dim3(B), dim3(kGroupThreads), 0, s, blk_cnt, blk_P, B, T, n,
+                     k, topk_idx, lrank, counts, f, P, offsets, perm_token, slot_of, tl);
   return hipGetLastError();
 }
 
