@@ -56,6 +56,11 @@ SMALL = {
     # column tails in both projections).
     "decode_bf16": moe_synth.MoEConfig("decode_bf16", T=40, d=256, N=16, m=2, K=3, K_s=1,
                                        d_ff=160, dtype="bf16"),
+    # 256 experts (the most the library takes) and a histogram table of
+    # 129 route blocks x 256 experts: too big for the one-pass grouping, so
+    # the layer takes the separate scan and scatter kernels.
+    "wide_bf16": moe_synth.MoEConfig("wide_bf16", T=2064, d=64, N=64, m=4, K=2, K_s=1,
+                                     d_ff=32, dtype="bf16"),
     # Skewed popularity, no shared experts: some expert gets more than 32
     # rows, so its weights are streamed once per 32 rows.
     "decode_skew_bf16": moe_synth.MoEConfig("decode_skew_bf16", T=64, d=128, N=8, m=1, K=2,
