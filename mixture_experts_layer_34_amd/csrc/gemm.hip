@@ -31,12 +31,22 @@ namespace moe {
 namespace {
 
 constexpr int BM = kTileM;          // 128 rows (tokens)
-constexpr int WN = 128;             // weight rows per wave
-constexpr int BN = 4 * WN;          // 512 weight rows per tile
 constexpr int BK = 32;              // K slice
 constexpr int LDK = BK + 8;         // padded LDS row (elements): 80 B
 constexpr int kThreads = 256;
-constexpr int kUpCols = BN / 2;     // d_ff columns per up tile (64 per wave)
+
+// Tile width: NBW 32-row weight bands per wave, 4 waves.  NBW = 4 gives
+// 128 x 512 tiles (one workgroup per CU); NBW = 2 gives 128 x 256 tiles
+// with half the accumulators, so two workgroups share a CU and one's
+// prologue and epilogue overlap the other's MFMAs.
+template <int NBW>
+struct Tile {
+  static constexpr int WN = 32 * NBW;  // weight rows per wave
+  static constexpr int BN = 4 * WN;    // weight rows per tile
+  static constexpr int UPC = BN / 2;   // d_ff columns per up tile (W1 + W3 rows)
+};
+constexpr int BN = Tile<4>::BN;       // the row-major-weight pipeline's tile
+constexpr int kUpCols = Tile<4>::UPC;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -196,18 +206,21 @@ struct PipeLds {
 // Weights in the packed layout (see pack_kernel): each wave loads its own
 // weight fragments straight into registers with coalesced 1 KB loads, two
 // slices ahead; only the activations (shared by the 4 waves) go through LDS.
-// Every slice is 32 steps, one MFMA each, fenced so the compiler keeps this
-// order: MFMA i covers weight block nb = i/8, k half kk = (i/4)%2, row block
-// mi = i%4 (an accumulator is reused 4 MFMAs later, never back to back).
-//   steps 0-7   read the next slice's activation fragments from LDS
-//   step 8nb+7  reload the two weight fragments of block nb (slice s+2)
-//   step 20     store the staged activations of slice s+2 into LDS
-//   step 22     load the activations of slice s+4 into that staging set
-template <bool UP>
+// Every slice is 8*NBW steps, one MFMA each, fenced so the compiler keeps
+// this order: MFMA i covers weight band nb = i/8, k half kk = (i/4)%2, row
+// block mi = i%4 (an accumulator is reused 4 MFMAs later, never back to
+// back).
+//   steps 0-7    read the next slice's activation fragments from LDS
+//   step 8nb+7   reload the two weight fragments of band nb (slice s+2)
+//   step kAst    store the staged activations of slice s+2 into LDS
+//   step kAst+2  load the activations of slice s+4 into that staging set
+template <bool UP, int NBW>
 struct PipePacked {
+  static constexpr int kSteps = 8 * NBW;
+  static constexpr int kAst = kSteps - 12 + (NBW == 2 ? 2 : 0);  // 20 (NBW 4), 10 (NBW 2)
   const GemmSeg& g;
-  const uint16_t* bb[4];
-  uint32_t bo[4];
+  const uint16_t* bb[NBW];
+  uint32_t bo[NBW];
   uint32_t aoff[2];
   int ns, lane, lc, lr;
   uint16_t (*sA)[BM * LDK];
@@ -218,7 +231,7 @@ struct PipePacked {
 #pragma unroll
     for (int i = 0; i < 2; ++i) r[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
   }
-  __device__ __forceinline__ void bload(bf16x8 (&b)[2][4], int nb, int s) const {
+  __device__ __forceinline__ void bload(bf16x8 (&b)[2][NBW], int nb, int s) const {
     const uint32_t kb = (uint32_t)clampk(s) * 2;  // 16-wide k blocks
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + (kb + kk) * 1024u);
@@ -236,23 +249,33 @@ struct PipePacked {
   // of slice s+2 into bc; staged activations rs (slice s+2) into LDS buffer
   // `buf`, then slice s+4 into rs.
   __device__ __forceinline__ void slice(int s, int buf, const bf16x8 (&ac)[2][4],
-                                        bf16x8 (&an)[2][4], bf16x8 (&bc)[2][4], u32x4 (&rs)[2],
-                                        f32x16 (&acc)[4][4]) const {
+                                        bf16x8 (&an)[2][4], bf16x8 (&bc)[2][NBW], u32x4 (&rs)[2],
+                                        f32x16 (&acc)[4][NBW]) const {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < kSteps; ++i) {
       const int nb = i >> 3, kk = (i >> 2) & 1, mi = i & 3;
       acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[kk][nb], ac[kk][mi], acc[mi][nb],
                                                             0, 0, 0);
       if (i < 8) rfrag(an, i >> 2, i & 3, buf ^ 1);
-      if (i == 20) astore(rs, buf);
-      if (i == 22) aload(rs, s + 4);
+      if (i == kAst) astore(rs, buf);
+      if (i == kAst + 2) aload(rs, s + 4);
       if ((i & 7) == 7) bload(bc, nb, s + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) const {
+  // Loads of one slice's weights and of the activations four slices on, in
+  // the order a steady-state slice issues them.
+  __device__ __forceinline__ void preload(bf16x8 (&b)[2][NBW], int sb, u32x4 (&r)[2],
+                                          int sa) const {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      bload(b, nb, sb);
+      if (8 * nb + 7 < kAst + 2 && kAst + 2 < 8 * nb + 15) aload(r, sa);
+    }
+  }
+  __device__ __forceinline__ void run(f32x16 (&acc)[4][NBW]) const {
     u32x4 R0[2], R1[2];
-    bf16x8 A0[2][4], A1[2][4], B0[2][4], B1[2][4];
+    bf16x8 A0[2][4], A1[2][4], B0[2][NBW], B1[2][NBW];
     // Issue order mirrors two steady-state slices so the wait counts the
     // compiler derives at the loop head are the steady-state ones.
     aload(R0, 0);
@@ -260,16 +283,8 @@ struct PipePacked {
     astore(R0, 0);
     astore(R1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    bload(B0, 0, 0);
-    bload(B0, 1, 0);
-    aload(R0, 2);
-    bload(B0, 2, 0);
-    bload(B0, 3, 0);
-    bload(B1, 0, 1);
-    bload(B1, 1, 1);
-    aload(R1, 3);
-    bload(B1, 2, 1);
-    bload(B1, 3, 1);
+    preload(B0, 0, R0, 2);
+    preload(B1, 1, R1, 3);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 #pragma unroll
@@ -285,7 +300,7 @@ struct PipePacked {
     }
     if (s < ns) {  // odd slice count: MFMAs only
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < kSteps; ++i) {
         const int nb = i >> 3, kk = (i >> 2) & 1, mi = i & 3;
         acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B0[kk][nb], A0[kk][mi],
                                                               acc[mi][nb], 0, 0, 0);
@@ -294,10 +309,14 @@ struct PipePacked {
   }
 };
 
-template <bool UP, bool PACKED>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
+template <bool UP, bool PACKED, int NBW>
+__global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs args) {
+  using TL = Tile<NBW>;
+  constexpr int OC = UP ? TL::UPC : TL::BN;  // output columns of the tile
+  constexpr int kStage = 64 * (OC + 4);      // epilogue staging tile (elements)
+  constexpr int kSB = PACKED ? kStage : (2 * BN * LDK > kStage ? 2 * BN * LDK : kStage);
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kSB];
 
   const int G0 = seg_m_tiles(args.seg[0]) * args.seg[0].nN;
   const int G1 = args.nseg > 1 ? seg_m_tiles(args.seg[1]) * args.seg[1].nN : 0;
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   const int lc = tid & 3, lr = tid >> 2;  // 16-byte chunk of a 32-wide row; row 0..63
   // 32-bit byte offsets from uniform bases (the ABI keeps every operand
   // below 2^31 elements).
-  uint32_t aoff[2], boff[8];
+  uint32_t aoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = lr + 64 * i;
@@ -350,22 +369,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   }
   const uint16_t* b0base = g.B0 + (int64_t)e * g.b_stride;
   const uint16_t* b1base = UP ? g.B1 + (int64_t)e * g.b_stride : b0base;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = lr + 64 * i;  // tile row 0..511
-    int brow = UP ? nt * kUpCols + (r & (kUpCols - 1)) : nt * BN + r;
-    if (brow > g.N - 1) brow = g.N - 1;  // clamped rows: outputs not stored
-    boff[i] = ((uint32_t)brow * (uint32_t)g.K + lc * 8) * 2u;
-  }
-  // This wave's weight rows inside the tile: up = 64 W1 rows (and the same
-  // 64 W3 rows at +kUpCols), down = 128 W2 rows.
-  const int nr = UP ? wave * 64 : wave * WN;
+  // This wave's weight rows inside the tile: up = UPC/4 W1 rows (and the
+  // same W3 rows), down = WN W2 rows.
+  const int nr = UP ? wave * (TL::UPC / 4) : wave * TL::WN;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NBW];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mi][nb][j] = 0.f;
 
@@ -374,22 +386,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   // for shorter tiles would not fit the register budget next to this one.
   const int mblocks = (rows + 31) >> 5;
   const int ns = g.K / BK;  // K is a multiple of 32
-  if (PACKED) {
+  if constexpr (PACKED) {
     // Packed weights: 32-row bands of 16-wide k blocks (512 elements each).
     const uint32_t KB = (uint32_t)(g.K / 16);
-    PipePacked<UP> pipe{g, {}, {}, {aoff[0], aoff[1]}, ns, lane, lc, lr, sA};
+    PipePacked<UP, NBW> pipe{g, {}, {}, {aoff[0], aoff[1]}, ns, lane, lc, lr, sA};
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      int brow = UP ? nt * kUpCols + nr + (nb & 1) * 32 : nt * BN + nr + nb * 32;
+    for (int nb = 0; nb < NBW; ++nb) {
+      // up: bands 0..NBW/2-1 of W1, then the same bands of W3; down: W2
+      int brow = UP ? nt * TL::UPC + nr + (nb % (NBW / 2)) * 32 : nt * TL::BN + nr + nb * 32;
       if (brow > g.N - 32) brow = g.N - 32;  // clamped bands: outputs not stored
-      pipe.bb[nb] = (UP && nb >= 2) ? b1base : b0base;
+      pipe.bb[nb] = (UP && nb >= NBW / 2) ? b1base : b0base;
       pipe.bo[nb] = ((uint32_t)(brow >> 5) * KB * 512u + lane * 8) * 2u;
     }
     pipe.run(acc);
   } else {
+    static_assert(NBW == 4, "row-major weights take the 128 x 512 tile");
+    uint32_t boff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = lr + 64 * i;  // tile row 0..511
+      int brow = UP ? nt * kUpCols + (r & (kUpCols - 1)) : nt * BN + r;
+      if (brow > g.N - 1) brow = g.N - 1;  // clamped rows: outputs not stored
+      boff[i] = ((uint32_t)brow * (uint32_t)g.K + lc * 8) * 2u;
+    }
     PipeLds<UP, 4> pipe{g, b0base, b1base, {aoff[0], aoff[1]},
                         {boff[0], boff[1], boff[2], boff[3], boff[4], boff[5], boff[6], boff[7]},
-                        ns, nr, lane, lc, lr, sA, sB};
+                        ns, nr, lane, lc, lr, sA,
+                        reinterpret_cast<uint16_t(*)[BN * LDK]>(&sB[0])};
     pipe.run(acc);
   }
 
@@ -399,10 +422,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
   // accumulator registers, four consecutive output columns: one 8-byte LDS
   // write per group.  The staging row pitch (in 4-byte words) is 2 mod 64,
   // so the 32 tokens of a write land in distinct bank pairs.
-  constexpr int OC = UP ? kUpCols : BN;  // output columns of the tile
   constexpr int LDO = OC + 4;
   constexpr int CPR = OC / 8;            // 16-byte chunks per row
-  uint16_t* stile = &sB[0][0];
+  uint16_t* stile = &sB[0];
   const int cbase = nt * OC;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -413,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
       if (mi >= mblocks) continue;
       const int tl = mh * 32 + (lane & 31);
 #pragma unroll
-      for (int nb = 0; nb < (UP ? 2 : 4); ++nb) {
+      for (int nb = 0; nb < (UP ? NBW / 2 : NBW); ++nb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = nr + nb * 32 + 8 * q + 4 * (lane >> 5);
@@ -423,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs args) {
             const float x = acc[mi][nb][4 * q + e];
             if (UP) {
               const float gate = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-              v[e] = gate * acc[mi][nb + 2][4 * q + e];
+              v[e] = gate * acc[mi][nb + NBW / 2][4 * q + e];
             } else {
               v[e] = x;
             }
@@ -503,6 +525,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
 
 }  // namespace
 
+template <int NBW>
 static GemmSeg up_seg(const FfnArgs& a) {
   GemmSeg up{};
   up.A = (const uint16_t*)a.x;
@@ -515,7 +538,7 @@ static GemmSeg up_seg(const FfnArgs& a) {
   up.N = a.d_ff_g;
   up.C = (uint16_t*)a.hbuf;
   up.ldc = a.d_ff_g;
-  up.nN = (a.d_ff_g + kUpCols - 1) / kUpCols;
+  up.nN = (a.d_ff_g + Tile<NBW>::UPC - 1) / Tile<NBW>::UPC;
   if (a.tiles) {
     up.tile_row0 = a.tiles->row0;
     up.tile_rows = a.tiles->rows;
@@ -527,8 +550,9 @@ static GemmSeg up_seg(const FfnArgs& a) {
   return up;
 }
 
+template <int NBW>
 static GemmSeg down_seg(const FfnArgs& a) {
-  GemmSeg dn = up_seg(a);
+  GemmSeg dn = up_seg<NBW>(a);
   dn.A = (const uint16_t*)a.hbuf;
   dn.a_rows = nullptr;
   dn.lda = a.d_ff_g;
@@ -539,7 +563,7 @@ static GemmSeg down_seg(const FfnArgs& a) {
   dn.N = a.d;
   dn.C = (uint16_t*)a.y;
   dn.ldc = a.d;
-  dn.nN = (a.d + BN - 1) / BN;
+  dn.nN = (a.d + Tile<NBW>::BN - 1) / Tile<NBW>::BN;
   return dn;
 }
 
@@ -547,25 +571,33 @@ static int max_m_tiles(const FfnArgs& a) {
   return a.tiles ? a.tiles->max_tiles : (int)((a.rows + BM - 1) / BM);
 }
 
-template <bool UP>
-static hipError_t launch_bf16(const FfnArgs* segs, int nseg, bool packed, hipStream_t s) {
+template <bool UP, bool PACKED, int NBW>
+static hipError_t launch_bf16_t(const FfnArgs* segs, int nseg, hipStream_t s) {
   GemmArgs args{};
   int grid = 0;
   args.nseg = 0;
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].rows == 0) continue;
-    args.seg[args.nseg] = UP ? up_seg(segs[i]) : down_seg(segs[i]);
+    args.seg[args.nseg] = UP ? up_seg<NBW>(segs[i]) : down_seg<NBW>(segs[i]);
     grid += max_m_tiles(segs[i]) * args.seg[args.nseg].nN;
     ++args.nseg;
   }
   if (args.nseg == 0) return hipSuccess;
-  if (packed)
-    hipLaunchKernelGGL((gemm_bf16_kernel<UP, true>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       args);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<UP, false>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       args);
+  hipLaunchKernelGGL((gemm_bf16_kernel<UP, PACKED, NBW>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     s, args);
   return hipGetLastError();
+}
+
+// Packed weights: the up projection takes the 128 x 256 tile (d_ff = 1408
+// is 11 of its column tiles, and two workgroups share a CU), the down
+// projection the 128 x 512 tile.  Row-major weights: 128 x 512 for both.
+template <bool UP>
+static hipError_t launch_bf16(const FfnArgs* segs, int nseg, bool packed, hipStream_t s) {
+  if (!packed) return launch_bf16_t<UP, false, 4>(segs, nseg, s);
+  if constexpr (UP)
+    return launch_bf16_t<true, true, 2>(segs, nseg, s);
+  else
+    return launch_bf16_t<false, true, 4>(segs, nseg, s);
 }
 
 static hipError_t launch_f32(const FfnArgs& a, bool up, hipStream_t s) {
