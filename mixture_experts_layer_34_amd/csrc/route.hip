@@ -48,6 +48,10 @@ __device__ __forceinline__ RouteSmem carve(char* smem, int n, int k) {
 size_t route_smem_bytes(int n, int k) {
   return sizeof(float) * (size_t)6 * kRouteTok * (n + 1) + sizeof(int) * (size_t)kRouteTok * k;
 }
+__host__ __device__ inline size_t route_smem_bytes_aligned(int n, int k) {
+  return ((sizeof(float) * (size_t)6 * kRouteTok * (n + 1) + sizeof(int) * (size_t)kRouteTok * k) +
+          15) & ~(size_t)15;
+}
 
 // Cross-lane moves inside a 16-lane DPP row (VALU latency, no LDS crossbar).
 template <int CTRL>
@@ -136,6 +140,48 @@ __device__ void block_hist_rank(const RouteSmem& s, int n, int k, int64_t blk, i
 // bf16 logits with MFMA 16x16x32.  NB = expert blocks of 16 (compile time).
 // Wave w accumulates the 32-wide hidden slices [w*S/8, (w+1)*S/8), loading a
 // chunk of U slices before its MFMAs.
+// Partial logits of the 8 waves (each over its hidden slices) into s.lg.
+// C layout: lane holds rows 4*(lane/16) + j, column lane % 16.  Waves 4..7
+// store first, waves 0..3 add theirs on top, then the four slots are added
+// in a fixed order.
+template <int NB>
+__device__ __forceinline__ void reduce_partials(const f32x4 (&acc)[NB], int n, const RouteSmem& s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int stride = kRouteTok * s.ldl;
+  float* part = s.part + (wave & 3) * stride;
+  if (wave >= 4) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = nb * 16 + r16;
+      if (col < n) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[((lane >> 4) * 4 + j) * s.ldl + col] = acc[nb][j];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = nb * 16 + r16;
+      if (col < n) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float* q = part + ((lane >> 4) * 4 + j) * s.ldl + col;
+          *q = acc[nb][j] + *q;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < kRouteTok * n; p += kThreads) {
+    const int tl = p / n, e = p - tl * n;
+    const int o = tl * s.ldl + e;
+    s.lg[o] = ((s.part[o] + s.part[stride + o]) + s.part[2 * stride + o]) + s.part[3 * stride + o];
+  }
+}
+
 template <int NB>
 __device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __restrict__ cent,
                             int64_t T, int d, int n, int64_t blk, const RouteSmem& s) {
@@ -184,41 +230,102 @@ __device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __re
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
     }
   }
-  // C layout: lane holds rows 4*(lane/16) + j, column lane % 16.  Waves 4..7
-  // store first, waves 0..3 add theirs on top, then the four slots are added
-  // in a fixed order.
-  const int stride = kRouteTok * s.ldl;
-  float* part = s.part + (wave & 3) * stride;
-  if (wave >= 4) {
+  reduce_partials<NB>(acc, n, s);
+}
+
+// bf16 logits with the hidden dimension staged through LDS (n <= 64, and
+// d <= 2048 so a wave's slices fit one round of loads).  Each wave reads
+// its hidden range in chunks of two 32-wide slices; one load instruction
+// covers 8 rows x 128 contiguous bytes (whole cache lines, where the MFMA
+// operand layout would read 16 rows x 64 bytes), every chunk of the wave is
+// in flight at once, and the wave rewrites each chunk into MFMA operand
+// order in its own LDS region: [activations: 2 blocks][centroids: NB x 2
+// blocks] of 64 lanes x 16 bytes.  Same MFMAs, same per-wave slice order
+// and the same reduction as logits_bf16, so the logits are identical.
+constexpr int kStageChunks = 4;  // chunks of two slices per wave (d <= 2048)
+
+// 16-byte slot j of an operand block lives at slot j ^ (((j >> 4) & 7) << 1):
+// a permutation inside every 64-slot block that spreads both the staging
+// writes (8 rows x 8 pieces per instruction) and the operand reads (64
+// consecutive slots) over all bank groups.
+__device__ __forceinline__ uint32_t stage_slot(uint32_t j) { return j ^ (((j >> 4) & 7u) << 1); }
+
+template <int NB>
+__device__ __forceinline__ int stage_region_bytes() {
+  return (2 + 2 * NB) * 1024;
+}
+
+template <int NB>
+__device__ void logits_bf16_staged(const uint16_t* __restrict__ u,
+                                   const uint16_t* __restrict__ cent, int64_t T, int d, int n,
+                                   int64_t blk, const RouteSmem& s, char* stage) {
+  constexpr int kLdB = 2 * NB;    // centroid load instructions per chunk
+  constexpr int kLd = kLdB + 2;   // + 2 for the 16 token rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  char* reg = stage + wave * stage_region_bytes<NB>();
+  const int S = d / 32;
+  const int s0 = wave * S / kWaves, s1 = (wave + 1) * S / kWaves;
+  const int nsl = s1 - s0;         // this wave's slices (at most 8)
+  const int nch = (nsl + 1) >> 1;  // chunks of two slices
+  const int lr8 = lane >> 3, pc = lane & 7;
+  uint32_t go[kLd], wo[kLd];       // global byte offsets (chunk 0), LDS byte offsets
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = nb * 16 + r16;
-      if (col < n) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) part[((lane >> 4) * 4 + j) * s.ldl + col] = acc[nb][j];
-      }
+  for (int i = 0; i < kLd; ++i) {
+    const int r = (i < kLdB ? i : i - kLdB) * 8 + lr8;  // centroid row / token row
+    const int L = (r & 15) + 16 * (pc & 3), uu = pc >> 2;
+    if (i < kLdB) {
+      const int e = r < n ? r : n - 1;
+      go[i] = ((uint32_t)e * (uint32_t)d + (uint32_t)(s0 * 32 + pc * 8)) * 2u;
+      wo[i] = 2048u + stage_slot((uint32_t)(((r >> 4) * 2 + uu) * 64 + L)) * 16u;
+    } else {
+      int64_t t = blk * kRouteTok + r;
+      if (t > T - 1) t = T - 1;
+      go[i] = ((uint32_t)t * (uint32_t)d + (uint32_t)(s0 * 32 + pc * 8)) * 2u;
+      wo[i] = stage_slot((uint32_t)(uu * 64 + L)) * 16u;
     }
   }
-  __syncthreads();
-  if (wave < 4) {
+  u32x4 buf[kStageChunks][kLd];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = nb * 16 + r16;
-      if (col < n) {
+  for (int c = 0; c < kStageChunks; ++c) {
+    // pieces past the wave's last slice (odd slice count) are not read
+    const bool ok = c < nch && 64 * c + pc * 8 < nsl * 32;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float* q = part + ((lane >> 4) * 4 + j) * s.ldl + col;
-          *q = acc[nb][j] + *q;
+    for (int i = 0; i < kLd; ++i)
+      buf[c][i] = ok ? ld_off<u32x4>(i < kLdB ? cent : u, go[i] + (uint32_t)c * 128u)
+                     : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kStageChunks; ++c) {
+    if (c < nch) {
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) *reinterpret_cast<u32x4*>(reg + wo[i]) = buf[c][i];
+      // the wave reads what its other lanes wrote
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        if (2 * c + uu < nsl) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(reg + stage_slot((uint32_t)(uu * 64 + lane)) * 16);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(
+                reg + 2048 + stage_slot((uint32_t)((nb * 2 + uu) * 64 + lane)) * 16);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
+          }
         }
       }
+      // reads done before the next chunk overwrites the region
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
-  __syncthreads();
-  for (int p = tid; p < kRouteTok * n; p += kThreads) {
-    const int tl = p / n, e = p - tl * n;
-    const int o = tl * s.ldl + e;
-    s.lg[o] = ((s.part[o] + s.part[stride + o]) + s.part[2 * stride + o]) + s.part[3 * stride + o];
-  }
+  reduce_partials<NB>(acc, n, s);
 }
 
 __device__ void logits_f32(const float* __restrict__ u, const float* __restrict__ cent,
@@ -316,7 +423,7 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
   block_hist_rank(s, n, k, blk, T, blk_cnt, lrank);
 }
 
-template <int NB>
+template <int NB, bool STAGED>
 __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ u, const uint16_t* __restrict__ cent, int64_t T, int d, int n,
     int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
@@ -324,7 +431,10 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const RouteSmem s = carve(smem, n, k);
   const int64_t blk = blockIdx.x;
-  logits_bf16<NB>(u, cent, T, d, n, blk, s);
+  if constexpr (STAGED)
+    logits_bf16_staged<NB>(u, cent, T, d, n, blk, s, smem + route_smem_bytes_aligned(n, k));
+  else
+    logits_bf16<NB>(u, cent, T, d, n, blk, s);
   __syncthreads();
   route_tail<NB>(T, n, k, blk, s, topk_idx, topk_gate, blk_cnt, blk_P, lrank);
 }
@@ -757,23 +867,34 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
 #undef MOE_ROUTE_F32
     return hipGetLastError();
   }
-#define MOE_ROUTE_CASE(NBV)                                                                    \
+#define MOE_ROUTE_CASE(NBV, STG)                                                               \
   {                                                                                            \
-    if (sm > kDefaultLds) {                                                                    \
-      const hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel<NBV>,            \
+    const size_t smv = STG ? route_smem_bytes_aligned(n, k) + (size_t)kWaves * (2 + 2 * NBV) * 1024 \
+                           : sm;                                                               \
+    if (smv > kDefaultLds) {                                                                   \
+      const hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel<NBV, STG>,       \
                                                hipFuncAttributeMaxDynamicSharedMemorySize,     \
-                                               (int)sm);                                       \
+                                               (int)smv);                                      \
       if (e != hipSuccess) return e;                                                           \
     }                                                                                          \
-    hipLaunchKernelGGL(route_bf16_kernel<NBV>, dim3(B), dim3(kThreads), sm, s,                 \
+    hipLaunchKernelGGL((route_bf16_kernel<NBV, STG>), dim3(B), dim3(kThreads), smv, s,         \
                        (const uint16_t*)u, (const uint16_t*)cent, T, d, n, k, topk_idx,        \
                        topk_gate, blk_cnt, blk_P, lrank);                                      \
   }
-  if (nb <= 1) MOE_ROUTE_CASE(1)
-  else if (nb <= 2) MOE_ROUTE_CASE(2)
-  else if (nb <= 4) MOE_ROUTE_CASE(4)
-  else if (nb <= 8) MOE_ROUTE_CASE(8)
-  else MOE_ROUTE_CASE(16)
+  // Staged loads while a wave's hidden range fits one round (d <= 2048) and
+  // the operand regions fit LDS (n <= 64).
+  const bool staged = d <= 2048 && nb <= 4;
+  if (nb <= 1) {
+    if (staged) MOE_ROUTE_CASE(1, true) else MOE_ROUTE_CASE(1, false)
+  } else if (nb <= 2) {
+    if (staged) MOE_ROUTE_CASE(2, true) else MOE_ROUTE_CASE(2, false)
+  } else if (nb <= 4) {
+    if (staged) MOE_ROUTE_CASE(4, true) else MOE_ROUTE_CASE(4, false)
+  } else if (nb <= 8) {
+    MOE_ROUTE_CASE(8, false)
+  } else {
+    MOE_ROUTE_CASE(16, false)
+  }
 #undef MOE_ROUTE_CASE
   return hipGetLastError();
 }
