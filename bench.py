@@ -153,8 +153,9 @@ class Layer:
         self.moe, self.torch, self.cfg = moe, torch, cfg
         dev = "cuda"
         self.p = moe.problem(cfg.T, cfg.d, cfg.N, cfg.m, cfg.K, cfg.K_s, cfg.d_ff, cfg.dtype)
-        self.u = to_device(inp["u"], dev)
-        self.c = to_device(inp["centroids"], dev)
+        self.u = inp["u"] if isinstance(inp["u"], torch.Tensor) else to_device(inp["u"], dev)
+        self.c = (inp["centroids"] if isinstance(inp["centroids"], torch.Tensor)
+                  else to_device(inp["centroids"], dev))
         self.weights = weight_sets
         self.h = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
         self.idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
@@ -215,6 +216,72 @@ def time_layer(layer: Layer, hip: Hip, steps: int, warmup: int) -> dict:
                 marked_ms_per_step=marked_total, kernels=names)
 
 
+def gpu_shape_inputs(cfg, seed, torch, moe, copies):
+    """Inputs of a workload drawn on the GPU (seeded torch normals) with the
+    workload's distributions: u ~ N(0,1); centroids ~ N(0, cent_std) (1/sqrt(d)
+    by default) with Zipf-scaled rows where the workload says so; weights
+    ~ N(0, w_std); bf16, weights packed.  For timing only: unlike the parity
+    inputs, the top-k margins are not certified."""
+    import math
+
+    import moe_synth
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    T, d, n, f, ks = cfg.T, cfg.d, cfg.n, cfg.d_ff, cfg.K_s
+    bf = torch.bfloat16
+    u = torch.randn((T, d), generator=g, device="cuda").to(bf)
+    cstd = cfg.cent_std if cfg.cent_std is not None else 1.0 / math.sqrt(d)
+    c = torch.randn((n, d), generator=g, device="cuda") * cstd
+    if cfg.zipf_s:
+        z = torch.from_numpy(moe_synth.zipf_row_scale(n, cfg.zipf_s)).to(device="cuda",
+                                                                           dtype=torch.float32)
+        c = c * z[:, None]
+    c = c.to(bf)
+    p = moe.problem(T, d, cfg.N, cfg.m, cfg.K, ks, f, cfg.dtype)
+    shapes = [("w1", (n, f, d)), ("w3", (n, f, d)), ("w2", (n, d, f))]
+    if ks:
+        shapes += [("ws1", (ks * f, d)), ("ws3", (ks * f, d)), ("ws2", (d, ks * f))]
+    sets = []
+    for _ in range(copies):
+        st = {"ws1": None, "ws3": None, "ws2": None}
+        for name, shape in shapes:
+            src = (torch.randn(shape, generator=g, device="cuda") * cfg.w_std).to(bf)
+            dst = torch.empty_like(src)
+            moe.moe_pack_weights(p, src.numel() // shape[-1], shape[-1], src, dst)
+            del src
+            st[name] = dst
+        sets.append(st)
+    torch.cuda.synchronize()
+    return {"u": u, "centroids": c}, sets
+
+
+def other_shape(name, cfg, torch, moe, hip, steps, warmup) -> dict:
+    """Layer tokens/s and grouped-GEMM MFMA fraction of one more model shape."""
+    inp, sets = gpu_shape_inputs(cfg, 0, torch, moe, copies=1 if cfg.n * cfg.d_ff * cfg.d > 5e8 else 2)
+    layer = Layer(cfg, inp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
+    res = time_layer(layer, hip, steps, warmup)
+    counts = layer.counts.cpu().numpy()
+    work = kernel_work(cfg, int((counts > 0).sum()))
+    gemm_flop = work["up_swiglu"]["flop"] + work["down"]["flop"]
+    gemm_s = (res["kernel_ms"]["up_swiglu"] + res["kernel_ms"]["down"]) * 1e-3
+    ms = res["ms_per_step"]
+    out = {
+        "workload": f"{name}: T={cfg.T}, d={cfg.d}, {cfg.n} routed (top-{cfg.k}) + {cfg.K_s} shared,"
+                    f" SwiGLU d_ff={cfg.d_ff}, bf16" + (f", Zipf({cfg.zipf_s}) router skew"
+                                                          if cfg.zipf_s else ""),
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4),
+        "grouped_gemm_tflops": round(gemm_flop / gemm_s / 1e12, 1),
+        "grouped_gemm_mfma_frac": round(gemm_flop / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "max_expert_rows": int(counts.max()),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in res["kernel_ms"].items()},
+        "inputs": "drawn on the GPU (seeded normals of the workload's distributions)",
+    }
+    del layer, sets, inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, inp, seconds: float) -> dict:
     """The oracle on the first T_s tokens of the workload as their own batch
     (the whole batch when it fits the time budget).  The probe is large
@@ -248,6 +315,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other-shapes", action="store_true",
+                    help="skip the 2B- and 145B-shaped layers")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -363,6 +432,12 @@ def main():
             "kernel_us": {k: round(v * 1e3, 2) for k, v in dres["kernel_ms"].items()},
         }
         del dl
+    if not args.no_other_shapes:
+        out["other_shapes"] = {}
+        for name in ("2b", "145b"):
+            log(f"timing the {name}-shaped layer")
+            out["other_shapes"][name] = other_shape(name, moe_synth.CONFIGS[name], torch, moe, hip,
+                                                    max(10, args.steps // 3), 3)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

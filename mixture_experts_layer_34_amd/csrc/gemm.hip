@@ -589,15 +589,19 @@ static hipError_t launch_bf16_t(const FfnArgs* segs, int nseg, hipStream_t s) {
 }
 
 // Packed weights: the up projection takes the 128 x 256 tile (d_ff = 1408
-// is 11 of its column tiles, and two workgroups share a CU), the down
-// projection the 128 x 512 tile.  Row-major weights: 128 x 512 for both.
+// is 11 of its column tiles, and two workgroups share a CU); the down
+// projection the 128 x 512 tile when d is a multiple of 512, else the
+// 128 x 256 one (d = 1280 is 5 of those, 2.5 of the wide ones).  Row-major
+// weights: 128 x 512 for both.
 template <bool UP>
 static hipError_t launch_bf16(const FfnArgs* segs, int nseg, bool packed, hipStream_t s) {
   if (!packed) return launch_bf16_t<UP, false, 4>(segs, nseg, s);
-  if constexpr (UP)
+  if constexpr (UP) {
     return launch_bf16_t<true, true, 2>(segs, nseg, s);
-  else
-    return launch_bf16_t<false, true, 4>(segs, nseg, s);
+  } else {
+    if (segs[0].d % Tile<4>::BN == 0) return launch_bf16_t<false, true, 4>(segs, nseg, s);
+    return launch_bf16_t<false, true, 2>(segs, nseg, s);
+  }
 }
 
 static hipError_t launch_f32(const FfnArgs& a, bool up, hipStream_t s) {
