@@ -61,6 +61,15 @@ SMALL = {
     # the layer takes the separate scan and scatter kernels.
     "wide_bf16": moe_synth.MoEConfig("wide_bf16", T=2064, d=64, N=64, m=4, K=2, K_s=1,
                                      d_ff=32, dtype="bf16"),
+    # Degenerate routings: one kept expert per token; every expert kept
+    # (k = n, the order of the slots is the only choice left); and the
+    # largest top-k the library takes (k = 64 of n = 128).
+    "topk1_bf16": moe_synth.MoEConfig("topk1_bf16", T=130, d=96, N=16, m=1, K=2, K_s=1,
+                                      d_ff=64, dtype="bf16"),
+    "all_experts_bf16": moe_synth.MoEConfig("all_experts_bf16", T=100, d=96, N=8, m=1, K=8,
+                                            K_s=0, d_ff=64, dtype="bf16"),
+    "topk64_bf16": moe_synth.MoEConfig("topk64_bf16", T=48, d=64, N=128, m=1, K=64, K_s=0,
+                                       d_ff=32, dtype="bf16"),
     # Skewed popularity, no shared experts: some expert gets more than 32
     # rows, so its weights are streamed once per 32 rows.
     "decode_skew_bf16": moe_synth.MoEConfig("decode_skew_bf16", T=64, d=128, N=8, m=1, K=2,
