@@ -10,9 +10,10 @@
 // d_ff columns; down: two consecutive bands of W2, or one where the
 // reduction is long, so that every item streams about the same bytes) and
 // the group's rows in passes of 32 (one pass unless a group holds more than
-// 32 rows).  The MFMA 32x32x16 takes a weight band as its first operand and
-// 32 activation rows as its second; kSkDepth 16-wide k blocks are kept in
-// flight in a register ring.  SwiGLU is applied in registers (gate and up
+// 32 rows; a lone dense group, the shared experts, gives each pass an item
+// of its own so its waves end with the others).  The MFMA 32x32x16 takes a
+// weight band as its first operand and 32 activation rows as its second;
+// kSkDepth 16-wide k blocks are kept in flight in a register ring.  SwiGLU is applied in registers (gate and up
 // values of one (row, column) sit in the same lane and register).
 #include "common.h"
 #include "kernels.h"
@@ -40,6 +41,8 @@ struct SkSeg {
   int n_groups;
   int64_t rows;
   int bands;               // down: W2 bands per item (1 or 2); up: 1 column band
+  int nbands;              // band items per group
+  int passes;              // single group: 32-row passes split over items (else 1)
   int nblk;                // items per group
 };
 
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs args) {
   const int si = L < G0 ? 0 : 1;
   if (si) L -= G0;
   const SkSeg& g = args.seg[si];
-  const int e = L / g.nblk, blk = L - e * g.nblk;
+  const int e = L / g.nblk;
+  int blk = L - e * g.nblk;
   int64_t r0 = 0, nrows = g.rows;
   if (g.offsets) {  // caller data: clamped into [0, rows]
     int64_t a = g.offsets[e], b = g.offsets[e + 1];
@@ -147,6 +151,15 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs args) {
     b = b < a ? a : (b > g.rows ? g.rows : b);
     r0 = a;
     nrows = b - a;
+  } else if (g.passes > 1) {
+    // Runs of 8 * passes items: 8 bands x passes row passes, the passes of
+    // one band 8 items apart so they are dispatched to the same XCD and
+    // share its L2 for the band's weights.
+    const int run = 8 * g.passes, q = blk % run, pass = q / 8;
+    blk = (blk / run) * 8 + (q & 7);
+    if (blk >= g.nbands) return;
+    r0 = (int64_t)pass * 32;
+    nrows = g.rows - r0 < 32 ? g.rows - r0 : 32;
   }
   if (nrows <= 0) return;  // an expert nobody chose: its weights are not read
 
@@ -202,6 +215,14 @@ SkSeg sk_seg(const FfnArgs& a, bool up, int bands) {
   s.offsets = a.tiles ? a.offsets : nullptr;
   s.n_groups = a.tiles ? a.n_groups : 1;
   s.rows = a.rows;
+  // A single group's 32-row passes go to separate items, so its waves take
+  // as long as the others' instead of a multiple.
+  s.nbands = s.nblk;
+  s.passes = 1;
+  if (!s.offsets && s.rows > 32) {
+    s.passes = (int)((s.rows + 31) / 32);
+    s.nblk = (s.nbands + 7) / 8 * 8 * s.passes;
+  }
   return s;
 }
 
