@@ -13,8 +13,9 @@
 // 32 rows; a lone dense group, the shared experts, gives each pass an item
 // of its own so its waves end with the others).  The MFMA 32x32x16 takes a
 // weight band as its first operand and 32 activation rows as its second;
-// kSkDepth 16-wide k blocks are kept in flight in a register ring.  SwiGLU is applied in registers (gate and up
-// values of one (row, column) sit in the same lane and register).
+// kSkDepth 16-wide k blocks are kept in flight in a register ring.  SwiGLU
+// is applied in registers (gate and up values of one (row, column) sit in
+// the same lane and register).
 #include "common.h"
 #include "kernels.h"
 
@@ -22,7 +23,11 @@ namespace moe {
 namespace {
 
 constexpr int kSkThreads = 64;  // one wave
-constexpr int kSkDepth = 8;     // 16-wide k blocks in flight
+// 16-wide k blocks in flight per wave.  Six keep a wave within 168
+// registers, so three waves share a SIMD and a 64-token layer's items all
+// run in one round (eight would leave a second round of a few waves).
+constexpr int kSkDepth = 6;
+constexpr int kSkWavesPerSimd = 3;
 
 typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
 
@@ -136,7 +141,7 @@ __device__ __forceinline__ void skinny_item(const SkSeg& g, int64_t r0, int64_t 
 }
 
 template <bool UP>
-__global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs args) {
+__global__ __launch_bounds__(kSkThreads, kSkWavesPerSimd) void skinny_kernel(SkArgs args) {
   int L = blockIdx.x;
   const int G0 = args.seg[0].n_groups * args.seg[0].nblk;
   const int si = L < G0 ? 0 : 1;
