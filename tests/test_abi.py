@@ -226,3 +226,12 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout
     assert out.count("libamdhip64") == 1, out
+
+
+def test_layer_kernel_sequence():
+    # Histogram tables of up to 32768 entries take the one-pass grouping
+    # kernel, larger ones the separate scan and scatter.
+    assert moe.moe_layer_kernels(p16(T=64)) == ["route", "group", "up_swiglu", "down", "combine"]
+    assert moe.moe_layer_kernels(p16(T=8192))[:2] == ["route", "group"]
+    assert moe.moe_layer_kernels(p16(T=8208))[:3] == ["route", "scan", "scatter"]
+    assert moe.moe_layer_kernels(p16(dtype="f32"))[2:4] == ["up_swiglu_f32", "down_f32"]

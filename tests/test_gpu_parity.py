@@ -285,3 +285,39 @@ def test_layer_bitwise_deterministic(case):
     b = run_layer(case, fl, ws=ws)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_layer_graph_replays(case):
+    """The layer captured as a HIP graph reproduces the eager bits on every
+    replay, back to back and after an eager call on the same workspace, with
+    junk written to the outputs before each replay."""
+    cfg = case.cfg
+    if case.name in FULL and case.name != "16b_decode":
+        pytest.skip("graph replay is checked on the small and the decode workloads")
+    fl = moe.MOE_PACKED_WEIGHTS if cfg.dtype == "bf16" else 0
+    want = run_layer(case, fl)
+    p, d = prob(cfg), "cuda"
+    t = case.weights(bool(fl & moe.MOE_PACKED_WEIGHTS))
+    out = {k: torch.empty_like(v) for k, v in want.items()}
+    ws = workspace(p, d)
+    args = lambda: (p, t["u"], t["centroids"], t["w1"], t["w3"], t["w2"], t["ws1"], t["ws3"],
+                    t["ws2"], out["h"], out["topk_idx"], out["topk_gate"], out["counts"],
+                    out["f"], out["P"], fl, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_layer_fwd(*args())  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_layer_fwd(*args())
+    for i, eager_between in enumerate((False, True, False)):
+        for v in out.values():
+            v.fill_(-3)
+        if eager_between:
+            run_layer(case, fl, ws=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in want:
+            assert torch.equal(out[k], want[k]), (i, k)
