@@ -207,11 +207,13 @@ struct PipeLds {
 // weight fragments straight into registers with coalesced 1 KB loads, two
 // slices ahead; only the activations (shared by the 4 waves) go through LDS.
 // Every slice is 8*NBW steps, one MFMA each, fenced so the compiler keeps
-// this order: MFMA i covers weight band nb = i/8, k half kk = (i/4)%2, row
-// block mi = i%4 (an accumulator is reused 4 MFMAs later, never back to
-// back).
-//   steps 0-7    read the next slice's activation fragments from LDS
-//   step 8nb+7   reload the two weight fragments of band nb (slice s+2)
+// this order: MFMA i covers weight band nb = i%NBW, then row block
+// mi = (i/NBW)%4, then k half kk = i/(4*NBW) (an accumulator is reused
+// 4*NBW MFMAs later; consecutive MFMAs share the activation fragment).
+//   after the last MFMA of an activation fragment: read the next slice's
+//                fragment into the same registers (one fragment set)
+//   after the last MFMA of a weight fragment (row block 3): reload it with
+//                slice s+2's
 //   step kAst    store the staged activations of slice s+2 into LDS
 //   step kAst+2  load the activations of slice s+4 into that staging set
 template <bool UP, int NBW>
@@ -231,10 +233,9 @@ struct PipePacked {
 #pragma unroll
     for (int i = 0; i < 2; ++i) r[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
   }
-  __device__ __forceinline__ void bload(bf16x8 (&b)[2][NBW], int nb, int s) const {
-    const uint32_t kb = (uint32_t)clampk(s) * 2;  // 16-wide k blocks
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + (kb + kk) * 1024u);
+  __device__ __forceinline__ void bload(bf16x8 (&b)[2][NBW], int kk, int nb, int s) const {
+    const uint32_t kb = (uint32_t)clampk(s) * 2 + kk;  // 16-wide k block
+    b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + kb * 1024u);
   }
   __device__ __forceinline__ void astore(const u32x4 (&r)[2], int buf) const {
 #pragma unroll
@@ -245,21 +246,21 @@ struct PipePacked {
     const int ko = kk * 16 + (lane >> 5) * 8;
     a[kk][mi] = *reinterpret_cast<const bf16x8*>(&sA[buf][(mi * 32 + (lane & 31)) * LDK + ko]);
   }
-  // One slice: MFMAs on (ac, bc); next slice's fragments into an; weights
-  // of slice s+2 into bc; staged activations rs (slice s+2) into LDS buffer
-  // `buf`, then slice s+4 into rs.
-  __device__ __forceinline__ void slice(int s, int buf, const bf16x8 (&ac)[2][4],
-                                        bf16x8 (&an)[2][4], bf16x8 (&bc)[2][NBW], u32x4 (&rs)[2],
-                                        f32x16 (&acc)[4][NBW]) const {
+  // One slice: MFMAs on (a, bc).  Right after its last MFMA an activation
+  // fragment is replaced by the next slice's (one fragment set), and a
+  // weight fragment by slice s+2's; the staged activations rs (slice s+2)
+  // go into LDS buffer `buf` at step kAst, then slice s+4 into rs.
+  __device__ __forceinline__ void slice(int s, int buf, bf16x8 (&a)[2][4], bf16x8 (&bc)[2][NBW],
+                                        u32x4 (&rs)[2], f32x16 (&acc)[4][NBW]) const {
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
-      const int nb = i >> 3, kk = (i >> 2) & 1, mi = i & 3;
-      acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[kk][nb], ac[kk][mi], acc[mi][nb],
+      const int q = i / NBW, nb = i % NBW, kk = q >> 2, mi = q & 3;
+      acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[kk][nb], a[kk][mi], acc[mi][nb],
                                                             0, 0, 0);
-      if (i < 8) rfrag(an, i >> 2, i & 3, buf ^ 1);
+      if (nb == NBW - 1) rfrag(a, kk, mi, buf ^ 1);
+      if (mi == 3) bload(bc, kk, nb, s + 2);
       if (i == kAst) astore(rs, buf);
       if (i == kAst + 2) aload(rs, s + 4);
-      if ((i & 7) == 7) bload(bc, nb, s + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -268,14 +269,15 @@ struct PipePacked {
   __device__ __forceinline__ void preload(bf16x8 (&b)[2][NBW], int sb, u32x4 (&r)[2],
                                           int sa) const {
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      bload(b, nb, sb);
-      if (8 * nb + 7 < kAst + 2 && kAst + 2 < 8 * nb + 15) aload(r, sa);
+    for (int i = 0; i < kSteps; ++i) {
+      const int q = i / NBW, nb = i % NBW, kk = q >> 2, mi = q & 3;
+      if (mi == 3) bload(b, kk, nb, sb);
+      if (i == kAst + 2) aload(r, sa);
     }
   }
   __device__ __forceinline__ void run(f32x16 (&acc)[4][NBW]) const {
     u32x4 R0[2], R1[2];
-    bf16x8 A0[2][4], A1[2][4], B0[2][NBW], B1[2][NBW];
+    bf16x8 A[2][4], B0[2][NBW], B1[2][NBW];
     // Issue order mirrors two steady-state slices so the wait counts the
     // compiler derives at the loop head are the steady-state ones.
     aload(R0, 0);
@@ -290,19 +292,19 @@ struct PipePacked {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) rfrag(A0, kk, mi, 0);
+      for (int mi = 0; mi < 4; ++mi) rfrag(A, kk, mi, 0);
     int s = 0;
     for (; s + 2 <= ns; s += 2) {
-      slice(s, 0, A0, A1, B0, R0, acc);
+      slice(s, 0, A, B0, R0, acc);
       __syncthreads();
-      slice(s + 1, 1, A1, A0, B1, R1, acc);
+      slice(s + 1, 1, A, B1, R1, acc);
       __syncthreads();
     }
     if (s < ns) {  // odd slice count: MFMAs only
 #pragma unroll
       for (int i = 0; i < kSteps; ++i) {
-        const int nb = i >> 3, kk = (i >> 2) & 1, mi = i & 3;
-        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B0[kk][nb], A0[kk][mi],
+        const int q = i / NBW, nb = i % NBW, kk = q >> 2, mi = q & 3;
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B0[kk][nb], A[kk][mi],
                                                               acc[mi][nb], 0, 0, 0);
       }
     }
