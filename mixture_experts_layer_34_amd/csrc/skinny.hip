@@ -23,11 +23,17 @@ namespace moe {
 namespace {
 
 constexpr int kSkThreads = 64;  // one wave
-// 16-wide k blocks in flight per wave.  Six keep a wave within 168
-// registers, so three waves share a SIMD and a 64-token layer's items all
-// run in one round (eight would leave a second round of a few waves).
+// 16-wide k blocks in flight per wave.  Six keep a two-band wave within
+// 168 registers, so three waves share a SIMD and a 64-token layer's items
+// all run in one round (eight would leave a second round of a few waves).
+// A one-band wave keeps twice as many blocks in flight in the same
+// registers, so it streams its band as fast as a two-band wave streams two.
 constexpr int kSkDepth = 6;
 constexpr int kSkWavesPerSimd = 3;
+template <bool TWO>
+constexpr int sk_depth() {
+  return TWO ? kSkDepth : 2 * kSkDepth;
+}
 
 typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
 
@@ -82,30 +88,31 @@ __device__ __forceinline__ void skinny_item(const SkSeg& g, int64_t r0, int64_t 
       acc_a[j] = 0.f;
       acc_b[j] = 0.f;
     }
-    bf16x8 fa[kSkDepth], fb[kSkDepth], fx[kSkDepth];
+    constexpr int kDepth = sk_depth<TWO>();
+    bf16x8 fa[kDepth], fb[TWO ? kDepth : 1], fx[kDepth];
     auto load = [&](int slot, int kb) {
       kb = kb < KB ? kb : KB - 1;  // past the end: a block nobody reads
       fa[slot] = ld_off<bf16x8>(wa, wl + (uint32_t)kb * 1024u);
-      if (TWO) fb[slot] = ld_off<bf16x8>(wb, wl + (uint32_t)kb * 1024u);
+      if constexpr (TWO) fb[slot] = ld_off<bf16x8>(wb, wl + (uint32_t)kb * 1024u);
       fx[slot] = ld_off<bf16x8>(g.X, xo + (uint32_t)kb * 32u);
     };
     auto mma = [&](int slot) {
       acc_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot], fx[slot], acc_a, 0, 0, 0);
-      if (TWO)
+      if constexpr (TWO)
         acc_b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot], fx[slot], acc_b, 0, 0, 0);
     };
 #pragma unroll
-    for (int j = 0; j < kSkDepth; ++j) load(j, j);
+    for (int j = 0; j < kDepth; ++j) load(j, j);
     int kb0 = 0;
-    for (; kb0 + kSkDepth <= KB; kb0 += kSkDepth) {
+    for (; kb0 + kDepth <= KB; kb0 += kDepth) {
 #pragma unroll
-      for (int j = 0; j < kSkDepth; ++j) {
+      for (int j = 0; j < kDepth; ++j) {
         mma(j);
-        load(j, kb0 + j + kSkDepth);
+        load(j, kb0 + j + kDepth);
       }
     }
 #pragma unroll
-    for (int j = 0; j < kSkDepth; ++j)
+    for (int j = 0; j < kDepth; ++j)
       if (kb0 + j < KB) mma(j);
 
     // Lane: activation row tok of this pass; register r: band row
