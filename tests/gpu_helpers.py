@@ -70,6 +70,10 @@ SMALL = {
                                             K_s=0, d_ff=64, dtype="bf16"),
     "topk64_bf16": moe_synth.MoEConfig("topk64_bf16", T=48, d=64, N=128, m=1, K=64, K_s=0,
                                        d_ff=32, dtype="bf16"),
+    # One token: a single, mostly empty route block; every group but k is
+    # empty and the shared experts see one row.
+    "one_token_bf16": moe_synth.MoEConfig("one_token_bf16", T=1, d=64, N=8, m=1, K=3, K_s=1,
+                                          d_ff=32, dtype="bf16"),
     # Skewed popularity, no shared experts: some expert gets more than 32
     # rows, so its weights are streamed once per 32 rows.
     "decode_skew_bf16": moe_synth.MoEConfig("decode_skew_bf16", T=64, d=128, N=8, m=1, K=2,
