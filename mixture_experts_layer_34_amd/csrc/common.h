@@ -10,8 +10,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte register payload
 
-constexpr int kWave = 64;
-
 // bf16 storage is handled as raw 16-bit patterns.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -24,10 +22,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
-
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Element type traits: storage type and its conversion to fp32.
@@ -35,7 +29,6 @@ template <int DT> struct Elem;
 template <> struct Elem<0> {  // fp32
   typedef float T;
   static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
-  static __device__ __forceinline__ float cvt(float x) { return x; }
   static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
 };
 template <> struct Elem<1> {  // bf16 bits
@@ -48,8 +41,6 @@ template <> struct Elem<1> {  // bf16 bits
   }
 };
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-
 // Load through a wave-uniform base and a 32-bit byte offset, which maps to
 // the global_load form with an SGPR base, a VGPR offset and an immediate.
 template <typename V>
@@ -57,17 +48,9 @@ __device__ __forceinline__ V ld_off(const void* __restrict__ base, uint32_t byte
   return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
 }
 
-// Map a linear workgroup id to a logical tile so that each XCD (workgroups
-// are dealt round-robin over the 8 XCDs) processes one contiguous range of
-// logical tiles: neighbouring tiles then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int w, int G) {
-  constexpr int kXcd = 8;
-  const int q = G / kXcd, r = G % kXcd;
-  const int x = w % kXcd, i = w / kXcd;
-  return x * q + (x < r ? x : r) + i;
-}
-
-// Two segments of tiles in one launch: each XCD first takes an even share of
+// Two segments of tiles in one launch, mapped so that each XCD (workgroups
+// are dealt round-robin over the 8 XCDs) works on contiguous logical tiles,
+// which then share that XCD's L2: each XCD first takes an even share of
 // segment 1's tiles (the longer ones, so they start early), then a
 // contiguous range of segment 0's tiles.  The shares add up to the number of
 // live workgroups (w < G0 + G1) the round-robin deal gives each XCD.

@@ -35,7 +35,7 @@ struct RouteSmem {
   int ldl;
 };
 
-__device__ __forceinline__ RouteSmem carve(char* smem, int n, int k) {
+__device__ __forceinline__ RouteSmem carve(char* smem, int n) {
   RouteSmem s;
   s.ldl = n + 1;
   s.part = reinterpret_cast<float*>(smem);
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
     int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     int32_t* __restrict__ blk_cnt, float* __restrict__ blk_P, int32_t* __restrict__ lrank) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const RouteSmem s = carve(smem, n, k);
+  const RouteSmem s = carve(smem, n);
   const int64_t blk = blockIdx.x;
   if constexpr (STAGED)
     logits_bf16_staged<NB>(u, cent, T, d, n, blk, s, smem + route_smem_bytes_aligned(n, k));
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     int32_t* __restrict__ blk_cnt, float* __restrict__ blk_P, int32_t* __restrict__ lrank) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const RouteSmem s = carve(smem, n, k);
+  const RouteSmem s = carve(smem, n);
   const int64_t blk = blockIdx.x;
   logits_f32(u, cent, T, d, n, blk, s);
   __syncthreads();
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ blk_cnt,
                                                         int32_t* __restrict__ lrank) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const RouteSmem s = carve(smem, n, k);
+  const RouteSmem s = carve(smem, n);
   const int64_t blk = blockIdx.x;
   for (int p = threadIdx.x; p < kRouteTok * k; p += kThreads) {
     const int tl = p / k, j = p - tl * k;
