@@ -129,6 +129,10 @@ def kernel_work(cfg, n_active: int, es: int = 2) -> dict:
                           routed_flop=routed_up["flop"])
     w["down"] = dict(flop=routed_dn["flop"] + sh_dn["flop"], bytes=routed_dn["bytes"] + sh_dn["bytes"],
                      routed_flop=routed_dn["flop"])
+    # small batches: logits over (token block x 16 experts) workgroups, then
+    # one workgroup routes and groups the batch
+    w["logits"] = dict(flop=2 * T * d * n, bytes=T * d * es + n * d * es + T * n * 4)
+    w["route_group"] = dict(flop=0, bytes=T * n * 4 + R * 20 + n * 12)
     w["combine"] = dict(flop=2 * R * d, bytes=3 * T * d * es + R * d * es + R * 8)
     return w
 

@@ -51,7 +51,7 @@ bool aligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) 
 // Workspace regions, each 256-byte aligned.
 struct Layout {
   size_t blk_cnt, blk_P, blk_base, lrank, offsets, perm_token, slot_of;
-  size_t t_row0, t_rows, t_off, t_count;
+  size_t t_row0, t_rows, t_off, t_count, lg;
   size_t hbuf, ybuf, hsbuf, sbuf;
   size_t total;
   int max_tiles;
@@ -83,6 +83,7 @@ Layout layout(const Dims& d) {
   L.t_rows = take((size_t)L.max_tiles * 4);
   L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
   L.t_count = take(4);
+  L.lg = take((size_t)(d.T < moe::kSmallBatch ? d.T : moe::kSmallBatch) * d.n * 4);
   const size_t hs_el = (size_t)d.T * d.K_s * d.d_ff;
   L.hcap = R * d.d_ff > hs_el ? R * d.d_ff : hs_el;
   L.hbuf = take(L.hcap * d.esize);
@@ -304,10 +305,14 @@ int moe_layer_kernels(const moe_problem* p, int flags, const char** names, int m
   const bool tiled = p->dtype == MOE_BF16;
   const char* seq[10];
   int c = 0;
-  seq[c++] = "route";
-  if (moe::group_in_one_pass(d.T, d.n)) {
+  if (moe::route_small(p->dtype, d.T)) {
+    seq[c++] = "logits";
+    seq[c++] = "route_group";
+  } else if (moe::group_in_one_pass(d.T, d.n)) {
+    seq[c++] = "route";
     seq[c++] = "group";
   } else {
+    seq[c++] = "route";
     seq[c++] = "scan";
     seq[c++] = "scatter";
   }
@@ -357,22 +362,34 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   };
   MOE_TRY(mark());
 
-  MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
-                            at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
-                            at<int32_t>(ws, L.lrank), s));
-  MOE_TRY(mark());
-  if (moe::group_in_one_pass(d.T, d.n)) {
-    MOE_TRY(moe::launch_group(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
-                              topk_idx, at<int32_t>(ws, L.lrank), counts, f, P, offsets,
-                              perm_token, slot_of, &tl, s));
+  if (moe::route_small(p->dtype, d.T)) {
+    // Small batch: logits spread over the GPU, then one workgroup routes and
+    // groups the whole batch.
+    float* lg = at<float>(ws, L.lg);
+    MOE_TRY(moe::launch_logits_small(u, centroids, d.T, d.d, d.n, lg, s));
+    MOE_TRY(mark());
+    MOE_TRY(moe::launch_route_small(lg, d.T, d.n, d.k, topk_idx, topk_gate, counts, f, P, offsets,
+                                    perm_token, slot_of, &tl, s));
     MOE_TRY(mark());
   } else {
-    MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n, d.k,
-                             counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+    MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
+                              at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
+                              at<int32_t>(ws, L.lrank), s));
     MOE_TRY(mark());
-    MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
-                                d.T, d.n, d.k, perm_token, slot_of, nullptr, nullptr, 0, s));
-    MOE_TRY(mark());
+    if (moe::group_in_one_pass(d.T, d.n)) {
+      MOE_TRY(moe::launch_group(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n,
+                                d.k, topk_idx, at<int32_t>(ws, L.lrank), counts, f, P, offsets,
+                                perm_token, slot_of, &tl, s));
+      MOE_TRY(mark());
+    } else {
+      MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n,
+                               d.k, counts, f, P, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+      MOE_TRY(mark());
+      MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank),
+                                  at<int32_t>(ws, L.blk_base), d.T, d.n, d.k, perm_token,
+                                  slot_of, nullptr, nullptr, 0, s));
+      MOE_TRY(mark());
+    }
   }
   // Routed experts (rows gathered from u through perm_token) and the shared
   // experts (one dense SwiGLU of width K_s*d_ff over all tokens) go through

@@ -29,6 +29,19 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
                         int k, int32_t* topk_idx, float* topk_gate, int32_t* blk_cnt,
                         float* blk_P, int32_t* lrank, hipStream_t s);
 
+// Routing and grouping of batches of at most 64 tokens (bf16) in two
+// launches: logits over (token block x 16 experts) workgroups into lg
+// [T][n] fp32, then one workgroup for softmax, top-k, counts, f, P, offsets,
+// perm_token, slot_of and the tile list (when tiles != nullptr).
+constexpr int kSmallBatch = 64;  // most tokens of the small-batch routing
+bool route_small(int dtype, int64_t T);
+hipError_t launch_logits_small(const void* u, const void* cent, int64_t T, int d, int n, float* lg,
+                               hipStream_t s);
+hipError_t launch_route_small(const float* lg, int64_t T, int n, int k, int32_t* topk_idx,
+                              float* topk_gate, int32_t* counts, float* f, float* P,
+                              int32_t* offsets, int32_t* perm_token, int32_t* slot_of,
+                              const TileList* tiles, hipStream_t s);
+
 // Histogram and ranks from a given topk_idx (standalone grouping).
 hipError_t launch_hist(const int32_t* topk_idx, int64_t T, int n, int k, int32_t* blk_cnt,
                        int32_t* lrank, hipStream_t s);

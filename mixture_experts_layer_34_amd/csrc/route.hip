@@ -342,9 +342,68 @@ __device__ void logits_f32(const float* __restrict__ u, const float* __restrict_
   }
 }
 
+// Softmax and top-k of one token on a 16-lane DPP row.  Lane q of the row
+// keeps the logits of experts q, q+16, ... (NB of them) in registers, so the
+// k selection rounds touch no memory.  Writes the softmax values to srow and
+// the kept experts to sidx (-1 when the token is past T) and, for a real
+// token t, its topk_idx / topk_gate row.
+template <int NB>
+__device__ __forceinline__ void token_topk(const float* row, float* srow, int* sidx, int q, int n,
+                                           int k, bool valid, int64_t t,
+                                           int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_gate) {
+  float v[NB];
+#pragma unroll
+  for (int r = 0; r < NB; ++r) {
+    const int i = q + 16 * r;
+    v[r] = i < n ? row[i] : -INFINITY;
+  }
+  float mx = v[0];
+#pragma unroll
+  for (int r = 1; r < NB; ++r) mx = fmaxf(mx, v[r]);
+  mx = row_max(mx);
+  float ev[NB];
+  float z = 0.f;
+#pragma unroll
+  for (int r = 0; r < NB; ++r) {
+    ev[r] = q + 16 * r < n ? expf(v[r] - mx) : 0.f;
+    z += ev[r];
+  }
+  z = row_sum(z);
+#pragma unroll
+  for (int r = 0; r < NB; ++r)
+    if (q + 16 * r < n) srow[q + 16 * r] = ev[r] / z;
+  // k rounds of a row arg-max; each lane scans its experts in ascending
+  // order, so a strict '>' keeps the lower index among equal logits, and a
+  // taken expert's logit becomes -inf.
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      if (v[r] > bv) {
+        bv = v[r];
+        bi = q + 16 * r;
+      }
+    }
+    row_argmax(bv, bi);
+    if ((bi & 15) == q) {
+      const int rr = bi >> 4;
+#pragma unroll
+      for (int r = 0; r < NB; ++r)
+        if (r == rr) v[r] = -INFINITY;
+    }
+    if (q == 0) {
+      sidx[j] = valid ? bi : -1;
+      if (valid) {
+        topk_idx[t * k + j] = bi;
+        topk_gate[t * k + j] = srow[bi];
+      }
+    }
+  }
+}
+
 // Softmax, top-k, P partials, histogram.  Logits are already in s.lg.
-// Lane q of a token's DPP row keeps the logits of experts q, q+16, ... (NB
-// of them) in registers, so the k selection rounds touch no memory.
 template <int NB>
 __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem& s,
                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
@@ -352,60 +411,10 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
                            int32_t* __restrict__ lrank) {
   const int tid = threadIdx.x;
   if (tid < kTailThreads) {  // whole waves
-    const int tl = tid >> 4, q = tid & 15;
+    const int tl = tid >> 4;
     const int64_t t = blk * kRouteTok + tl;
-    const bool valid = t < T;
-    const float* row = s.lg + tl * s.ldl;
-    float* srow = s.sv + tl * s.ldl;
-    float v[NB];
-#pragma unroll
-    for (int r = 0; r < NB; ++r) {
-      const int i = q + 16 * r;
-      v[r] = i < n ? row[i] : -INFINITY;
-    }
-    float mx = v[0];
-#pragma unroll
-    for (int r = 1; r < NB; ++r) mx = fmaxf(mx, v[r]);
-    mx = row_max(mx);
-    float ev[NB];
-    float z = 0.f;
-#pragma unroll
-    for (int r = 0; r < NB; ++r) {
-      ev[r] = q + 16 * r < n ? expf(v[r] - mx) : 0.f;
-      z += ev[r];
-    }
-    z = row_sum(z);
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-      if (q + 16 * r < n) srow[q + 16 * r] = ev[r] / z;
-    // k rounds of a row arg-max; each lane scans its experts in ascending
-    // order, so a strict '>' keeps the lower index among equal logits, and a
-    // taken expert's logit becomes -inf.
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int r = 0; r < NB; ++r) {
-        if (v[r] > bv) {
-          bv = v[r];
-          bi = q + 16 * r;
-        }
-      }
-      row_argmax(bv, bi);
-      if ((bi & 15) == q) {
-        const int rr = bi >> 4;
-#pragma unroll
-        for (int r = 0; r < NB; ++r)
-          if (r == rr) v[r] = -INFINITY;
-      }
-      if (q == 0) {
-        s.sidx[tl * k + j] = valid ? bi : -1;
-        if (valid) {
-          topk_idx[t * k + j] = bi;
-          topk_gate[t * k + j] = srow[bi];
-        }
-      }
-    }
+    token_topk<NB>(s.lg + tl * s.ldl, s.sv + tl * s.ldl, s.sidx + tl * k, tid & 15, n, k, t < T,
+                   t, topk_idx, topk_gate);
   }
   __syncthreads();
   // P partial of this block, tokens ascending.
@@ -491,6 +500,41 @@ __device__ int scan256(int v, int* wsum, int* total) {
   if (tid == 255) *total = pre + incl;
   __syncthreads();
   return pre + incl - v;
+}
+
+// M-tile list from expert totals (s_cnt) and offsets (s_off, n + 1 entries)
+// held in LDS; s_toff is n + 1 ints of LDS scratch.  Every thread of the
+// block must call it.
+__device__ void emit_tile_list(const TileList& tl, int n, const int* s_cnt, const int* s_off,
+                               int* s_toff, int* wsum, int* s_total, int nthreads) {
+  const int tid = threadIdx.x;
+  const int cnt_e = tid < n ? s_cnt[tid] : 0;
+  const int toff = scan256((cnt_e + kTileM - 1) / kTileM, wsum, s_total);
+  if (tid < n) {
+    s_toff[tid] = toff;
+    tl.off[tid] = toff;
+  }
+  if (tid == 0) {
+    s_toff[n] = *s_total;
+    tl.off[n] = *s_total;
+    *tl.count = *s_total;
+  }
+  __syncthreads();
+  // Tile t belongs to the last expert whose first tile is <= t.
+  const int total = s_toff[n];
+  for (int t = tid; t < total && t < tl.max_tiles; t += nthreads) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= t)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int r = (t - s_toff[lo]) * kTileM;
+    tl.row0[t] = s_off[lo] + r;
+    tl.rows[t] = s_cnt[lo] - r < kTileM ? s_cnt[lo] - r : kTileM;
+  }
 }
 
 // Writes the M-tiles of one group (rows cnt starting at grouped row first).
@@ -778,33 +822,138 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
     if (pos >= 0) perm_token[pos] = (int32_t)t;
   }
   if (blk != 0 || !tl.off) return;
-  // M-tile list (workgroup 0).
-  const int nt_e = tid < n ? (cnt_e + kTileM - 1) / kTileM : 0;
-  const int toff = scan256(nt_e, wsum, &s_total);
-  if (tid < n) {
-    s_toff[tid] = toff;
-    tl.off[tid] = toff;
+  emit_tile_list(tl, n, s_tot, s_off, s_toff, wsum, &s_total, kGroupThreads);  // workgroup 0
+}
+
+// ------------------------------------------------ routing of small batches
+
+// Batches of at most 64 tokens (bf16).  The per-block router above puts the
+// whole centroid matrix through each of a few CUs and leaves the rest idle;
+// here the logits are spread over (token block x 16 experts) workgroups, and
+// one workgroup then routes and groups the whole batch, so no per-block
+// histograms or bases are needed.
+
+// Logits of 16 tokens x 16 experts (expert group blockIdx.y) into lg[T][n]:
+// the same MFMA sequence and reduction as the per-block router, so the
+// values are the same bits.
+template <bool STAGED>
+__global__ __launch_bounds__(kThreads) void logits_small_kernel(
+    const uint16_t* __restrict__ u, const uint16_t* __restrict__ cent, int64_t T, int d, int n,
+    float* __restrict__ lg) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const RouteSmem s = carve(smem, 16);
+  const int64_t blk = blockIdx.x;
+  const int e0 = blockIdx.y * 16;
+  const int ng = n - e0 < 16 ? n - e0 : 16;
+  const uint16_t* cg = cent + (int64_t)e0 * d;
+  if constexpr (STAGED)
+    logits_bf16_staged<1>(u, cg, T, d, ng, blk, s, smem + route_smem_bytes_aligned(16, 0));
+  else
+    logits_bf16<1>(u, cg, T, d, ng, blk, s);
+  __syncthreads();
+  for (int p = threadIdx.x; p < kRouteTok * 16; p += kThreads) {
+    const int tl = p >> 4, e = p & 15;
+    const int64_t t = blk * kRouteTok + tl;
+    if (t < T && e < ng) lg[t * n + e0 + e] = s.lg[tl * s.ldl + e];
   }
-  if (tid == 0) {
-    s_toff[n] = s_total;
-    tl.off[n] = s_total;
-    *tl.count = s_total;
+}
+
+constexpr int kSmallTok = kSmallBatch;         // tokens one routing workgroup takes
+constexpr int kSmallThreads = 16 * kSmallTok;  // a 16-lane DPP row per token
+
+__host__ __device__ inline size_t route_small_smem_bytes(int n, int k) {
+  const size_t ldl = (size_t)n + 1;
+  return sizeof(float) * 2 * kSmallTok * ldl                          // logits, softmax
+         + sizeof(int) * ((size_t)kSmallTok * k + 3 * (kMaxExperts + 1) + 8);
+}
+
+// Softmax, top-k, P, counts / f, ranks, offsets, the stable scatter and the
+// M-tile list of a batch of T <= 64 tokens, one workgroup: token t is lane
+// t of every wave, so one ballot per expert gives its count and the rank of
+// each of its tokens.
+template <int NB>
+__global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
+    const float* __restrict__ lg, int64_t T, int n, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, int32_t* __restrict__ counts, float* __restrict__ f,
+    float* __restrict__ P, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ slot_of, TileList tl) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int ldl = n + 1;
+  float* s_lg = reinterpret_cast<float*>(smem);  // [64][ldl] logits, then ranks
+  float* s_sv = s_lg + kSmallTok * ldl;          // [64][ldl] softmax values
+  int* s_idx = reinterpret_cast<int*>(s_sv + kSmallTok * ldl);  // [64][k]
+  int* s_cnt = s_idx + kSmallTok * k;
+  int* s_off = s_cnt + (kMaxExperts + 1);
+  int* s_toff = s_off + (kMaxExperts + 1);
+  int* wsum = s_toff + (kMaxExperts + 1);
+  int* s_total = wsum + 4;
+  int* s_rk = reinterpret_cast<int*>(s_lg);
+  const int tid = threadIdx.x;
+  for (int p = tid; p < T * n; p += kSmallThreads) {
+    const int t = p / n;
+    s_lg[t * ldl + (p - t * n)] = lg[p];
   }
   __syncthreads();
-  const int total = s_toff[n];
-  for (int t = tid; t < total && t < tl.max_tiles; t += kGroupThreads) {
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_toff[mid] <= t)
-        lo = mid;
-      else
-        hi = mid;
-    }
-    const int r = (t - s_toff[lo]) * kTileM;
-    tl.row0[t] = s_off[lo] + r;
-    tl.rows[t] = s_tot[lo] - r < kTileM ? s_tot[lo] - r : kTileM;
+  {
+    const int t = tid >> 4;  // a whole DPP row shares its token
+    if (t < T)
+      token_topk<NB>(s_lg + t * ldl, s_sv + t * ldl, s_idx + t * k, tid & 15, n, k, true, t,
+                     topk_idx, topk_gate);
   }
+  __syncthreads();
+  // P, tokens ascending.
+  for (int e = tid; e < n; e += kSmallThreads) {
+    float acc = 0.f;
+    for (int t = 0; t < T; ++t) acc += s_sv[t * ldl + e];
+    P[e] = acc / (float)T;
+  }
+  // Counts and ranks: wave w takes experts w, w + 16, ...; lane = token.
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;  // this token's experts
+    if (lane < T)
+      for (int j = 0; j < k; ++j) {
+        const int e = s_idx[lane * k + j];
+        const uint64_t b = 1ull << (e & 63);
+        switch (e >> 6) {
+          case 0: bits0 |= b; break;
+          case 1: bits1 |= b; break;
+          case 2: bits2 |= b; break;
+          default: bits3 |= b; break;
+        }
+      }
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int e = wave; e < n; e += kSmallThreads / 64) {
+      const int w = e >> 6;
+      const uint64_t word = w == 0 ? bits0 : (w == 1 ? bits1 : (w == 2 ? bits2 : bits3));
+      const bool has = (word >> (e & 63)) & 1ull;
+      const uint64_t m = __ballot(has);
+      if (lane == 0) s_cnt[e] = __popcll(m);
+      if (has) s_rk[lane * ldl + e] = __popcll(m & below);
+    }
+  }
+  __syncthreads();
+  const int cnt_e = tid < n ? s_cnt[tid] : 0;
+  const int off_e = scan256(cnt_e, wsum, s_total);
+  if (tid < n) {
+    s_off[tid] = off_e;
+    offsets[tid] = off_e;
+    counts[tid] = cnt_e;
+    f[tid] = (float)((int64_t)cnt_e * n) / (float)((int64_t)k * T);
+  }
+  if (tid == 0) {
+    s_off[n] = *s_total;
+    offsets[n] = *s_total;
+  }
+  __syncthreads();
+  for (int p = tid; p < T * k; p += kSmallThreads) {
+    const int t = p / k;
+    const int e = s_idx[p];
+    const int pos = s_off[e] + s_rk[t * ldl + e];
+    slot_of[p] = pos;
+    perm_token[pos] = t;
+  }
+  if (tl.off) emit_tile_list(tl, n, s_cnt, s_off, s_toff, wsum, s_total, kSmallThreads);
 }
 
 constexpr int kTileThreads = 256;
@@ -896,6 +1045,51 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
     MOE_ROUTE_CASE(16, false)
   }
 #undef MOE_ROUTE_CASE
+  return hipGetLastError();
+}
+
+bool route_small(int dtype, int64_t T) { return dtype == 1 && T <= kSmallTok; }
+
+hipError_t launch_logits_small(const void* u, const void* cent, int64_t T, int d, int n, float* lg,
+                               hipStream_t s) {
+  const int B = (int)((T + kRouteTok - 1) / kRouteTok);
+  const dim3 grid((unsigned)B, (unsigned)((n + 15) / 16));
+  if (d <= 2048) {
+    const size_t sm = route_smem_bytes_aligned(16, 0) + (size_t)kWaves * 4 * 1024;
+    hipLaunchKernelGGL(logits_small_kernel<true>, grid, dim3(kThreads), sm, s,
+                       (const uint16_t*)u, (const uint16_t*)cent, T, d, n, lg);
+  } else {
+    hipLaunchKernelGGL(logits_small_kernel<false>, grid, dim3(kThreads),
+                       route_smem_bytes(16, 0), s, (const uint16_t*)u, (const uint16_t*)cent, T,
+                       d, n, lg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small(const float* lg, int64_t T, int n, int k, int32_t* topk_idx,
+                              float* topk_gate, int32_t* counts, float* f, float* P,
+                              int32_t* offsets, int32_t* perm_token, int32_t* slot_of,
+                              const TileList* tiles, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  const TileList tl = tiles ? *tiles : TileList{nullptr, nullptr, nullptr, nullptr, 0};
+  const size_t sm = route_small_smem_bytes(n, k);
+  const int nb = (n + 15) / 16;
+#define MOE_ROUTE_SMALL(NBV)                                                                   \
+  {                                                                                            \
+    if (sm > kDefaultLds) {                                                                    \
+      e = hipFuncSetAttribute((const void*)route_small_kernel<NBV>,                            \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);            \
+      if (e != hipSuccess) return e;                                                           \
+    }                                                                                          \
+    hipLaunchKernelGGL(route_small_kernel<NBV>, dim3(1), dim3(kSmallThreads), sm, s, lg, T, n, \
+                       k, topk_idx, topk_gate, counts, f, P, offsets, perm_token, slot_of, tl); \
+  }
+  if (nb <= 1) MOE_ROUTE_SMALL(1)
+  else if (nb <= 2) MOE_ROUTE_SMALL(2)
+  else if (nb <= 4) MOE_ROUTE_SMALL(4)
+  else if (nb <= 8) MOE_ROUTE_SMALL(8)
+  else MOE_ROUTE_SMALL(16)
+#undef MOE_ROUTE_SMALL
   return hipGetLastError();
 }
 

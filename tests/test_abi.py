@@ -229,9 +229,14 @@ def test_one_hip_runtime_per_process():
 
 
 def test_layer_kernel_sequence():
-    # Histogram tables of up to 32768 entries take the one-pass grouping
-    # kernel, larger ones the separate scan and scatter.
-    assert moe.moe_layer_kernels(p16(T=64)) == ["route", "group", "up_swiglu", "down", "combine"]
+    # Batches of at most 64 bf16 tokens: logits spread over the GPU, then one
+    # workgroup routes and groups the batch.  Larger batches: per-block
+    # routing, then the one-pass grouping kernel for histogram tables of up
+    # to 32768 entries, the separate scan and scatter beyond.
+    assert moe.moe_layer_kernels(p16(T=64)) == ["logits", "route_group", "up_swiglu", "down",
+                                                "combine"]
+    assert moe.moe_layer_kernels(p16(T=64, dtype="f32"))[:2] == ["route", "group"]
+    assert moe.moe_layer_kernels(p16(T=65))[:2] == ["route", "group"]
     assert moe.moe_layer_kernels(p16(T=8192))[:2] == ["route", "group"]
     assert moe.moe_layer_kernels(p16(T=8208))[:3] == ["route", "scan", "scatter"]
     assert moe.moe_layer_kernels(p16(dtype="f32"))[2:4] == ["up_swiglu_f32", "down_f32"]
