@@ -393,14 +393,16 @@ __device__ __forceinline__ void token_topk(const float* row, float* srow, int* s
       for (int r = 0; r < NB; ++r)
         if (r == rr) v[r] = -INFINITY;
     }
-    if (q == 0) {
-      sidx[j] = valid ? bi : -1;
-      if (valid) {
-        topk_idx[t * k + j] = bi;
-        topk_gate[t * k + j] = srow[bi];
-      }
-    }
+    if (q == 0) sidx[j] = valid ? bi : -1;
   }
+  // The row's lanes write the kept experts and their gates together (the
+  // rounds above carry no memory wait).
+  if (valid)
+    for (int j = q; j < k; j += 16) {
+      const int e = sidx[j];
+      topk_idx[t * k + j] = e;
+      topk_gate[t * k + j] = srow[e];
+    }
 }
 
 // Softmax, top-k, P partials, histogram.  Logits are already in s.lg.
