@@ -355,6 +355,8 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm_token = at<int32_t>(ws, L.perm_token);
   int32_t* slot_of = at<int32_t>(ws, L.slot_of);
+  // Few rows per expert: the weight-streaming FFN.
+  const bool skinny = d.T <= 64 && use_skinny(packed, d.T * d.k, d.n);
   int mark_i = 0;
   auto mark = [&]() -> hipError_t {
     if (!marks) return hipSuccess;
@@ -368,8 +370,9 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
     float* lg = at<float>(ws, L.lg);
     MOE_TRY(moe::launch_logits_small(u, centroids, d.T, d.d, d.n, lg, s));
     MOE_TRY(mark());
+    // (the weight-streaming FFN reads no tile list)
     MOE_TRY(moe::launch_route_small(lg, d.T, d.n, d.k, topk_idx, topk_gate, counts, f, P, offsets,
-                                    perm_token, slot_of, &tl, s));
+                                    perm_token, slot_of, skinny ? nullptr : &tl, s));
     MOE_TRY(mark());
   } else {
     MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
@@ -435,7 +438,6 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
     sbuf = b.y;
     nseg = 2;
   }
-  const bool skinny = d.T <= 64 && use_skinny(packed, d.T * d.k, d.n);
   if (skinny) {
     MOE_TRY(moe::launch_ffn_skinny(segs, nseg, true, s));
     MOE_TRY(mark());

@@ -903,11 +903,14 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
                      topk_idx, topk_gate);
   }
   __syncthreads();
-  // P, tokens ascending.
-  for (int e = tid; e < n; e += kSmallThreads) {
+  // P: the 16 lanes of a DPP row take one expert; lane q sums tokens q,
+  // q + 16, ... ascending, then a fixed butterfly adds the 16 partial sums.
+  for (int e0 = tid >> 4; e0 < n; e0 += kSmallThreads / 16) {
+    const int q = tid & 15;
     float acc = 0.f;
-    for (int t = 0; t < T; ++t) acc += s_sv[t * ldl + e];
-    P[e] = acc / (float)T;
+    for (int t = q; t < T; t += 16) acc += s_sv[t * ldl + e0];
+    acc = row_sum(acc);
+    if (q == 0) P[e0] = acc / (float)T;
   }
   // Counts and ranks: wave w takes experts w, w + 16, ...; lane = token.
   {
