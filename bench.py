@@ -310,6 +310,36 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
                        f"{el:.1f} s")
 
 
+def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
+    """The 64-token layer on the 16B-shaped packed weights (drawn here when
+    not given): time per step and HBM rate of its algorithmic bytes (every
+    weight of every touched expert once, plus activations)."""
+    import moe_synth
+    dcfg = moe_synth.CONFIGS["16b_decode"]
+    log("timing the 64-token decode regime")
+    if sets is None:
+        dinp, sets = gpu_shape_inputs(dcfg, 0, torch, moe, copies=args.rotate)
+    else:
+        du, dc, _ = moe_synth.make_router_inputs(dcfg, seed=0)
+        dinp = dict(inp, u=du, centroids=dc)
+    dl = Layer(dcfg, dinp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
+    dres = time_layer(dl, hip, max(args.steps, 20), args.warmup)
+    dcounts = dl.counts.cpu().numpy()
+    dwork = kernel_work(dcfg, int((dcounts > 0).sum()))
+    dbytes = sum(dwork[name]["bytes"] for name in dres["kernels"])  # the launched kernels
+    dms = dres["ms_per_step"]
+    del dl
+    return {
+        "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
+        "ms_per_step": round(dms, 4),
+        "algorithmic_bytes": int(dbytes),
+        "hbm_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "experts_touched": int((dcounts > 0).sum()),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in dres["kernel_ms"].items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +353,8 @@ def main():
                     help="skip the 2B- and 145B-shaped layers")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the 64-token decode regime (for its kernel profile)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is built and timed on a single "
@@ -341,6 +373,9 @@ def main():
         copy_probe(torch)
         return
     hip = Hip()
+    if args.decode_only:
+        print(json.dumps({"decode_64tok": decode_regime(torch, moe, hip, args)}), flush=True)
+        return
     cfg = moe_synth.CONFIGS["16b"]
     log(f"generating inputs for {cfg}")
     inp = moe_synth.make_inputs(cfg, seed=0)
@@ -416,26 +451,7 @@ def main():
     }
     del layer
     if not args.no_decode:
-        dcfg = moe_synth.CONFIGS["16b_decode"]
-        log("timing the 64-token decode regime")
-        du, dc, _ = moe_synth.make_router_inputs(dcfg, seed=0)
-        dinp = dict(inp, u=du, centroids=dc)
-        dl = Layer(dcfg, dinp, sets, moe, torch, flags)
-        dres = time_layer(dl, hip, max(args.steps, 20), args.warmup)
-        dcounts = dl.counts.cpu().numpy()
-        dwork = kernel_work(dcfg, int((dcounts > 0).sum()))
-        dbytes = sum(w["bytes"] for w in dwork.values())
-        dms = dres["ms_per_step"]
-        out["decode_64tok"] = {
-            "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
-            "ms_per_step": round(dms, 4),
-            "algorithmic_bytes": int(dbytes),
-            "hbm_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "experts_touched": int((dcounts > 0).sum()),
-            "kernel_us": {k: round(v * 1e3, 2) for k, v in dres["kernel_ms"].items()},
-        }
-        del dl
+        out["decode_64tok"] = decode_regime(torch, moe, hip, args, inp, sets)
     if not args.no_other_shapes:
         out["other_shapes"] = {}
         for name in ("2b", "145b"):
