@@ -70,6 +70,10 @@ SMALL = {
                                             K_s=0, d_ff=64, dtype="bf16"),
     "topk64_bf16": moe_synth.MoEConfig("topk64_bf16", T=48, d=64, N=128, m=1, K=64, K_s=0,
                                        d_ff=32, dtype="bf16"),
+    # 63 routed experts (the 2B shape's odd count: the last 16-expert group of
+    # the small-batch logits holds 15) and a ragged last route block.
+    "odd_experts_bf16": moe_synth.MoEConfig("odd_experts_bf16", T=50, d=128, N=63, m=1, K=8,
+                                            K_s=1, d_ff=64, dtype="bf16"),
     # One token: a single, mostly empty route block; every group but k is
     # empty and the shared experts see one row.
     "one_token_bf16": moe_synth.MoEConfig("one_token_bf16", T=1, d=64, N=8, m=1, K=3, K_s=1,
