@@ -5,17 +5,15 @@
 // padding.
 //
 // A work item is one wave (a workgroup of its own: there is no LDS and no
-// barrier, and single waves spread evenly over the CUs).  It owns one or two
-// 32-row bands of packed weights (up: the W1 and the W3 band of the same 32
-// d_ff columns; down: two consecutive bands of W2, or one where the
-// reduction is long, so that every item streams about the same bytes) and
-// the group's rows in passes of 32 (one pass unless a group holds more than
-// 32 rows; a lone dense group, the shared experts, gives each pass an item
-// of its own so its waves end with the others).  The MFMA 32x32x16 takes a
-// weight band as its first operand and 32 activation rows as its second;
-// kSkDepth 16-wide k blocks are kept in flight in a register ring.  SwiGLU
-// is applied in registers (gate and up values of one (row, column) sit in
-// the same lane and register).
+// barrier, and single waves spread evenly over the CUs).  It owns 32-row
+// bands of packed weights (up: the W1 and the W3 band of the same 32 d_ff
+// columns; down: one band of W2) and the group's rows in passes of 32 (one
+// pass unless a group holds more than 32 rows; a lone dense group, the
+// shared experts, gives each pass an item of its own so its waves end with
+// the others).  The MFMA 32x32x16 takes a weight band as its first operand
+// and 32 activation rows as its second; 16-wide k blocks are kept in flight
+// in a register ring.  SwiGLU is applied in registers (gate and up values
+// of one (row, column) sit in the same lane and register).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,11 +21,11 @@ namespace moe {
 namespace {
 
 constexpr int kSkThreads = 64;  // one wave
-// 16-wide k blocks in flight per wave.  Six keep a two-band wave within
-// 168 registers, so three waves share a SIMD and a 64-token layer's items
-// all run in one round (eight would leave a second round of a few waves).
-// A one-band wave keeps twice as many blocks in flight in the same
-// registers, so it streams its band as fast as a two-band wave streams two.
+// 16-wide k blocks in flight per wave: 6 for a band pair, 12 for a single
+// band, 12 KB of weights either way.  Both fit 168 registers, so three waves
+// share a SIMD (a 64-token layer's 2992 up-projection items then all run in
+// one round; eight blocks per band pair would not fit and left a second
+// round of a few waves).
 constexpr int kSkDepth = 6;
 constexpr int kSkWavesPerSimd = 3;
 template <bool TWO>
@@ -51,7 +49,6 @@ struct SkSeg {
   const int32_t* offsets;  // nullable: a single group of `rows` rows
   int n_groups;
   int64_t rows;
-  int bands;               // down: W2 bands per item (1 or 2); up: 1 column band
   int nbands;              // band items per group
   int passes;              // single group: 32-row passes split over items (else 1)
   int nblk;                // items per group
@@ -63,7 +60,7 @@ struct SkArgs {
 };
 
 // All passes of one item over its group's rows.  TWO: a second weight band
-// (up: the W3 band; down: the next W2 band) is streamed next to the first.
+// (the up projection's W3 band) is streamed next to the first.
 template <bool UP, bool TWO>
 __device__ __forceinline__ void skinny_item(const SkSeg& g, int64_t r0, int64_t nrows,
                                             const uint16_t* wa, const uint16_t* wb, int row_a,
@@ -184,18 +181,14 @@ __global__ __launch_bounds__(kSkThreads, kSkWavesPerSimd) void skinny_kernel(SkA
     skinny_item<true, true>(g, r0, nrows, base + bo, g.W1 + (int64_t)e * g.w_stride + bo, row,
                             row);
   } else {
-    const int row_a = blk * 32 * g.bands, row_b = row_a + 32;
-    if (row_a >= g.N) return;
-    const uint16_t* wa = base + (int64_t)(row_a >> 5) * KB * 512;
-    if (g.bands == 2 && row_b < g.N)
-      skinny_item<false, true>(g, r0, nrows, wa, base + (int64_t)(row_b >> 5) * KB * 512, row_a,
-                               row_b);
-    else
-      skinny_item<false, false>(g, r0, nrows, wa, wa, row_a, row_b);
+    const int row = blk * 32;
+    if (row >= g.N) return;
+    const uint16_t* wa = base + (int64_t)(row >> 5) * KB * 512;
+    skinny_item<false, false>(g, r0, nrows, wa, wa, row, row);
   }
 }
 
-SkSeg sk_seg(const FfnArgs& a, bool up, int bands) {
+SkSeg sk_seg(const FfnArgs& a, bool up) {
   SkSeg s{};
   if (up) {
     s.X = (const uint16_t*)a.x;
@@ -208,7 +201,6 @@ SkSeg sk_seg(const FfnArgs& a, bool up, int bands) {
     s.N = a.d_ff_g;
     s.C = (uint16_t*)a.hbuf;
     s.ldc = a.d_ff_g;
-    s.bands = 1;
     s.nblk = (a.d_ff_g + 31) / 32;
   } else {
     s.X = (const uint16_t*)a.hbuf;
@@ -221,8 +213,7 @@ SkSeg sk_seg(const FfnArgs& a, bool up, int bands) {
     s.N = a.d;
     s.C = (uint16_t*)a.y;
     s.ldc = a.d;
-    s.bands = bands;
-    s.nblk = (a.d + 32 * bands - 1) / (32 * bands);
+    s.nblk = (a.d + 31) / 32;
   }
   s.offsets = a.tiles ? a.offsets : nullptr;
   s.n_groups = a.tiles ? a.n_groups : 1;
@@ -241,12 +232,8 @@ SkSeg sk_seg(const FfnArgs& a, bool up, int bands) {
 }  // namespace
 
 hipError_t launch_ffn_skinny(const FfnArgs* segs, int nseg, bool up, hipStream_t s) {
-  // Items stream bands x K weights.  The down projection of the segment with
-  // the shortest reduction takes two bands per item, a segment with at least
-  // twice that reduction one band; the longer segment is dealt first.
-  int kmin = 0;
-  for (int i = 0; i < nseg; ++i)
-    if (segs[i].rows > 0 && (kmin == 0 || segs[i].d_ff_g < kmin)) kmin = segs[i].d_ff_g;
+  // An item streams one band pair (up) or one band (down) over the whole
+  // reduction; the segment with the longer reduction is dealt first.
   int order[2] = {0, 1};
   if (nseg == 2 && segs[1].d_ff_g > segs[0].d_ff_g) {
     order[0] = 1;
@@ -257,8 +244,7 @@ hipError_t launch_ffn_skinny(const FfnArgs* segs, int nseg, bool up, hipStream_t
   for (int oi = 0; oi < nseg; ++oi) {
     const FfnArgs& a = segs[order[oi]];
     if (a.rows == 0) continue;
-    const int bands = a.d_ff_g >= 2 * kmin ? 1 : 2;
-    args.seg[args.nseg] = sk_seg(a, up, bands);
+    args.seg[args.nseg] = sk_seg(a, up);
     grid += args.seg[args.nseg].n_groups * args.seg[args.nseg].nblk;
     ++args.nseg;
   }
