@@ -711,7 +711,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 // workgroup reads the whole [B][ldn] histogram table (small: a few tens of
 // KB), forms the per-expert totals and its own block's prefix, hence the
 // expert offsets and its block's bases, and scatters its tokens' (t, j)
-// pairs.  Workgroup 0 also writes counts, f, P, offsets and the M-tile list.
+// pairs.  Workgroup 0 also writes counts, f, P and offsets, the last
+// workgroup the M-tile list.
 // Every workgroup derives the same totals (exact integer sums), so no
 // workgroup waits for another.
 constexpr int kGroupThreads = 256;
@@ -738,19 +739,31 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
   const int r0 = c * per < B ? c * per : B;
   const int r1 = r0 + per < B ? r0 + per : B;
   const int64_t col = 4 * e4;
+  // Workgroup 0 also sums the P partials, rows ascending inside a chunk,
+  // then a fixed butterfly over chunks; its P rows load in the same batches
+  // as the count rows.
+  const bool with_P = blk == 0 && blk_P;
   i32x4 tot = {0, 0, 0, 0}, pre = {0, 0, 0, 0};
+  f32x4v ps = {0.f, 0.f, 0.f, 0.f};
   if (act) {
     // eight rows in flight at a time
     for (int rb = r0; rb < r1; rb += 8) {
       i32x4 v[8];
+      f32x4v pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = rb + i < r1 ? *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)(rb + i) * ldn + col)
-                           : i32x4{0, 0, 0, 0};
+      for (int i = 0; i < 8; ++i) {
+        const bool in = rb + i < r1;
+        v[i] = in ? *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)(rb + i) * ldn + col)
+                  : i32x4{0, 0, 0, 0};
+        pv[i] = in && with_P
+                    ? *reinterpret_cast<const f32x4v*>(blk_P + (int64_t)(rb + i) * ldn + col)
+                    : f32x4v{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         tot += v[i];
         if (rb + i < blk) pre += v[i];
+        ps += pv[i];  // rows ascending
       }
     }
   }
@@ -769,20 +782,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
         s_base[col + q] = pre[q];
       }
   }
-  // P: workgroup 0 sums the block partials, rows ascending inside a chunk,
-  // then a fixed butterfly over chunks.
-  if (blk == 0 && blk_P) {
-    f32x4v ps = {0.f, 0.f, 0.f, 0.f};
-    if (act)
-      for (int rb = r0; rb < r1; rb += 8) {
-        f32x4v v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          v[i] = rb + i < r1 ? *reinterpret_cast<const f32x4v*>(blk_P + (int64_t)(rb + i) * ldn + col)
-                             : f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ps += v[i];  // rows ascending
-      }
+  if (with_P) {
     for (int m = C >> 1; m >= 1; m >>= 1) ps += shfl_xor4(ps, m, C);
     if (act && c == 0) {
 #pragma unroll
@@ -823,8 +823,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
     slot_of[p] = pos;
     if (pos >= 0) perm_token[pos] = (int32_t)t;
   }
-  if (blk != 0 || !tl.off) return;
-  emit_tile_list(tl, n, s_tot, s_off, s_toff, wsum, &s_total, kGroupThreads);  // workgroup 0
+  // The M-tile list: the last workgroup (workgroup 0 has the P sums).
+  if (blk != B - 1 || !tl.off) return;
+  emit_tile_list(tl, n, s_tot, s_off, s_toff, wsum, &s_total, kGroupThreads);
 }
 
 // ------------------------------------------------ routing of small batches
