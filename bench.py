@@ -11,8 +11,9 @@ previous one.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel
 (timed live with HIP events recorded on the launch stream), per-kernel
-times, the 64-token decode regime's HBM rate, and the CPU oracle timed on a
-bounded sample of the same workload.
+times, the 64-token decode regime's HBM rate, the 2B- and 145B-shaped
+layers, a granularity sweep (the 16B budget cut into m = 1, 2, 4, 8 finer
+experts), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -351,6 +352,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-other-shapes", action="store_true",
                     help="skip the 2B- and 145B-shaped layers")
+    ap.add_argument("--no-granularity", action="store_true",
+                    help="skip the granularity sweep (m = 1, 2, 4, 8 at a fixed budget)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
@@ -458,6 +461,16 @@ def main():
             log(f"timing the {name}-shaped layer")
             out["other_shapes"][name] = other_shape(name, moe_synth.CONFIGS[name], torch, moe, hip,
                                                     max(10, args.steps // 3), 3)
+    if not args.no_granularity:
+        # Fine-grained segmentation at a fixed expert budget (total and
+        # activated widths constant; m = 1 is GShard's top-2 layer): the cost
+        # of finer cuts in layer throughput and GEMM efficiency.
+        out["granularity_sweep"] = {}
+        for name, gcfg in moe_synth.GRANULARITY.items():
+            log(f"timing the granularity sweep: {name}")
+            r = other_shape(name, gcfg, torch, moe, hip, max(10, args.steps // 3), 3)
+            r["m"], r["n_routed"], r["top_k"], r["d_ff"] = gcfg.m, gcfg.n, gcfg.k, gcfg.d_ff
+            out["granularity_sweep"][name] = r
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -591,17 +591,22 @@ static hipError_t launch_bf16_t(const FfnArgs* segs, int nseg, hipStream_t s) {
 }
 
 // Packed weights: the up projection takes the 128 x 256 tile (d_ff = 1408
-// is 11 of its column tiles, and two workgroups share a CU); the down
-// projection the 128 x 512 tile when d is a multiple of 512, else the
-// 128 x 256 one (d = 1280 is 5 of those, 2.5 of the wide ones).  Row-major
-// weights: 128 x 512 for both.
+// is 11 of its column tiles, and two workgroups share a CU).  The down
+// projection takes the 128 x 256 tile too, except next to a shared-expert
+// segment (whose tiles are twice as long and dealt first) with d a multiple
+// of 512, where the 128 x 512 tile measured faster (16B- and 145B-shaped
+// layers; without shared experts, and for d = 1280, the narrow tile was).
+// Row-major weights: 128 x 512 for both.
 template <bool UP>
 static hipError_t launch_bf16(const FfnArgs* segs, int nseg, bool packed, hipStream_t s) {
   if (!packed) return launch_bf16_t<UP, false, 4>(segs, nseg, s);
   if constexpr (UP) {
     return launch_bf16_t<true, true, 2>(segs, nseg, s);
   } else {
-    if (segs[0].d % Tile<4>::BN == 0) return launch_bf16_t<false, true, 4>(segs, nseg, s);
+    int live = 0;
+    for (int i = 0; i < nseg; ++i) live += segs[i].rows > 0 ? 1 : 0;
+    if (live == 2 && segs[0].d % Tile<4>::BN == 0)
+      return launch_bf16_t<false, true, 4>(segs, nseg, s);
     return launch_bf16_t<false, true, 2>(segs, nseg, s);
   }
 }

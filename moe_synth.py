@@ -77,6 +77,19 @@ CONFIGS = {
 }
 
 
+# Granularity sweep at a fixed budget: the 16B shape's N = 16 experts of width
+# D = 4 x 1408 = 5632, K = 2 of them active, cut into m finer experts each
+# (n = 16m experts of width D/m, k = 2m kept) with no shared experts, so the
+# total and the activated expert parameters stay the same for every m; m = 1
+# is GShard's top-2 layer (DeepSeekMoE explainer, "Routing in a classic MoE
+# layer" and the fine-grained segmentation it describes).
+GRANULARITY = {
+    f"gran_m{m}": MoEConfig(f"gran_m{m}", T=4096, d=2048, N=16, m=m, K=2, K_s=0,
+                            d_ff=5632 // m, dtype=BF16)
+    for m in (1, 2, 4, 8)
+}
+
+
 def _rng(seed: int, stream: str, sub: int = 0) -> np.random.Generator:
     return np.random.default_rng([seed, _STREAM[stream], sub])
 

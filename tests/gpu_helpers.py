@@ -83,7 +83,16 @@ SMALL = {
     "decode_skew_bf16": moe_synth.MoEConfig("decode_skew_bf16", T=64, d=128, N=8, m=1, K=2,
                                             K_s=0, d_ff=96, dtype="bf16", zipf_s=3.0),
 }
+# The granularity sweep at a small size: GShard top-2 of 4 experts (m = 1)
+# and the same budget cut eightfold (m = 8: top-16 of 32 experts of width 32).
+SMALL.update({
+    "gran_m1_bf16": moe_synth.MoEConfig("gran_m1_bf16", T=256, d=128, N=4, m=1, K=2, K_s=0,
+                                        d_ff=256, dtype="bf16"),
+    "gran_m8_bf16": moe_synth.MoEConfig("gran_m8_bf16", T=256, d=128, N=4, m=8, K=2, K_s=0,
+                                        d_ff=32, dtype="bf16"),
+})
 FULL = {k: v for k, v in moe_synth.CONFIGS.items() if k != "tiny"}
+FULL.update(moe_synth.GRANULARITY)
 ALL = dict(SMALL, **FULL)
 
 _cache: dict = {}

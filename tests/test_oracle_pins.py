@@ -406,3 +406,20 @@ def test_combine_matches_layer():
     y_perm[pm["slot_of"].ravel()] = o["Y"].reshape(-1, cfg.d)
     h = oracle.combine(y_perm, pm["slot_of"], o["topk_gate"], o["S"], inp["u"])
     assert (h == o["h"]).all()
+
+
+def test_granularity_sweep_keeps_the_budget():
+    """The granularity sweep cuts the 16B shape's 16 experts of width 5632
+    (2 active) into m finer ones: total and activated expert widths stay the
+    same, and m = 1 with no shared experts is GShard's top-2 layer."""
+    g = moe_synth.GRANULARITY
+    assert sorted(c.m for c in g.values()) == [1, 2, 4, 8]
+    for c in g.values():
+        assert c.K_s == 0 and c.N == 16 and c.K == 2 and c.d == 2048
+        assert c.n * c.d_ff == 16 * 5632      # all experts
+        assert c.k * c.d_ff == 2 * 5632       # experts a token passes through
+        assert c.n == 16 * c.m and c.k == 2 * c.m
+    m1 = g["gran_m1"]
+    assert (m1.n, m1.k, m1.K_s) == (16, 2, 0)
+    # at m = 4 the fine experts have the 16B shape's width
+    assert g["gran_m4"].d_ff == moe_synth.CONFIGS["16b"].d_ff
