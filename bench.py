@@ -172,14 +172,48 @@ class Layer:
         self.flags = flags
         self.stream = torch.cuda.current_stream().cuda_stream
 
-    def run(self, i: int, marks=None):
+    def run(self, i: int, marks=None, stream=None):
         w = self.weights[i % len(self.weights)]
         args = (self.p, self.u, self.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"],
                 self.h, self.idx, self.gate, self.counts, self.f, self.P, self.flags, self.ws)
+        s = self.stream if stream is None else stream
         if marks is None:
-            self.moe.moe_layer_fwd(*args, stream=self.stream)
+            self.moe.moe_layer_fwd(*args, stream=s)
         else:
-            self.moe.moe_layer_fwd_marked(*args, marks, stream=self.stream)
+            self.moe.moe_layer_fwd_marked(*args, marks, stream=s)
+
+
+def time_graph(layer: Layer, steps: int, warmup: int) -> float:
+    """ms per step of the layer replayed from a HIP graph that holds one
+    step per weight copy (captured through torch's graph API on its capture
+    stream)."""
+    torch = layer.torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.run(0, stream=side.cuda_stream)  # first call outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    n = len(layer.weights)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream().cuda_stream
+        for i in range(n):
+            layer.run(i, stream=s)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // n)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n)
+    del g
+    return ms
 
 
 def time_layer(layer: Layer, hip: Hip, steps: int, warmup: int) -> dict:
@@ -325,6 +359,7 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
         dinp = dict(inp, u=du, centroids=dc)
     dl = Layer(dcfg, dinp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
     dres = time_layer(dl, hip, max(args.steps, 20), args.warmup)
+    gms = time_graph(dl, max(args.steps, 20), args.warmup)
     dcounts = dl.counts.cpu().numpy()
     dwork = kernel_work(dcfg, int((dcounts > 0).sum()))
     dbytes = sum(dwork[name]["bytes"] for name in dres["kernels"])  # the launched kernels
@@ -337,6 +372,9 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
         "hbm_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
         "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "experts_touched": int((dcounts > 0).sum()),
+        "launch": "back-to-back moe_layer_fwd calls on one stream",
+        "graph_ms_per_step": round(gms, 4),
+        "graph_hbm_GBps": round(dbytes / (gms * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in dres["kernel_ms"].items()},
     }
 

@@ -46,6 +46,10 @@ def _load():
     lib.oracle_permute.argtypes = [i64, i32, i32, P, P, P, P]
     lib.oracle_expert.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_layer_bwd.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32,
+                                     P, P, P, P, P, P, P, P,
+                                     P, P, P, ctypes.c_double, i32, P, i64, P, P,
+                                     P, i32, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_layer.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32,
                                  P, P, P, P, P, P, P, P, P, i64,
@@ -181,6 +185,53 @@ def combine(y_perm: np.ndarray, slot_of: np.ndarray, gate: np.ndarray, shared=No
     if rc != 0:
         raise RuntimeError(f"oracle_combine failed ({rc})")
     return h
+
+
+BWD_NO_RESIDUAL, BWD_NO_SHARED = 1, 2
+
+
+def layer_bwd(inp: dict, N: int, m: int, K: int, K_s: int, topk_idx: np.ndarray, f: np.ndarray,
+              dh: np.ndarray, alpha: float, flags: int = 0, toks=None, want_dcent: bool = True,
+              experts=None, want_shared: bool = True) -> dict:
+    """Gradients of sum <dh, h> + alpha * sum_i f_i P_i (fp64 results).
+    topk_idx and f are the routing of the forward (oracle.route).  toks:
+    token rows of du (all tokens when None); experts: routed experts whose
+    weight gradients are formed (none when None)."""
+    u = _c(inp["u"])
+    T, d = u.shape
+    dt = _dt(u)
+    w1 = _c(inp["w1"])
+    d_ff = w1.shape[1]
+    n, k = sizes(N, m, K, K_s)
+    assert w1.shape[0] == n and topk_idx.shape == (T, k) and dh.shape == (T, d)
+    tk = None if toks is None else np.ascontiguousarray(toks, np.int64)
+    nt = T if tk is None else tk.size
+    ex = None if experts is None else np.ascontiguousarray(experts, np.int32)
+    ne = 0 if ex is None else ex.size
+    shared = K_s > 0 and not (flags & BWD_NO_SHARED)
+    out = dict(du=np.empty((nt, d), np.float64))
+    if want_dcent:
+        out["dcent"] = np.empty((n, d), np.float64)
+    if ne:
+        out["dw1"] = np.empty((ne, d_ff, d), np.float64)
+        out["dw3"] = np.empty((ne, d_ff, d), np.float64)
+        out["dw2"] = np.empty((ne, d, d_ff), np.float64)
+    if shared and want_shared:
+        out["dws1"] = np.empty((K_s * d_ff, d), np.float64)
+        out["dws3"] = np.empty((K_s * d_ff, d), np.float64)
+        out["dws2"] = np.empty((d, K_s * d_ff), np.float64)
+    ws = [(_c(inp.get(x)) if K_s > 0 else None) for x in ("ws1", "ws3", "ws2")]
+    rc = _load().oracle_layer_bwd(
+        T, d, N, m, K, K_s, d_ff, dt, _p(u), _p(_c(inp["centroids"])), _p(w1),
+        _p(_c(inp["w3"])), _p(_c(inp["w2"])), _p(ws[0]), _p(ws[1]), _p(ws[2]),
+        _p(np.ascontiguousarray(topk_idx, np.int32)), _p(np.ascontiguousarray(f, np.float32)),
+        _p(np.ascontiguousarray(dh, np.float32)), float(alpha), flags, _p(tk), nt,
+        _p(out["du"]), _p(out.get("dcent")), _p(ex), ne, _p(out.get("dw1")),
+        _p(out.get("dw3")), _p(out.get("dw2")), _p(out.get("dws1")), _p(out.get("dws3")),
+        _p(out.get("dws2")))
+    if rc != 0:
+        raise RuntimeError(f"oracle_layer_bwd failed ({rc})")
+    return out
 
 
 def threads() -> int:

@@ -339,6 +339,367 @@ int oracle_combine(int64_t T, int d, int k, int dtype, const void *residual, con
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Backward pass (fp64 arithmetic; inputs widened exactly).
+ *
+ * The quantity differentiated is the layer's output contracted with an
+ * upstream gradient dh, plus the expert-level balance loss of section
+ * "Expert-level balance loss" with coefficient alpha:
+ *   L = sum_t <dh_t, h_t> + alpha * sum_i f_i P_i.
+ * The kept set of every token and the counts behind f_i are piecewise
+ * constant in the inputs, so they carry no gradient; the gates and P_i
+ * carry it through the softmax.  Chain rule, written out:
+ *   expert on x with gate g (g = 1 for a shared expert), upstream dh:
+ *     a = W1 x, b = W3 x, hid = SiLU(a) * b,
+ *     dhid = W2^T dh                 (ungated),
+ *     dg   = <dhid, hid>             (= <dh, W2 hid>, the gate's gradient),
+ *     da   = g dhid * b * SiLU'(a),  db = g dhid * SiLU(a),
+ *     dx  += W1^T da + W3^T db,
+ *     dW1 += da x^T, dW3 += db x^T, dW2 += (g dh) hid^T,
+ *   SiLU'(z) = sigma(z) (1 + z (1 - sigma(z))), sigma the logistic function;
+ *   ds_i = dg of the slot that kept i (0 if none) + alpha f_i / T,
+ *   dl_i = s_i (ds_i - sum_j s_j ds_j)        (softmax),
+ *   du  += dl^T E (router), de_i = sum_t dl_{t,i} u_t,
+ *   du  += dh (residual) + dx of the kept and the shared experts.
+ * ------------------------------------------------------------------------ */
+
+#define ORC_BWD_NO_RESIDUAL 1
+#define ORC_BWD_NO_SHARED 2
+
+static double orc_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* Affinities of token t in fp64: l [n] logits, s [n] softmax. */
+static void orc_scores64(const void *u, const void *cent, int64_t t, int d, int n, int dtype,
+                         double *l, double *s) {
+  double mx = 0.0, z = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j)
+      acc += (double)orc_get(u, (size_t)t * d + j, dtype) *
+             (double)orc_get(cent, (size_t)i * d + j, dtype);
+    l[i] = acc;
+    if (i == 0 || acc > mx) mx = acc;
+  }
+  for (int i = 0; i < n; ++i) {
+    s[i] = exp(l[i] - mx);
+    z += s[i];
+  }
+  for (int i = 0; i < n; ++i) s[i] /= z;
+}
+
+/*
+ * One expert's forward pieces on x [d] and the gradient of its hidden layer:
+ * a, b [d_ff]; hid [d_ff]; dhid = W2^T dy [d_ff] (dy [d], ungated).
+ * Weights: W1/W3 rows of length d at o13 + c*ldw13; W2 row i at o2 + i*ldw2.
+ */
+static void orc_expert_fwd64(int d, int d_ff, const double *x, const void *w1, const void *w3,
+                             size_t o13, size_t ldw13, const void *w2, size_t o2, size_t ldw2,
+                             int dtype, const double *dy, double *a, double *b, double *hid,
+                             double *dhid) {
+  for (int c = 0; c < d_ff; ++c) {
+    double sa = 0.0, sb = 0.0;
+    for (int j = 0; j < d; ++j) {
+      sa += (double)orc_get(w1, o13 + (size_t)c * ldw13 + j, dtype) * x[j];
+      sb += (double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * x[j];
+    }
+    a[c] = sa;
+    b[c] = sb;
+    hid[c] = sa * orc_sigmoid(sa) * sb;
+  }
+  for (int c = 0; c < d_ff; ++c) {
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i)
+      acc += (double)orc_get(w2, o2 + (size_t)c + (size_t)i * ldw2, dtype) * dy[i];
+    dhid[c] = acc;
+  }
+}
+
+/* da, db of the SwiGLU from a, b, dhid and the gate g. */
+static void orc_swiglu_bwd64(int d_ff, double g, const double *a, const double *b,
+                             const double *dhid, double *da, double *db) {
+  for (int c = 0; c < d_ff; ++c) {
+    const double sg = orc_sigmoid(a[c]);
+    const double silu = a[c] * sg;
+    const double dsilu = sg * (1.0 + a[c] * (1.0 - sg));
+    da[c] = g * dhid[c] * b[c] * dsilu;
+    db[c] = g * dhid[c] * silu;
+  }
+}
+
+/* dx += W1^T da + W3^T db. */
+static void orc_dx64(int d, int d_ff, const void *w1, const void *w3, size_t o13, size_t ldw13,
+                     int dtype, const double *da, const double *db, double *dx) {
+  for (int j = 0; j < d; ++j) {
+    double acc = 0.0;
+    for (int c = 0; c < d_ff; ++c)
+      acc += (double)orc_get(w1, o13 + (size_t)c * ldw13 + j, dtype) * da[c] +
+             (double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * db[c];
+    dx[j] += acc;
+  }
+}
+
+/*
+ * Weight gradients of one expert over its rows (ascending token order):
+ * row r has input token tok[r], gate g[r] and upstream dh[tok[r]].
+ * dw1, dw3 [d_ff][d] and dw2 [d][ldw2o] (columns 0 .. d_ff-1 written).
+ */
+static int orc_expert_wgrad64(int d, int d_ff, int64_t nr, const int64_t *tok, const double *g,
+                              const void *u, const float *dh, const void *w1, const void *w3,
+                              size_t o13, size_t ldw13, const void *w2, size_t o2, size_t ldw2,
+                              int dtype, double *dw1, double *dw3, double *dw2, size_t ldw2o) {
+  const size_t R = nr > 0 ? (size_t)nr : 1;
+  double *X = (double *)malloc(sizeof(double) * R * d);
+  double *DY = (double *)malloc(sizeof(double) * R * d);
+  double *HID = (double *)malloc(sizeof(double) * R * d_ff);
+  double *DA = (double *)malloc(sizeof(double) * R * d_ff);
+  double *DB = (double *)malloc(sizeof(double) * R * d_ff);
+  int fail = !X || !DY || !HID || !DA || !DB;
+  if (!fail) {
+#pragma omp parallel
+    {
+      double *a = (double *)malloc(sizeof(double) * (size_t)d_ff);
+      double *b = (double *)malloc(sizeof(double) * (size_t)d_ff);
+      double *dhid = (double *)malloc(sizeof(double) * (size_t)d_ff);
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < nr; ++r) {
+        if (!a || !b || !dhid) {
+#pragma omp atomic write
+          fail = 1;
+          continue;
+        }
+        double *x = X + (size_t)r * d, *dy = DY + (size_t)r * d;
+        for (int j = 0; j < d; ++j) {
+          x[j] = (double)orc_get(u, (size_t)tok[r] * d + j, dtype);
+          dy[j] = g[r] * (double)dh[(size_t)tok[r] * d + j];
+        }
+        orc_expert_fwd64(d, d_ff, x, w1, w3, o13, ldw13, w2, o2, ldw2, dtype, dy, a, b,
+                         HID + (size_t)r * d_ff, dhid);
+        /* dy is gated already, so the SwiGLU backward takes gate one */
+        orc_swiglu_bwd64(d_ff, 1.0, a, b, dhid, DA + (size_t)r * d_ff, DB + (size_t)r * d_ff);
+      }
+      free(a);
+      free(b);
+      free(dhid);
+    }
+  }
+  if (!fail) {
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < d_ff; ++c)
+      for (int j = 0; j < d; ++j) {
+        double s1 = 0.0, s3 = 0.0;
+        for (int64_t r = 0; r < nr; ++r) {
+          s1 += DA[(size_t)r * d_ff + c] * X[(size_t)r * d + j];
+          s3 += DB[(size_t)r * d_ff + c] * X[(size_t)r * d + j];
+        }
+        dw1[(size_t)c * d + j] = s1;
+        dw3[(size_t)c * d + j] = s3;
+      }
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < d; ++i)
+      for (int c = 0; c < d_ff; ++c) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < nr; ++r) acc += DY[(size_t)r * d + i] * HID[(size_t)r * d_ff + c];
+        dw2[(size_t)i * ldw2o + c] = acc;
+      }
+  }
+  free(X);
+  free(DY);
+  free(HID);
+  free(DA);
+  free(DB);
+  return fail ? ORC_ERR_MEM : ORC_OK;
+}
+
+/*
+ * Gradients of L.  Inputs as oracle_layer (dtype storage), plus the routing
+ * the forward made (topk_idx [T][k] and f [n], as oracle_route returns them),
+ * dh [T][d] fp32 and alpha.  flags: ORC_BWD_NO_RESIDUAL drops the residual
+ * term of h, ORC_BWD_NO_SHARED the shared experts.  Outputs (fp64, each may
+ * be NULL to skip it):
+ *   du [nt][d]        rows of the tokens toks[0..nt) (all tokens if toks NULL)
+ *   dcent [n][d]      needs every token's softmax gradient
+ *   dw1, dw3 [ne][d_ff][d], dw2 [ne][d][d_ff]   experts[0..ne)
+ *   dws1, dws3 [K_s*d_ff][d], dws2 [d][K_s*d_ff] shared experts
+ */
+int oracle_layer_bwd(int64_t T, int d, int N, int m, int K, int K_s, int d_ff, int dtype,
+                     const void *u, const void *cent, const void *w1, const void *w3,
+                     const void *w2, const void *ws1, const void *ws3, const void *ws2,
+                     const int32_t *topk_idx, const float *f, const float *dh, double alpha,
+                     int flags, const int64_t *toks, int64_t nt, double *du, double *dcent,
+                     const int32_t *experts, int ne, double *dw1, double *dw3, double *dw2,
+                     double *dws1, double *dws3, double *dws2) {
+  int n, k;
+  if (oracle_sizes(N, m, K, K_s, &n, &k) != ORC_OK) return ORC_ERR_ARG;
+  const int shared = K_s > 0 && !(flags & ORC_BWD_NO_SHARED);
+  if (T < 1 || d < 1 || d_ff < 1 || (shared && (!ws1 || !ws3 || !ws2))) return ORC_ERR_ARG;
+  if (!toks) nt = T;
+  const size_t ldws2 = (size_t)K_s * d_ff;
+  int fail = 0;
+
+  /* Per-token part: softmax gradient (all tokens when dcent is wanted) and du. */
+  double *DL = NULL;
+  if (dcent) {
+    DL = (double *)malloc(sizeof(double) * (size_t)T * n);
+    if (!DL) return ORC_ERR_MEM;
+  }
+  const int64_t nrow = dcent ? T : (du ? nt : 0);
+#pragma omp parallel
+  {
+    double *x = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dy = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dx = (double *)malloc(sizeof(double) * (size_t)d);
+    double *l = (double *)malloc(sizeof(double) * (size_t)n);
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double *ds = (double *)malloc(sizeof(double) * (size_t)n);
+    double *a = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *b = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *hid = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *dhid = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *da = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *db = (double *)malloc(sizeof(double) * (size_t)d_ff);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrow; ++r) {
+      if (!x || !dy || !dx || !l || !s || !ds || !a || !b || !hid || !dhid || !da || !db) {
+#pragma omp atomic write
+        fail = 1;
+        continue;
+      }
+      /* token of this row; when every token is visited, du rows are looked up later */
+      const int64_t t = dcent ? r : (toks ? toks[r] : r);
+      for (int j = 0; j < d; ++j) {
+        x[j] = (double)orc_get(u, (size_t)t * d + j, dtype);
+        dy[j] = (double)dh[(size_t)t * d + j];
+        dx[j] = (flags & ORC_BWD_NO_RESIDUAL) ? 0.0 : dy[j];
+      }
+      orc_scores64(u, cent, t, d, n, dtype, l, s);
+      for (int i = 0; i < n; ++i) ds[i] = alpha * (double)f[i] / (double)T;
+      /* kept experts: gate gradient and input gradient */
+      for (int j = 0; j < k; ++j) {
+        const int e = topk_idx[(size_t)t * k + j];
+        const double g = s[e];
+        orc_expert_fwd64(d, d_ff, x, w1, w3, (size_t)e * d_ff * d, (size_t)d, w2,
+                         (size_t)e * d * d_ff, (size_t)d_ff, dtype, dy, a, b, hid, dhid);
+        double dg = 0.0;
+        for (int c = 0; c < d_ff; ++c) dg += dhid[c] * hid[c];
+        ds[e] += dg;
+        orc_swiglu_bwd64(d_ff, g, a, b, dhid, da, db);
+        orc_dx64(d, d_ff, w1, w3, (size_t)e * d_ff * d, (size_t)d, dtype, da, db, dx);
+      }
+      /* shared experts, weight one */
+      for (int q = 0; shared && q < K_s; ++q) {
+        orc_expert_fwd64(d, d_ff, x, ws1, ws3, (size_t)q * d_ff * d, (size_t)d, ws2,
+                         (size_t)q * d_ff, ldws2, dtype, dy, a, b, hid, dhid);
+        orc_swiglu_bwd64(d_ff, 1.0, a, b, dhid, da, db);
+        orc_dx64(d, d_ff, ws1, ws3, (size_t)q * d_ff * d, (size_t)d, dtype, da, db, dx);
+      }
+      /* softmax backward, then the router's share of du */
+      double sds = 0.0;
+      for (int i = 0; i < n; ++i) sds += s[i] * ds[i];
+      for (int i = 0; i < n; ++i) {
+        const double dl = s[i] * (ds[i] - sds);
+        if (DL) DL[(size_t)t * n + i] = dl;
+        for (int j = 0; j < d; ++j) dx[j] += dl * (double)orc_get(cent, (size_t)i * d + j, dtype);
+      }
+      if (du && !dcent) memcpy(du + (size_t)r * d, dx, sizeof(double) * (size_t)d);
+      if (du && dcent) {
+        /* every token visited: keep the rows the caller listed */
+        if (!toks) {
+          memcpy(du + (size_t)t * d, dx, sizeof(double) * (size_t)d);
+        } else {
+          for (int64_t q = 0; q < nt; ++q)
+            if (toks[q] == t) memcpy(du + (size_t)q * d, dx, sizeof(double) * (size_t)d);
+        }
+      }
+    }
+    free(x);
+    free(dy);
+    free(dx);
+    free(l);
+    free(s);
+    free(ds);
+    free(a);
+    free(b);
+    free(hid);
+    free(dhid);
+    free(da);
+    free(db);
+  }
+  if (fail) {
+    free(DL);
+    return ORC_ERR_MEM;
+  }
+  if (dcent) {
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+          acc += DL[(size_t)t * n + i] * (double)orc_get(u, (size_t)t * d + j, dtype);
+        dcent[(size_t)i * d + j] = acc;
+      }
+    free(DL);
+  }
+
+  /* Routed experts' weight gradients: rows = tokens that kept the expert. */
+  if (ne > 0 && (dw1 || dw3 || dw2)) {
+    if (!dw1 || !dw3 || !dw2 || !experts) return ORC_ERR_ARG;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)T);
+    double *g = (double *)malloc(sizeof(double) * (size_t)T);
+    double *l = (double *)malloc(sizeof(double) * (size_t)n);
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!tok || !g || !l || !s) fail = 1;
+    for (int q = 0; !fail && q < ne; ++q) {
+      const int e = experts[q];
+      if (e < 0 || e >= n) {
+        fail = 2;
+        break;
+      }
+      int64_t nr = 0;
+      for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j)
+          if (topk_idx[(size_t)t * k + j] == e) {
+            orc_scores64(u, cent, t, d, n, dtype, l, s);
+            tok[nr] = t;
+            g[nr] = s[e];
+            ++nr;
+          }
+      int rc = orc_expert_wgrad64(d, d_ff, nr, tok, g, u, dh, w1, w3, (size_t)e * d_ff * d,
+                                  (size_t)d, w2, (size_t)e * d * d_ff, (size_t)d_ff, dtype,
+                                  dw1 + (size_t)q * d_ff * d, dw3 + (size_t)q * d_ff * d,
+                                  dw2 + (size_t)q * d * d_ff, (size_t)d_ff);
+      if (rc != ORC_OK) fail = 1;
+    }
+    free(tok);
+    free(g);
+    free(l);
+    free(s);
+    if (fail) return fail == 2 ? ORC_ERR_ARG : ORC_ERR_MEM;
+  }
+
+  /* Shared experts: every token, gate one, expert by expert. */
+  if (shared && (dws1 || dws3 || dws2)) {
+    if (!dws1 || !dws3 || !dws2) return ORC_ERR_ARG;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)T);
+    double *g = (double *)malloc(sizeof(double) * (size_t)T);
+    if (!tok || !g) fail = 1;
+    for (int64_t t = 0; !fail && t < T; ++t) {
+      tok[t] = t;
+      g[t] = 1.0;
+    }
+    for (int q = 0; !fail && q < K_s; ++q) {
+      int rc = orc_expert_wgrad64(d, d_ff, T, tok, g, u, dh, ws1, ws3, (size_t)q * d_ff * d,
+                                  (size_t)d, ws2, (size_t)q * d_ff, ldws2, dtype,
+                                  dws1 + (size_t)q * d_ff * d, dws3 + (size_t)q * d_ff * d,
+                                  dws2 + (size_t)q * d_ff, ldws2);
+      if (rc != ORC_OK) fail = 1;
+    }
+    free(tok);
+    free(g);
+    if (fail) return ORC_ERR_MEM;
+  }
+  return ORC_OK;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif

@@ -32,6 +32,22 @@ MUTATIONS = {
                          "int32_t pos = cursor[e + 1] - 1 - (cursor[e]++ - offsets[e]);"),
     "shared_slice_stride": ("(size_t)q * d_ff, ldws2, dtype, hid, tmp);",
                             "(size_t)q * d_ff * d, ldws2, dtype, hid, tmp);"),
+    # backward pass
+    "dsilu_first_term_only": ("const double dsilu = sg * (1.0 + a[c] * (1.0 - sg));",
+                              "const double dsilu = sg;"),
+    "gate_dropped_in_da": ("da[c] = g * dhid[c] * b[c] * dsilu;", "da[c] = dhid[c] * b[c] * dsilu;"),
+    "softmax_bwd_uncentred": ("const double dl = s[i] * (ds[i] - sds);",
+                              "const double dl = s[i] * ds[i];"),
+    "balance_grad_without_1_over_T": ("ds[i] = alpha * (double)f[i] / (double)T;",
+                                      "ds[i] = alpha * (double)f[i];"),
+    "dw2_from_ungated_dy": ("dy[j] = g[r] * (double)dh[(size_t)tok[r] * d + j];",
+                            "dy[j] = (double)dh[(size_t)tok[r] * d + j];"),
+    "dx_w3_takes_da": ("(double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * db[c];",
+                       "(double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * da[c];"),
+    "residual_grad_dropped": ("dx[j] = (flags & ORC_BWD_NO_RESIDUAL) ? 0.0 : dy[j];",
+                              "dx[j] = 0.0;"),
+    "dcent_transposed_u": ("acc += DL[(size_t)t * n + i] * (double)orc_get(u, (size_t)t * d + j, dtype);",
+                           "acc += DL[(size_t)t * n + i] * (double)orc_get(u, (size_t)j * d + t % d, dtype);"),
 }
 
 
@@ -49,6 +65,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     "-shared", "-o", str(lib), str(mut), "-lm"], check=True)
     env = dict(os.environ, MOE_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True)
     assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
