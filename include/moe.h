@@ -1,5 +1,6 @@
 /*
- * moe.h -- C ABI of the DeepSeekMoE layer forward on one AMD MI355X (gfx950).
+ * moe.h -- C ABI of the DeepSeekMoE layer (forward and backward) on one AMD
+ * MI355X (gfx950).
  *
  * The layer (DeepSeekMoE explainer, deepforge.srivtx.xyz "DeepSeekMoE",
  * sections "Routing in a classic MoE layer", "Expert-level balance loss" and
@@ -17,7 +18,8 @@
  * Conventions for every entry point:
  *   - Buffers are DEVICE pointers owned by the caller; the library never
  *     allocates.  Scratch space comes from the caller's workspace `ws` of
- *     `ws_bytes` bytes (see moe_workspace_bytes).
+ *     `ws_bytes` bytes (see moe_workspace_bytes; moe_bwd_workspace_bytes for
+ *     the backward pass).
  *   - Every pointer must be 16-byte aligned; tensors are dense row-major.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously; no call synchronises the device or copies
@@ -76,8 +78,8 @@ typedef struct moe_problem {
   int32_t dtype; /* moe_dtype */
 } moe_problem;
 
-/* Flags.  MOE_NO_RESIDUAL / MOE_NO_SHARED (moe_layer_fwd only) drop a term
- * for component checks.  MOE_PACKED_WEIGHTS (moe_layer_fwd, moe_grouped_ffn):
+/* Flags.  MOE_NO_RESIDUAL / MOE_NO_SHARED (moe_layer_fwd, moe_layer_bwd) drop
+ * a term for component checks.  MOE_PACKED_WEIGHTS (moe_layer_fwd, moe_grouped_ffn):
  * every expert weight tensor is in the packed layout of moe_pack_weights
  * instead of row-major; bf16 only. */
 enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2, MOE_PACKED_WEIGHTS = 4 };
@@ -202,6 +204,59 @@ moe_status moe_layer_fwd_marked(const moe_problem *p, const void *u, const void 
  * invalid problem.
  */
 int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int max_names);
+
+/*
+ * Backward pass of the layer.  The gradients are those of
+ *   L = sum_t <dh_t, h_t> + alpha * sum_i f_i P_i
+ * (the layer's output against an upstream gradient dh, plus the
+ * expert-level balance loss of "Expert-level balance loss" with coefficient
+ * alpha), with the routing of the forward held fixed: the kept sets and the
+ * counts behind f_i are piecewise constant and carry no gradient, the gates
+ * and P_i carry it through the softmax.  Chain rule per expert on x with gate
+ * g: dhid = W2^T dh, dg = <dhid, SiLU(a) * b>, da = g dhid * b * SiLU'(a),
+ * db = g dhid * SiLU(a), dx = W1^T da + W3^T db, dW1 = da x^T,
+ * dW3 = db x^T, dW2 = g dh (SiLU(a) * b)^T; router: ds_i = dg (kept i) +
+ * alpha f_i / T, dl = s * (ds - <s, ds>), du += E^T dl, dE_i = sum_t dl_{t,i} u_t.
+ *   u, centroids, w1, w3, w2, ws1, ws3, ws2   as moe_layer_fwd (row-major; bf16)
+ *   topk_idx [T][k], topk_gate [T][k], f [n]  the forward's routing outputs
+ *   dh [T][d]         upstream gradient (bf16)
+ *   alpha             balance-loss coefficient (0: no balance term)
+ *   du [T][d], dcentroids [n][d]              out, fp32
+ *   dw1, dw3 [n][d_ff][d], dw2 [n][d][d_ff]   out, fp32 (zero for experts no
+ *                     token kept)
+ *   dws1, dws3 [K_s*d_ff][d], dws2 [d][K_s*d_ff]   out, fp32; NULL allowed
+ *                     when K_s = 0 or flags has MOE_NO_SHARED
+ *   flags             MOE_NO_RESIDUAL / MOE_NO_SHARED as moe_layer_fwd (the
+ *                     forward must have used the same flags)
+ *   ws                workspace of at least moe_bwd_workspace_bytes(p) bytes
+ * Intermediates (the SwiGLU gradients, q = W2^T dh, the experts' input
+ * gradients, the router's softmax gradient) are rounded to bf16; every
+ * product accumulates in fp32.  Requires p->dtype == MOE_BF16; packed
+ * weights give MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_layer_bwd(const moe_problem *p, const void *u, const void *centroids,
+                         const void *w1, const void *w3, const void *w2, const void *ws1,
+                         const void *ws3, const void *ws2, const int32_t *topk_idx,
+                         const float *topk_gate, const float *f, const void *dh, float alpha,
+                         float *du, float *dcentroids, float *dw1, float *dw3, float *dw2,
+                         float *dws1, float *dws3, float *dws2, int flags, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_layer_bwd needs on this problem; 0 when the problem
+ * is invalid or not bf16. */
+size_t moe_bwd_workspace_bytes(const moe_problem *p);
+
+/* moe_layer_bwd with measurement marks (as moe_layer_fwd_marked), and the
+ * number and labels of the kernels it launches. */
+moe_status moe_layer_bwd_marked(const moe_problem *p, const void *u, const void *centroids,
+                                const void *w1, const void *w3, const void *w2,
+                                const void *ws1, const void *ws3, const void *ws2,
+                                const int32_t *topk_idx, const float *topk_gate, const float *f,
+                                const void *dh, float alpha, float *du, float *dcentroids,
+                                float *dw1, float *dw3, float *dw2, float *dws1, float *dws3,
+                                float *dws2, int flags, void *ws, size_t ws_bytes, void *stream,
+                                void *const *marks);
+int moe_layer_bwd_kernels(const moe_problem *p, int flags, const char **names, int max_names);
 
 /* Static description of a status code. */
 const char *moe_status_str(moe_status s);

@@ -1,4 +1,4 @@
-"""DeepSeekMoE layer forward on one AMD MI355X (gfx950).
+"""DeepSeekMoE layer (forward and backward) on one AMD MI355X (gfx950).
 
 The compute path is libmoe.so (hand-written HIP, C ABI in include/moe.h);
 this package is its ctypes binding plus device-memory plumbing with torch.
@@ -12,8 +12,8 @@ _EXPORTS = ("MOE_BF16", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_NO_RE
             "MOE_NO_SHARED", "MOE_PACKED_WEIGHTS", "MoeError", "moe_combine",
             "moe_grouped_ffn", "moe_layer_fwd", "moe_layer_fwd_marked", "moe_layer_kernels",
             "moe_last_hip_error", "moe_pack_weights", "moe_permute", "moe_problem", "moe_route",
-            "moe_status_str",
-            "moe_workspace_bytes", "problem")
+            "moe_status_str", "moe_workspace_bytes", "problem", "moe_layer_bwd",
+            "moe_layer_bwd_marked", "moe_layer_bwd_kernels", "moe_bwd_workspace_bytes")
 __all__ = list(_EXPORTS)
 
 

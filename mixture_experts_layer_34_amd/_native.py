@@ -80,6 +80,16 @@ def _load():
     lib.moe_layer_kernels.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                       ctypes.c_int]
     lib.moe_layer_kernels.restype = ctypes.c_int
+    lib.moe_bwd_workspace_bytes.argtypes = [PP]
+    lib.moe_bwd_workspace_bytes.restype = sz
+    lib.moe_layer_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                  P, P, P, P, P, P, P, P, ctypes.c_int, P, sz, P]
+    lib.moe_layer_bwd.restype = st
+    lib.moe_layer_bwd_marked.argtypes = lib.moe_layer_bwd.argtypes + [P]
+    lib.moe_layer_bwd_marked.restype = st
+    lib.moe_layer_bwd_kernels.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                          ctypes.c_int]
+    lib.moe_layer_bwd_kernels.restype = ctypes.c_int
     return lib
 
 
@@ -194,3 +204,38 @@ def moe_layer_fwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx
         ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
         _ptr(ws3), _ptr(ws2), _ptr(h), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(f),
         _ptr(P), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream), arr))
+
+
+def moe_bwd_workspace_bytes(p: moe_problem) -> int:
+    return int(lib.moe_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_layer_bwd(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, dh, alpha,
+                  du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags, ws, ws_bytes=None,
+                  stream=None):
+    _check("moe_layer_bwd", lib.moe_layer_bwd(
+        ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
+        _ptr(ws3), _ptr(ws2), _ptr(topk_idx), _ptr(topk_gate), _ptr(f), _ptr(dh), float(alpha),
+        _ptr(du), _ptr(dcentroids), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3),
+        _ptr(dws2), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_layer_bwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, dh,
+                         alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags, ws, marks,
+                         ws_bytes=None, stream=None):
+    """marks: sequence of hipEvent_t handles (ints), len >= kernels + 1."""
+    arr = None if marks is None else (ctypes.c_void_p * len(marks))(*marks)
+    _check("moe_layer_bwd_marked", lib.moe_layer_bwd_marked(
+        ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
+        _ptr(ws3), _ptr(ws2), _ptr(topk_idx), _ptr(topk_gate), _ptr(f), _ptr(dh), float(alpha),
+        _ptr(du), _ptr(dcentroids), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3),
+        _ptr(dws2), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream), arr))
+
+
+def moe_layer_bwd_kernels(p, flags=0) -> list:
+    n = lib.moe_layer_bwd_kernels(ctypes.byref(p), flags, None, 0)
+    if n < 0:
+        raise MoeError("moe_layer_bwd_kernels", 2, "invalid problem")
+    names = (ctypes.c_char_p * n)()
+    lib.moe_layer_bwd_kernels(ctypes.byref(p), flags, names, n)
+    return [x.decode() for x in names]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "moe")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "skinny.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "skinny.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 

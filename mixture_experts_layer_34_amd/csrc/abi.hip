@@ -2,6 +2,7 @@
 // launch sequence.  Every check runs on the host before any HIP call, so a
 // rejected call enqueues nothing.
 #include "../../include/moe.h"
+#include "bwd.h"
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>
@@ -130,6 +131,69 @@ moe_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws)) return MOE_ERR_ALIGN;
   return MOE_OK;
+}
+
+// Backward-pass workspace: the grouping of the forward (rebuilt from
+// topk_idx), per-row gates, the SwiGLU backward's intermediates (q = dh W2
+// per row, da, db, gate * hid, gate-gradient partials), the input gradients
+// of the routed and shared experts, the router's logits and softmax
+// gradient, and per-chunk partial sums of the centroid gradient.
+struct BwdLayout {
+  size_t blk_cnt, blk_base, lrank, offsets, perm_token, slot_of;
+  size_t t_row0, t_rows, t_off, t_count;
+  size_t gperm, q, da, db, gh, dgp, dxp;
+  size_t qs, das, dbs, ghs, dxs;
+  size_t lg, dl, slabs;
+  size_t total;
+  int max_tiles, ldl, ldgp, kchunk, G;
+};
+
+BwdLayout bwd_layout(const Dims& d) {
+  BwdLayout L{};
+  const size_t B = (size_t)((d.T + kRouteTok - 1) / kRouteTok);
+  const size_t R = (size_t)d.T * d.k;
+  const size_t fs = (size_t)d.K_s * d.d_ff;
+  L.ldl = (d.n + 7) & ~7;
+  L.ldgp = 2 * ((d.d_ff + moe::kBgTile - 1) / moe::kBgTile);
+  // token chunks of the centroid gradient: at least 256 tokens, at most 64 chunks
+  const int64_t per = (d.T + 63) / 64;
+  L.kchunk = (int)(per > 256 ? (per + 63) & ~(int64_t)63 : 256);
+  L.G = (int)((d.T + L.kchunk - 1) / L.kchunk);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  const size_t ldn = (size_t)moe::blk_ld(d.n);
+  L.blk_cnt = take(B * ldn * 4);
+  L.blk_base = take(B * ldn * 4);
+  L.lrank = take(R * 4);
+  L.offsets = take((size_t)(d.n + 1) * 4);
+  L.perm_token = take(R * 4);
+  L.slot_of = take(R * 4);
+  L.max_tiles = (int)(R / kTileM) + MOE_MAX_EXPERTS;
+  L.t_row0 = take((size_t)L.max_tiles * 4);
+  L.t_rows = take((size_t)L.max_tiles * 4);
+  L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
+  L.t_count = take(4);
+  L.gperm = take(R * 4);
+  L.q = take(R * d.d_ff * 2);
+  L.da = take(R * d.d_ff * 2);
+  L.db = take(R * d.d_ff * 2);
+  L.gh = take(R * d.d_ff * 2);
+  L.dgp = take(R * L.ldgp * 4);
+  L.dxp = take(R * d.d * 2);
+  L.qs = take((size_t)d.T * fs * 2);
+  L.das = take((size_t)d.T * fs * 2);
+  L.dbs = take((size_t)d.T * fs * 2);
+  L.ghs = take((size_t)d.T * fs * 2);
+  L.dxs = take((size_t)d.T * d.d * 2);
+  L.lg = take((size_t)d.T * L.ldl * 4);
+  L.dl = take((size_t)d.T * L.ldl * 2);
+  L.slabs = take((size_t)L.G * d.n * d.d * 4);
+  L.total = o;
+  return L;
 }
 
 }  // namespace
@@ -452,6 +516,330 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
                               at<char>(ws, L.ybuf), slot_of, topk_gate, h, d.T, d.d, d.k, s));
   MOE_TRY(mark());
   return MOE_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t moe_bwd_workspace_bytes(const moe_problem* p) {
+  Dims d;
+  if (check_problem(p, &d) != MOE_OK || p->dtype != MOE_BF16) return 0;
+  return bwd_layout(d).total;
+}
+
+int moe_layer_bwd_kernels(const moe_problem* p, int flags, const char** names, int max_names) {
+  Dims d;
+  if (check_problem(p, &d) != MOE_OK) return -1;
+  (void)flags;
+  static const char* seq[] = {"hist", "scan", "scatter", "gates", "logits", "q",
+                              "ab_swiglu", "dx", "softmax_bwd", "du", "wgrad", "dcent_sum"};
+  const int c = (int)(sizeof(seq) / sizeof(seq[0]));
+  for (int i = 0; names && i < c && i < max_names; ++i) names[i] = seq[i];
+  return c;
+}
+
+moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void* centroids,
+                                const void* w1, const void* w3, const void* w2,
+                                const void* ws1, const void* ws3, const void* ws2,
+                                const int32_t* topk_idx, const float* topk_gate, const float* f,
+                                const void* dh, float alpha, float* du, float* dcentroids,
+                                float* dw1, float* dw3, float* dw2, float* dws1, float* dws3,
+                                float* dws2, int flags, void* ws, size_t ws_bytes, void* stream,
+                                void* const* marks) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS)) return MOE_ERR_SHAPE;
+  if (p->dtype != MOE_BF16 || (flags & MOE_PACKED_WEIGHTS)) return MOE_ERR_UNSUPPORTED;
+  const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
+  if (!u || !centroids || !w1 || !w3 || !w2 || !topk_idx || !topk_gate || !f || !dh || !du ||
+      !dcentroids || !dw1 || !dw3 || !dw2)
+    return MOE_ERR_NULL;
+  if (shared && (!ws1 || !ws3 || !ws2 || !dws1 || !dws3 || !dws2)) return MOE_ERR_NULL;
+  if (!aligned(u) || !aligned(centroids) || !aligned(w1) || !aligned(w3) || !aligned(w2) ||
+      !aligned(topk_idx) || !aligned(topk_gate) || !aligned(f) || !aligned(dh) || !aligned(du) ||
+      !aligned(dcentroids) || !aligned(dw1) || !aligned(dw3) || !aligned(dw2))
+    return MOE_ERR_ALIGN;
+  if (shared && (!aligned(ws1) || !aligned(ws3) || !aligned(ws2) || !aligned(dws1) ||
+                 !aligned(dws3) || !aligned(dws2)))
+    return MOE_ERR_ALIGN;
+  const BwdLayout L = bwd_layout(d);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws)) return MOE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int mark_i = 0;
+  auto mark = [&]() -> hipError_t {
+    if (!marks) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(marks[mark_i++]), s);
+  };
+  const int64_t R = d.T * d.k;
+  const int fs = d.K_s * d.d_ff;
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm_token);
+  int32_t* slot_of = at<int32_t>(ws, L.slot_of);
+  const moe::TileList tl{at<int32_t>(ws, L.t_row0), at<int32_t>(ws, L.t_rows),
+                         at<int32_t>(ws, L.t_off), at<int32_t>(ws, L.t_count), L.max_tiles};
+  MOE_TRY(mark());
+
+  // Grouping of the forward's routing (stable counting sort by expert).
+  MOE_TRY(moe::launch_hist(topk_idx, d.T, d.n, d.k, at<int32_t>(ws, L.blk_cnt),
+                           at<int32_t>(ws, L.lrank), s));
+  MOE_TRY(mark());
+  MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), nullptr, d.T, d.n, d.k, nullptr, nullptr,
+                           nullptr, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+  MOE_TRY(mark());
+  MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
+                              d.T, d.n, d.k, perm, slot_of, nullptr, nullptr, 0, s));
+  MOE_TRY(mark());
+  float* gperm = at<float>(ws, L.gperm);
+  MOE_TRY(moe::launch_perm_gates(slot_of, topk_gate, R, gperm, s));
+  MOE_TRY(mark());
+
+  // Router logits again (fp32 accumulation of bf16 products).
+  auto rows_seg = [&](moe::BgSeg& g) {
+    g.t_row0 = tl.row0;
+    g.t_rows = tl.rows;
+    g.t_off = tl.off;
+    g.t_count = tl.count;
+    g.n_groups = d.n;
+    g.max_tiles = tl.max_tiles;
+    g.a_map = perm;
+  };
+  float* lg = at<float>(ws, L.lg);
+  {
+    moe::BgSeg g{};
+    g.A[0] = u;
+    g.lda = d.d;
+    g.B[0] = centroids;
+    g.ldb = d.d;
+    g.npass = 1;
+    g.N = d.n;
+    g.K = d.d;
+    g.rows = d.T;
+    g.C = lg;
+    g.ldc = L.ldl;
+    MOE_TRY(moe::launch_bg(moe::BG_LOGITS, &g, 1, s));
+  }
+  MOE_TRY(mark());
+
+  // q = dh W2 for every grouped row (ungated), and for the shared experts.
+  uint16_t* q = at<uint16_t>(ws, L.q);
+  uint16_t* qs = at<uint16_t>(ws, L.qs);
+  {
+    moe::BgSeg g[2] = {};
+    rows_seg(g[0]);
+    g[0].A[0] = dh;
+    g[0].lda = d.d;
+    g[0].B[0] = w2;
+    g[0].ldb = d.d_ff;
+    g[0].b_gstride = (int64_t)d.d * d.d_ff;
+    g[0].npass = 1;
+    g[0].N = d.d_ff;
+    g[0].K = d.d;
+    g[0].bk_lim = d.d;
+    g[0].b_lim = d.d_ff;
+    g[0].C = q;
+    g[0].ldc = d.d_ff;
+    if (shared) {
+      g[1].A[0] = dh;
+      g[1].lda = d.d;
+      g[1].B[0] = ws2;
+      g[1].ldb = fs;
+      g[1].npass = 1;
+      g[1].N = fs;
+      g[1].K = d.d;
+      g[1].bk_lim = d.d;
+      g[1].b_lim = fs;
+      g[1].rows = d.T;
+      g[1].C = qs;
+      g[1].ldc = fs;
+    }
+    MOE_TRY(moe::launch_bg(moe::BG_PROJ, g, shared ? 2 : 1, s));
+  }
+  MOE_TRY(mark());
+
+  // a, b again; SwiGLU backward in the epilogue.
+  uint16_t* da = at<uint16_t>(ws, L.da);
+  uint16_t* db = at<uint16_t>(ws, L.db);
+  uint16_t* gh = at<uint16_t>(ws, L.gh);
+  uint16_t* das = at<uint16_t>(ws, L.das);
+  uint16_t* dbs = at<uint16_t>(ws, L.dbs);
+  uint16_t* ghs = at<uint16_t>(ws, L.ghs);
+  float* dgp = at<float>(ws, L.dgp);
+  {
+    moe::BgSeg g[2] = {};
+    rows_seg(g[0]);
+    g[0].A[0] = u;
+    g[0].lda = d.d;
+    g[0].B[0] = w1;
+    g[0].B2 = w3;
+    g[0].ldb = d.d;
+    g[0].b_gstride = (int64_t)d.d_ff * d.d;
+    g[0].npass = 1;
+    g[0].N = d.d_ff;
+    g[0].K = d.d;
+    g[0].ldc = d.d_ff;
+    g[0].q = q;
+    g[0].gate = gperm;
+    g[0].da = da;
+    g[0].db = db;
+    g[0].gh = gh;
+    g[0].dgp = dgp;
+    g[0].ldgp = L.ldgp;
+    if (shared) {
+      g[1].A[0] = u;
+      g[1].lda = d.d;
+      g[1].B[0] = ws1;
+      g[1].B2 = ws3;
+      g[1].ldb = d.d;
+      g[1].npass = 1;
+      g[1].N = fs;
+      g[1].K = d.d;
+      g[1].rows = d.T;
+      g[1].ldc = fs;
+      g[1].q = qs;
+      g[1].da = das;
+      g[1].db = dbs;
+      g[1].gh = ghs;
+    }
+    MOE_TRY(moe::launch_bg(moe::BG_SWIGLU, g, shared ? 2 : 1, s));
+  }
+  MOE_TRY(mark());
+
+  // Input gradients of the experts: dx = da W1 + db W3.
+  uint16_t* dxp = at<uint16_t>(ws, L.dxp);
+  uint16_t* dxs = at<uint16_t>(ws, L.dxs);
+  {
+    moe::BgSeg g[2] = {};
+    rows_seg(g[0]);
+    g[0].a_map = nullptr;  // grouped rows are dense here
+    g[0].A[0] = da;
+    g[0].A[1] = db;
+    g[0].lda = d.d_ff;
+    g[0].B[0] = w1;
+    g[0].B[1] = w3;
+    g[0].ldb = d.d;
+    g[0].b_gstride = (int64_t)d.d_ff * d.d;
+    g[0].npass = 2;
+    g[0].N = d.d;
+    g[0].K = d.d_ff;
+    g[0].bk_lim = d.d_ff;
+    g[0].b_lim = d.d;
+    g[0].C = dxp;
+    g[0].ldc = d.d;
+    if (shared) {
+      g[1].A[0] = das;
+      g[1].A[1] = dbs;
+      g[1].lda = fs;
+      g[1].B[0] = ws1;
+      g[1].B[1] = ws3;
+      g[1].ldb = d.d;
+      g[1].npass = 2;
+      g[1].N = d.d;
+      g[1].K = fs;
+      g[1].bk_lim = fs;
+      g[1].b_lim = d.d;
+      g[1].rows = d.T;
+      g[1].C = dxs;
+      g[1].ldc = d.d;
+    }
+    MOE_TRY(moe::launch_bg(moe::BG_PROJ, g, shared ? 2 : 1, s));
+  }
+  MOE_TRY(mark());
+
+  // Softmax backward with the gate gradients and the balance term.
+  uint16_t* dl = at<uint16_t>(ws, L.dl);
+  MOE_TRY(moe::launch_softmax_bwd(lg, L.ldl, d.T, d.n, d.k, topk_idx, slot_of, dgp, L.ldgp, f,
+                                  alpha, dl, s));
+  MOE_TRY(mark());
+
+  // du = dl E + residual + shared + sum of the kept experts' dx.
+  {
+    moe::BgSeg g{};
+    g.A[0] = dl;
+    g.lda = L.ldl;
+    g.B[0] = centroids;
+    g.ldb = d.d;
+    g.npass = 1;
+    g.N = d.d;
+    g.K = L.ldl;
+    g.bk_lim = d.n;
+    g.b_lim = d.d;
+    g.rows = d.T;
+    g.C = du;
+    g.ldc = d.d;
+    g.resid = (flags & MOE_NO_RESIDUAL) ? nullptr : dh;
+    g.dxs = shared ? dxs : nullptr;
+    g.dxp = dxp;
+    g.slot_of = slot_of;
+    g.k = d.k;
+    MOE_TRY(moe::launch_bg(moe::BG_DU, &g, 1, s));
+  }
+  MOE_TRY(mark());
+
+  // Weight gradients (one output per expert, reduced over its rows) and the
+  // centroid gradient's per-chunk partial sums, in one launch.
+  float* slabs = at<float>(ws, L.slabs);
+  {
+    moe::BgSeg g[7] = {};
+    int c = 0;
+    auto wseg = [&](const void* A, int64_t lda, int a_lim, const int32_t* amap, const void* B,
+                    int64_t ldb, int b_lim, const int32_t* bmap, int M, int N,
+                    const int32_t* koff, int kchunk, int K, int G, float* C) {
+      moe::BgSeg& x = g[c++];
+      x.A[0] = A;
+      x.lda = lda;
+      x.a_lim = a_lim;
+      x.a_map = amap;
+      x.B[0] = B;
+      x.ldb = ldb;
+      x.b_lim = b_lim;
+      x.b_map = bmap;
+      x.npass = 1;
+      x.M = M;
+      x.N = N;
+      x.koff = koff;
+      x.kchunk = kchunk;
+      x.K = K;
+      x.G = G;
+      x.C = C;
+      x.ldc = N;
+      x.c_gstride = (int64_t)M * N;
+    };
+    // dW1 = da^T x, dW3 = db^T x, dW2 = (g dh)^T hid per expert
+    wseg(da, d.d_ff, d.d_ff, nullptr, u, d.d, d.d, perm, d.d_ff, d.d, offsets, 0, 0, d.n, dw1);
+    wseg(db, d.d_ff, d.d_ff, nullptr, u, d.d, d.d, perm, d.d_ff, d.d, offsets, 0, 0, d.n, dw3);
+    wseg(dh, d.d, d.d, perm, gh, d.d_ff, d.d_ff, nullptr, d.d, d.d_ff, offsets, 0, 0, d.n, dw2);
+    if (shared) {
+      wseg(das, fs, fs, nullptr, u, d.d, d.d, nullptr, fs, d.d, nullptr, (int)d.T, (int)d.T, 1,
+           dws1);
+      wseg(dbs, fs, fs, nullptr, u, d.d, d.d, nullptr, fs, d.d, nullptr, (int)d.T, (int)d.T, 1,
+           dws3);
+      wseg(dh, d.d, d.d, nullptr, ghs, fs, fs, nullptr, d.d, fs, nullptr, (int)d.T, (int)d.T, 1,
+           dws2);
+    }
+    // dE = dl^T u over token chunks
+    wseg(dl, L.ldl, L.ldl, nullptr, u, d.d, d.d, nullptr, d.n, d.d, nullptr, L.kchunk, (int)d.T,
+         L.G, slabs);
+    MOE_TRY(moe::launch_bg(moe::BG_WGRAD, g, c, s));
+  }
+  MOE_TRY(mark());
+  MOE_TRY(moe::launch_slab_sum(slabs, L.G, (int64_t)d.n * d.d, dcentroids, s));
+  MOE_TRY(mark());
+  return MOE_OK;
+}
+
+moe_status moe_layer_bwd(const moe_problem* p, const void* u, const void* centroids,
+                         const void* w1, const void* w3, const void* w2, const void* ws1,
+                         const void* ws3, const void* ws2, const int32_t* topk_idx,
+                         const float* topk_gate, const float* f, const void* dh, float alpha,
+                         float* du, float* dcentroids, float* dw1, float* dw3, float* dw2,
+                         float* dws1, float* dws3, float* dws2, int flags, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return moe_layer_bwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f,
+                              dh, alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags,
+                              ws, ws_bytes, stream, nullptr);
 }
 
 }  // extern "C"

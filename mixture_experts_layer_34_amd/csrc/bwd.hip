@@ -1,0 +1,569 @@
+// Backward pass of the MoE layer on gfx950.
+//
+// Every product of the backward (the chain rule of SwiGLU experts, the
+// gate-weighted combine, the softmax router and the expert-level balance
+// loss) goes through one MFMA kernel: 128 x 128 output tiles, 64-deep K
+// slices staged through LDS with the next slice's global loads in flight,
+// four waves of 64 x 64 each (2 x 2 blocks of 32x32x16 bf16 MFMAs, fp32
+// accumulators).  Operands that are K-strided in memory (weights read
+// against their stored orientation, activations reduced over tokens) are
+// transposed on their way into LDS; see rb() for the bank layout.
+#include "bwd.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int BM = kBgTile, BN = kBgTile, BK = kBgK;
+constexpr int LDK = BK + 8;               // LDS row pitch (elements)
+constexpr int TILE_EL = BM * LDK + 32 * (BM / 16);  // one staged operand tile (see rb)
+constexpr int NT = 256;
+
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3 };
+
+// LDS position of tile row m (elements).  With 36-word rows, the MFMA
+// fragment reads (16 lanes on 16 consecutive rows, 16 bytes each) fall on
+// distinct banks; 16 more words before every band of 16 rows (16 (band mod 4)
+// modulo the 64 banks) also spread the transposing store of a K-strided
+// operand, where the 32 lanes of a half-wave write 8-byte pieces of 4 rows
+// 8 apart in each of 8 K groups.
+__device__ __forceinline__ int rb(int m) { return m * LDK + 32 * (m >> 4); }
+
+struct BgArgs {
+  BgSeg seg[kBgMaxSeg];
+  int start[kBgMaxSeg + 1];  // first workgroup of each segment
+  int nseg;
+};
+
+// ---- K-contiguous operand: the tile's 128 rows x 64 k.  Thread chunk
+// tid + 256 i covers row (tid >> 3) + 32 i and k (tid & 7) * 8 .. + 7.
+struct KcRows {
+  uint32_t off[4];  // byte offset of the row's first element
+  uint32_t ok;      // bit i: row i exists
+};
+
+__device__ __forceinline__ void kc_init(KcRows& R, int tid, int nvalid, const int32_t* map,
+                                        int64_t row0, int64_t ld) {
+  R.ok = 0;
+  const int kc = (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const bool v = r < nvalid;
+    const int64_t mr = v ? (map ? (int64_t)map[row0 + r] : row0 + r) : 0;
+    R.off[i] = (uint32_t)((mr * ld + kc) * 2);
+    R.ok |= (v ? 1u : 0u) << i;
+  }
+}
+
+__device__ __forceinline__ void kc_load(u32x4 v[4], const void* base, const KcRows& R, int k0,
+                                        int klim, int tid) {
+  const bool kin = k0 + (tid & 7) * 8 < klim;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (kin && ((R.ok >> i) & 1u))
+      v[i] = ld_off<u32x4>(base, R.off[i] + (uint32_t)k0 * 2u);
+    else
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void kc_store(uint16_t* s, const u32x4 v[4], int tid) {
+  const int kc = (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    *reinterpret_cast<u32x4*>(&s[rb(r) + kc]) = v[i];
+  }
+}
+
+// ---- K-strided operand: 64 k rows x 128 columns of the tile.  Thread:
+// columns mb*8 .. +7 with mb = 4 wave + (lane & 3), k rows kg*4 .. +3 with
+// kg = lane >> 2 (four lanes read 64 contiguous bytes of a row).
+__device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld,
+                                        const int32_t* map, int kbase, int klim, int col0,
+                                        int clim, int tid) {
+  const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
+  const int col = col0 + mb * 8;
+  const bool cin = col < clim;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int kr = kbase + kg * 4 + kk;
+    if (cin && kr < klim) {
+      const int64_t mr = map ? (int64_t)map[kr] : (int64_t)kr;
+      v[kk] = ld_off<u32x4>(base, (uint32_t)((mr * ld + col) * 2));
+    } else {
+      v[kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Transposes the thread's 4 (k) x 8 (columns) block into LDS rows = columns.
+__device__ __forceinline__ void ks_store(uint16_t* s, const u32x4 v[4], int tid) {
+  const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int w = i >> 1, sh = (i & 1) * 16;
+    const uint32_t lo = ((v[0][w] >> sh) & 0xFFFFu) | (((v[1][w] >> sh) & 0xFFFFu) << 16);
+    const uint32_t hi = ((v[2][w] >> sh) & 0xFFFFu) | (((v[3][w] >> sh) & 0xFFFFu) << 16);
+    *reinterpret_cast<uint2*>(&s[rb(mb * 8 + i) + kg * 4]) = make_uint2(lo, hi);
+  }
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+                    (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+}
+
+__device__ __forceinline__ void unpack4(uint2 p, float* o) {
+  o[0] = bf16_to_f32((uint16_t)(p.x & 0xFFFFu));
+  o[1] = bf16_to_f32((uint16_t)(p.x >> 16));
+  o[2] = bf16_to_f32((uint16_t)(p.y & 0xFFFFu));
+  o[3] = bf16_to_f32((uint16_t)(p.y >> 16));
+}
+
+// KGRP: k grouping; AKS / BKS: A / B K-strided in memory; DUAL: second B
+// with its own accumulators (SwiGLU's a and b).
+template <bool KGRP, bool AKS, bool BKS, int EPI, bool DUAL>
+__global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[DUAL ? 2 : 1][DUAL ? TILE_EL : 8];
+
+  const int bid = (int)blockIdx.x;
+  int si = 0;
+  while (si + 1 < args.nseg && bid >= args.start[si + 1]) ++si;
+  const BgSeg& g = args.seg[si];
+  const int L = bid - args.start[si];
+  const int nN = (g.N + BN - 1) / BN;
+
+  int e = 0, nt, m0, mvalid, kb, ke;
+  if constexpr (!KGRP) {
+    int mt;
+    if (g.t_off) {
+      if (L >= *g.t_count * nN) return;
+      int lo = 0, hi = g.n_groups;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.t_off[mid] * nN <= L)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      e = lo;
+      const int t0 = g.t_off[e], te = g.t_off[e + 1] - t0;
+      const int local = L - t0 * nN;
+      nt = local / te;
+      mt = t0 + (local - nt * te);
+      m0 = g.t_row0[mt];
+      mvalid = g.t_rows[mt];
+    } else {
+      const int num_m = (int)((g.rows + BM - 1) / BM);
+      nt = L / num_m;
+      mt = L - nt * num_m;
+      m0 = mt * BM;
+      mvalid = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
+    }
+    kb = 0;
+    ke = g.K;
+  } else {
+    const int nM = (g.M + BM - 1) / BM;
+    e = L / (nM * nN);
+    const int r = L - e * nM * nN;
+    nt = r / nM;
+    const int mt = r - nt * nM;
+    m0 = mt * BM;
+    mvalid = g.M - m0 < BM ? g.M - m0 : BM;
+    if (g.koff) {
+      kb = g.koff[e];
+      ke = g.koff[e + 1];
+    } else {
+      kb = e * g.kchunk;
+      ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+    }
+  }
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // Row maps of the K-contiguous operands (fixed across K slices).
+  KcRows ar{}, br{}, br2{};
+  if constexpr (!AKS) kc_init(ar, tid, mvalid, g.a_map, m0, g.lda);
+  if constexpr (!BKS) {
+    kc_init(br, tid, g.N - n0, nullptr, n0, g.ldb);
+    if constexpr (DUAL) br2 = br;
+  }
+
+  f32x16 acc[2][2], acc2[DUAL ? 2 : 1][DUAL ? 2 : 1];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[nb][mb][j] = 0.0f;
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc2[nb][mb][j] = 0.0f;
+      }
+    }
+
+  // Fragment rows of this lane (LDS element offsets, k = 0).
+  int fa[2], fb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    fa[i] = rb(wm * 64 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+    fb[i] = rb(wn * 64 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+  }
+
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  int buf = 0;
+  for (int p = 0; p < g.npass && nk > 0; ++p) {
+    const void* Ab = g.A[p];
+    const void* Bb = KGRP ? g.B[p]
+                          : static_cast<const void*>(static_cast<const uint16_t*>(g.B[p]) +
+                                                     (int64_t)e * g.b_gstride);
+    const void* B2b = nullptr;
+    if constexpr (DUAL)
+      B2b = static_cast<const void*>(static_cast<const uint16_t*>(g.B2) + (int64_t)e * g.b_gstride);
+    const int bklim = KGRP ? ke : g.bk_lim;
+
+    u32x4 ra[4], rbv[4], rb2[DUAL ? 4 : 1];
+    auto load = [&](int kt) {
+      const int k0 = kb + kt * BK;
+      if constexpr (AKS)
+        ks_load(ra, Ab, g.lda, g.a_map, k0, ke, m0, g.a_lim, tid);
+      else
+        kc_load(ra, Ab, ar, k0, ke, tid);
+      if constexpr (BKS) {
+        ks_load(rbv, Bb, g.ldb, KGRP ? g.b_map : nullptr, k0, bklim, n0, g.b_lim, tid);
+      } else {
+        kc_load(rbv, Bb, br, k0, ke, tid);
+        if constexpr (DUAL) kc_load(rb2, B2b, br2, k0, ke, tid);
+      }
+    };
+    auto store = [&](int b) {
+      if constexpr (AKS)
+        ks_store(sA[b], ra, tid);
+      else
+        kc_store(sA[b], ra, tid);
+      if constexpr (BKS) {
+        ks_store(sB[b], rbv, tid);
+      } else {
+        kc_store(sB[b], rbv, tid);
+        if constexpr (DUAL) kc_store(sB2[b], rb2, tid);
+      }
+    };
+
+    load(0);
+    store(buf);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][fa[i] + kk * 16]);
+          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][fb[i] + kk * 16]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[nb][mb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+        if constexpr (DUAL) {
+          bf16x8 b2[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            b2[i] = *reinterpret_cast<const bf16x8*>(&sB2[buf][fb[i] + kk * 16]);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              acc2[nb][mb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(b2[nb], af[mb], acc2[nb][mb], 0, 0, 0);
+        }
+      }
+      if (kt + 1 < nk) store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // Epilogue.  Accumulator element 4q + j of block (nb, mb) is row
+  // wm*64 + mb*32 + lane % 32 and column wn*64 + nb*32 + 8q + 4 (lane / 32) + j.
+  const int cbase = n0 + wn * 64 + 4 * (lane >> 5);
+  if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
+    const int mlim = KGRP ? g.M - m0 : mvalid;
+    char* C = static_cast<char*>(g.C) + (KGRP ? (int64_t)e * g.c_gstride * (EPI == EPI_F32 ? 4 : 2) : 0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int ml = wm * 64 + mb * 32 + (lane & 31);
+      if (ml >= mlim) continue;
+      const int64_t row = (int64_t)m0 + ml;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cbase + nb * 32 + 8 * q;
+          if (c >= g.N) continue;
+          const f32x16& a = acc[nb][mb];
+          if constexpr (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(C + (row * g.ldc + c) * 4) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          } else {
+            *reinterpret_cast<uint2*>(C + (row * g.ldc + c) * 2) =
+                pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          }
+        }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const uint16_t* Q = static_cast<const uint16_t*>(g.q);
+    uint16_t* DA = static_cast<uint16_t*>(g.da);
+    uint16_t* DB = static_cast<uint16_t*>(g.db);
+    uint16_t* GH = static_cast<uint16_t*>(g.gh);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int ml = wm * 64 + mb * 32 + (lane & 31);
+      const bool rin = ml < mvalid;
+      const int64_t row = (int64_t)m0 + (rin ? ml : 0);
+      const float gt = (g.gate && rin) ? g.gate[row] : 1.0f;
+      float part = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cbase + nb * 32 + 8 * q;
+          if (!rin || c >= g.N) continue;
+          const int64_t at = row * g.ldc + c;
+          float qv[4];
+          unpack4(*reinterpret_cast<const uint2*>(&Q[at]), qv);
+          float da[4], db[4], gh[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = acc[nb][mb][4 * q + j], b = acc2[nb][mb][4 * q + j];
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float sl = a * sg;
+            const float dsl = sg * (1.0f + a * (1.0f - sg));
+            const float hid = sl * b;
+            da[j] = gt * qv[j] * b * dsl;
+            db[j] = gt * qv[j] * sl;
+            gh[j] = gt * hid;
+            part += qv[j] * hid;
+          }
+          *reinterpret_cast<uint2*>(&DA[at]) = pack4(da[0], da[1], da[2], da[3]);
+          *reinterpret_cast<uint2*>(&DB[at]) = pack4(db[0], db[1], db[2], db[3]);
+          *reinterpret_cast<uint2*>(&GH[at]) = pack4(gh[0], gh[1], gh[2], gh[3]);
+        }
+      if (g.gate) {
+        part += __shfl_xor(part, 32);
+        if (rin && lane < 32) g.dgp[row * g.ldgp + nt * 2 + wn] = part;
+      }
+    }
+  } else {  // EPI_DU
+    const uint16_t* R = static_cast<const uint16_t*>(g.resid);
+    const uint16_t* S = static_cast<const uint16_t*>(g.dxs);
+    const uint16_t* X = static_cast<const uint16_t*>(g.dxp);
+    float* C = static_cast<float*>(g.C);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int ml = wm * 64 + mb * 32 + (lane & 31);
+      if (ml >= mvalid) continue;
+      const int64_t t = (int64_t)m0 + ml;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cbase + nb * 32 + 8 * q;
+          if (c >= g.N) continue;
+          float o[4], tmp[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * q + j];
+          const int64_t at = t * g.ldc + c;
+          if (R) {
+            unpack4(*reinterpret_cast<const uint2*>(&R[at]), tmp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+          }
+          if (S) {
+            unpack4(*reinterpret_cast<const uint2*>(&S[at]), tmp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+          }
+          for (int s = 0; s < g.k; ++s) {
+            const int64_t r = g.slot_of[t * g.k + s];
+            unpack4(*reinterpret_cast<const uint2*>(&X[r * g.ldc + c]), tmp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+          }
+          *reinterpret_cast<float4*>(&C[at]) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+  }
+}
+
+__global__ void perm_gates_kernel(const int32_t* __restrict__ slot_of,
+                                  const float* __restrict__ gate, int64_t R,
+                                  float* __restrict__ gperm) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < R) gperm[slot_of[i]] = gate[i];
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// One wave per token, four tokens per workgroup; lanes own experts
+// lane + 64 q.
+__global__ __launch_bounds__(256) void softmax_bwd_kernel(
+    const float* __restrict__ lg, int ldl, int64_t T, int n, int k,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ dgp, int ldgp, const float* __restrict__ f, float alpha,
+    uint16_t* __restrict__ dl) {
+  __shared__ float sds[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + w;
+  const bool live = t < T;
+  constexpr int Q = kMaxExperts / 64;
+  float s[Q];
+  float mx = -3.0e38f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = lane + 64 * q;
+    s[q] = (live && i < n) ? lg[t * ldl + i] : -3.0e38f;
+    mx = fmaxf(mx, s[q]);
+  }
+  mx = wave_max(mx);
+  float z = 0.0f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = lane + 64 * q;
+    s[q] = (live && i < n) ? __expf(s[q] - mx) : 0.0f;
+    z += s[q];
+  }
+  z = wave_sum(z);
+  const float inv = live ? 1.0f / z : 0.0f;
+  const float bal = alpha / (float)T;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = lane + 64 * q;
+    s[q] *= inv;
+    if (i < n) sds[w][i] = live ? bal * f[i] : 0.0f;
+  }
+  __syncthreads();
+  if (live) {
+    for (int j = lane; j < k; j += 64) {
+      const int64_t r = slot_of[t * k + j];
+      float dg = 0.0f;
+      for (int p = 0; p < ldgp; ++p) dg += dgp[r * ldgp + p];
+      sds[w][topk_idx[t * k + j]] += dg;  // the kept experts of a token are distinct
+    }
+  }
+  __syncthreads();
+  float ds[Q], dot = 0.0f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = lane + 64 * q;
+    ds[q] = i < n ? sds[w][i] : 0.0f;
+    dot += s[q] * ds[q];
+  }
+  dot = wave_sum(dot);
+  if (!live) return;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = lane + 64 * q;
+    if (i < ldl) dl[t * ldl + i] = i < n ? f32_to_bf16(s[q] * (ds[q] - dot)) : (uint16_t)0;
+  }
+}
+
+__global__ void slab_sum_kernel(const float4* __restrict__ slabs, int G, int64_t count4,
+                                float4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count4) return;
+  float4 a = slabs[i];
+  for (int g = 1; g < G; ++g) {
+    const float4 b = slabs[(int64_t)g * count4 + i];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  out[i] = a;
+}
+
+int seg_blocks(BgKind kind, const BgSeg& g) {
+  const int nN = (g.N + BN - 1) / BN;
+  if (kind == BG_WGRAD) return g.G * ((g.M + BM - 1) / BM) * nN;
+  if (g.t_off) return g.max_tiles * nN;
+  return (int)((g.rows + BM - 1) / BM) * nN;
+}
+
+template <bool KGRP, bool AKS, bool BKS, int EPI, bool DUAL>
+hipError_t launch_t(const BgArgs& args, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((bg_kernel<KGRP, AKS, BKS, EPI, DUAL>), dim3(grid), dim3(NT), 0, s, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
+  if (nseg < 1 || nseg > kBgMaxSeg) return hipErrorInvalidValue;
+  BgArgs args{};
+  args.nseg = nseg;
+  args.start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    args.seg[i] = segs[i];
+    args.start[i + 1] = args.start[i] + seg_blocks(kind, segs[i]);
+  }
+  for (int i = nseg + 1; i <= kBgMaxSeg; ++i) args.start[i] = args.start[nseg];
+  const int grid = args.start[nseg];
+  if (grid == 0) return hipSuccess;
+  switch (kind) {
+    case BG_LOGITS: return launch_t<false, false, false, EPI_F32, false>(args, grid, s);
+    case BG_PROJ: return launch_t<false, false, true, EPI_BF16, false>(args, grid, s);
+    case BG_SWIGLU: return launch_t<false, false, false, EPI_SWIGLU, true>(args, grid, s);
+    case BG_DU: return launch_t<false, false, true, EPI_DU, false>(args, grid, s);
+    case BG_WGRAD: return launch_t<true, true, true, EPI_F32, false>(args, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_perm_gates(const int32_t* slot_of, const float* topk_gate, int64_t R,
+                             float* gperm, hipStream_t s) {
+  const int64_t blocks = (R + 255) / 256;
+  hipLaunchKernelGGL(perm_gates_kernel, dim3((unsigned)blocks), dim3(256), 0, s, slot_of,
+                     topk_gate, R, gperm);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_bwd(const float* lg, int ldl, int64_t T, int n, int k,
+                              const int32_t* topk_idx, const int32_t* slot_of, const float* dgp,
+                              int ldgp, const float* f, float alpha, uint16_t* dl, hipStream_t s) {
+  const int64_t blocks = (T + 3) / 4;
+  hipLaunchKernelGGL(softmax_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, s, lg, ldl, T, n,
+                     k, topk_idx, slot_of, dgp, ldgp, f, alpha, dl);
+  return hipGetLastError();
+}
+
+hipError_t launch_slab_sum(const float* slabs, int G, int64_t count, float* out, hipStream_t s) {
+  const int64_t c4 = count / 4;
+  const int64_t blocks = (c4 + 255) / 256;
+  hipLaunchKernelGGL(slab_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(slabs), G, c4,
+                     reinterpret_cast<float4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace moe

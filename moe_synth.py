@@ -27,7 +27,7 @@ BF16 = "bf16"
 
 # Stream ids: one independent PCG64 stream per tensor.
 _STREAM = {"u": 1, "centroids": 2, "w1": 3, "w3": 4, "w2": 5,
-           "ws1": 6, "ws3": 7, "ws2": 8, "redraw": 9}
+           "ws1": 6, "ws3": 7, "ws2": 8, "redraw": 9, "dh": 10}
 
 MARGIN = 1e-4
 
@@ -185,6 +185,17 @@ def make_router_inputs(cfg: MoEConfig, seed: int = 0, certify: bool = True):
             if rounds > 1000:
                 raise RuntimeError("margin certification did not converge")
     return u, cent, redraws
+
+
+# Balance-loss coefficient alpha_1 the explainer gives (section "Expert-level
+# balance loss"): 0.01 for the 2B runs, 0.001 at 16B.
+BALANCE_ALPHA = {"2b": 0.01, "16b": 0.001}
+
+
+def make_upstream_grad(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """Gradient of a loss with respect to the layer output h [T][d] for the
+    backward pass: standard normals in the workload's storage type."""
+    return _store(_normal(_rng(seed, "dh"), (cfg.T, cfg.d), 1.0), cfg.dtype)
 
 
 def make_inputs(cfg: MoEConfig, seed: int = 0, certify: bool = True) -> dict:

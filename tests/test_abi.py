@@ -240,3 +240,45 @@ def test_layer_kernel_sequence():
     assert moe.moe_layer_kernels(p16(T=8192))[:2] == ["route", "group"]
     assert moe.moe_layer_kernels(p16(T=8208))[:3] == ["route", "scan", "scatter"]
     assert moe.moe_layer_kernels(p16(dtype="f32"))[2:4] == ["up_swiglu_f32", "down_f32"]
+
+
+def test_layer_bwd_checks():
+    p = p16()
+    ws = moe.moe_bwd_workspace_bytes(p)
+    assert ws > 0 and ws % 256 == 0
+    assert moe.moe_bwd_workspace_bytes(p16(dtype="f32")) == 0
+    # u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, dh
+    ins = [A] * 12
+    # du, dcent, dw1, dw3, dw2, dws1, dws3, dws2
+    outs = [A] * 8
+    call = lambda pp, i, a, o, flags, w: moe.moe_layer_bwd(pp, *i, a, *o, flags, A, w)
+    assert status(call, p16(dtype="f32"), ins, 0.0, outs, 0, BIG) == "MOE_ERR_UNSUPPORTED"
+    assert status(call, p, ins, 0.0, outs, moe.MOE_PACKED_WEIGHTS, BIG) == "MOE_ERR_UNSUPPORTED"
+    assert status(call, p, ins, 0.0, outs, 8, BIG) == "MOE_ERR_SHAPE"
+    assert status(call, p16(T=0), ins, 0.0, outs, 0, BIG) == "MOE_ERR_SHAPE"
+    for i in range(12):
+        if i in (5, 6, 7):
+            continue  # shared weights: checked below
+        bad = list(ins)
+        bad[i] = None
+        assert status(call, p, bad, 0.0, outs, 0, BIG) == "MOE_ERR_NULL", i
+        bad[i] = MIS
+        assert status(call, p, bad, 0.0, outs, 0, BIG) == "MOE_ERR_ALIGN", i
+    for i in range(8):
+        bad = list(outs)
+        bad[i] = None
+        assert status(call, p, ins, 0.0, bad, 0, BIG) == "MOE_ERR_NULL", i
+    # shared experts' weights and gradients may be NULL when they are dropped
+    no_sh_in = ins[:5] + [None] * 3 + ins[8:]
+    no_sh_out = outs[:5] + [None] * 3
+    assert status(call, p, no_sh_in, 0.0, outs, 0, BIG) == "MOE_ERR_NULL"
+    assert status(call, p, ins, 0.0, no_sh_out, 0, BIG) == "MOE_ERR_NULL"
+    assert status(call, p, no_sh_in, 0.0, no_sh_out, moe.MOE_NO_SHARED, ws - 256) == \
+        "MOE_ERR_WORKSPACE"
+    assert status(call, p, ins, 0.0, outs, 0, 0) == "MOE_ERR_WORKSPACE"
+
+
+def test_layer_bwd_kernel_sequence():
+    assert moe.moe_layer_bwd_kernels(p16()) == [
+        "hist", "scan", "scatter", "gates", "logits", "q", "ab_swiglu", "dx", "softmax_bwd",
+        "du", "wgrad", "dcent_sum"]
