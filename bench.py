@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the DeepSeekMoE layer forward on one MI355X.
+"""Benchmark of the DeepSeekMoE layer on one MI355X.
 
 Workload: the 16B-shaped layer (T = 4096 tokens, d = 2048, 64 routed
 fine-grained experts with 6 kept per token, 2 shared experts, SwiGLU
@@ -11,9 +11,11 @@ previous one.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel
 (timed live with HIP events recorded on the launch stream), per-kernel
-times, the 64-token decode regime's HBM rate, the 2B- and 145B-shaped
-layers, a granularity sweep (the 16B budget cut into m = 1, 2, 4, 8 finer
-experts), and the CPU oracle timed on a bounded sample of the same workload.
+times, the backward pass of the same layer (moe_layer_bwd: time per step,
+per-kernel times and its dominant kernel's roofline), the 64-token decode
+regime's HBM rate, the 2B- and 145B-shaped layers, a granularity sweep (the
+16B budget cut into m = 1, 2, 4, 8 finer experts), and the CPU oracle timed
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -135,6 +137,45 @@ def kernel_work(cfg, n_active: int, es: int = 2) -> dict:
     w["logits"] = dict(flop=2 * T * d * n, bytes=T * d * es + n * d * es + T * n * 4)
     w["route_group"] = dict(flop=0, bytes=T * n * 4 + R * 20 + n * 12)
     w["combine"] = dict(flop=2 * R * d, bytes=3 * T * d * es + R * d * es + R * 8)
+    return w
+
+
+def bwd_kernel_work(cfg, n_active: int, es: int = 2) -> dict:
+    """Algorithmic FLOPs and HBM bytes of each kernel of one moe_layer_bwd
+    call (gradients of u, the centroids and all expert weights).  The a, b
+    projections are recomputed, so the routed experts cost 8 products of
+    2 R d d_ff FLOPs against the forward's 3."""
+    T, d, f, n, k, ks = cfg.T, cfg.d, cfg.d_ff, cfg.n, cfg.k, cfg.K_s
+    R = T * k
+    fs = ks * f
+    ldl = (n + 7) // 8 * 8
+    G = max(1, (T + 255) // 256)
+    w = {}
+    w["hist"] = dict(flop=0, bytes=R * 8)
+    w["scan"] = dict(flop=0, bytes=((T + 15) // 16) * n * 8 + n * 8)
+    w["scatter"] = dict(flop=0, bytes=R * 4 * 4)
+    w["gather"] = dict(flop=0, bytes=2 * T * d * es + 2 * R * d * es + R * 12)
+    w["logits"] = dict(flop=2 * T * n * d, bytes=T * d * es + n * d * es + T * ldl * 4)
+    w["q"] = dict(flop=2 * R * d * f + 2 * T * d * fs,
+                  bytes=n_active * d * f * es + fs * d * es + (R + T) * d * es
+                  + (R * f + T * fs) * es)
+    w["ab_swiglu"] = dict(flop=4 * R * d * f + 4 * T * d * fs,
+                          bytes=2 * (n_active * f + fs) * d * es + (R + T) * d * es
+                          + 4 * (R * f + T * fs) * es + R * 8)
+    w["dx"] = dict(flop=4 * R * f * d + 4 * T * fs * d,
+                   bytes=2 * (n_active * f + fs) * d * es + 2 * (R * f + T * fs) * es
+                   + (R + T) * d * es)
+    w["softmax_bwd"] = dict(flop=0, bytes=T * ldl * 6 + R * 8 + R * 2 * ((f + 127) // 128) * 4)
+    w["du"] = dict(flop=2 * T * n * d, bytes=T * d * 4 + 2 * T * d * es + R * d * es + n * d * es)
+    w["wgrad13"] = dict(flop=4 * R * d * f + 4 * T * d * fs,
+                        bytes=2 * (n * f + fs) * d * 4 + 2 * (R * f + T * fs) * es
+                        + (R + T) * d * es)
+    w["wgrad2"] = dict(flop=2 * R * d * f + 2 * T * d * fs + 2 * T * n * d,
+                       bytes=(n * f + fs) * d * 4 + (R * f + T * fs) * es + (R + T) * d * es
+                       + T * ldl * es + T * d * es + G * n * d * 4)
+    w["wgrad"] = dict(flop=w["wgrad13"]["flop"] + w["wgrad2"]["flop"],
+                      bytes=w["wgrad13"]["bytes"] + w["wgrad2"]["bytes"])
+    w["dcent_sum"] = dict(flop=0, bytes=(G + 1) * n * d * 4)
     return w
 
 
@@ -379,6 +420,90 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
     }
 
 
+def backward_regime(torch, moe, hip, args, cfg, inp, layer) -> dict:
+    """moe_layer_bwd on the 16B-shaped layer: row-major weights (two copies
+    rotated), the forward's routing, a seeded upstream gradient and the
+    16B balance coefficient.  Time per step, per-kernel times from marks and
+    the roofline of the dominant kernel."""
+    import moe_synth
+    from mixture_experts_layer_34_amd.device import to_device
+    log("timing the 16B-shaped backward pass")
+    p = layer.p
+    layer.run(0)
+    torch.cuda.synchronize()
+    sets = [{k: to_device(inp[k], "cuda") for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}
+            for _ in range(args.rotate)]
+    dh = to_device(moe_synth.make_upstream_grad(cfg, seed=1), "cuda")
+    alpha = moe_synth.BALANCE_ALPHA["16b"]
+    f32 = dict(dtype=torch.float32, device="cuda")
+    n, d, f, fs = cfg.n, cfg.d, cfg.d_ff, cfg.K_s * cfg.d_ff
+    g = dict(du=torch.empty((cfg.T, d), **f32), dc=torch.empty((n, d), **f32),
+             dw1=torch.empty((n, f, d), **f32), dw3=torch.empty((n, f, d), **f32),
+             dw2=torch.empty((n, d, f), **f32), dws1=torch.empty((fs, d), **f32),
+             dws3=torch.empty((fs, d), **f32), dws2=torch.empty((d, fs), **f32))
+    ws = torch.empty(moe.moe_bwd_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    stream = layer.stream
+
+    def run(i, marks=None):
+        w = sets[i % len(sets)]
+        a = (p, layer.u, layer.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"],
+             layer.idx, layer.gate, layer.f, dh, alpha, g["du"], g["dc"], g["dw1"], g["dw3"],
+             g["dw2"], g["dws1"], g["dws3"], g["dws2"], 0, ws)
+        if marks is None:
+            moe.moe_layer_bwd(*a, stream=stream)
+        else:
+            moe.moe_layer_bwd_marked(*a, marks, stream=stream)
+
+    steps = max(10, args.steps // 2)
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    e0, e1 = hip.event(), hip.event()
+    rec(e0, stream)
+    for i in range(steps):
+        run(i)
+    rec(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    names = moe.moe_layer_bwd_kernels(p)
+    marks = [[hip.event() for _ in range(len(names) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        run(i, marks[i])
+    torch.cuda.synchronize()
+    per = {nm: sum(hip.ms(marks[i][j], marks[i][j + 1]) for i in range(steps)) / steps
+           for j, nm in enumerate(names)}
+    for row in marks:
+        for e in row:
+            hip.destroy(e)
+    hip.destroy(e0)
+    hip.destroy(e1)
+    n_active = int((layer.counts.cpu().numpy() > 0).sum())
+    work = bwd_kernel_work(cfg, n_active)
+    kern = {nm: dict(us=round(v * 1e3, 2), **roofline(work[nm]["flop"], work[nm]["bytes"],
+                                                       v * 1e-3)) for nm, v in per.items()}
+    dom = max(per, key=per.get)
+    droof = roofline(work[dom]["flop"], work[dom]["bytes"], per[dom] * 1e-3)
+    droof.update(kernel=dom, us_per_launch=round(per[dom] * 1e3, 2), traffic=None)
+    gemm = [nm for nm in names if nm in ("q", "ab_swiglu", "dx", "wgrad", "wgrad13", "wgrad2")]
+    gflop = sum(work[nm]["flop"] for nm in gemm)
+    gsec = sum(per[nm] for nm in gemm) * 1e-3
+    del sets, g, ws
+    return {
+        "workload": "DeepSeekMoE 16B-shaped layer backward: gradients of u, centroids and all "
+                    "expert weights, balance loss alpha = 0.001",
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "flop_per_step": int(sum(w["flop"] for w in work.values())),
+        "gemm_tflops": round(gflop / gsec / 1e12, 1),
+        "gemm_mfma_frac": round(gflop / gsec / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": droof,
+        "kernels": kern,
+        "weight_layout": "row-major",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +513,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the 16B-shaped backward pass")
     ap.add_argument("--no-other-shapes", action="store_true",
                     help="skip the 2B- and 145B-shaped layers")
     ap.add_argument("--no-granularity", action="store_true",
@@ -490,6 +617,9 @@ def main():
         "weight_pack_ms_once": round(pack_ms, 3),
         "wall_ms_per_step": round(res["wall_ms_per_step"], 4),
     }
+    if not args.no_backward:
+        out["backward_16b"] = backward_regime(torch, moe, hip, args, cfg, inp, layer)
+        out["backward_16b"]["train_step_ms"] = round(ms + out["backward_16b"]["ms_per_step"], 4)
     del layer
     if not args.no_decode:
         out["decode_64tok"] = decode_regime(torch, moe, hip, args, inp, sets)

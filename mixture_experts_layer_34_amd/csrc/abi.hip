@@ -134,14 +134,15 @@ moe_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
 }
 
 // Backward-pass workspace: the grouping of the forward (rebuilt from
-// topk_idx), per-row gates, the SwiGLU backward's intermediates (q = dh W2
+// topk_idx), per-row gates and the rows of u and dh in grouped order, the
+// SwiGLU backward's intermediates (q = dh W2
 // per row, da, db, gate * hid, gate-gradient partials), the input gradients
 // of the routed and shared experts, the router's logits and softmax
 // gradient, and per-chunk partial sums of the centroid gradient.
 struct BwdLayout {
   size_t blk_cnt, blk_base, lrank, offsets, perm_token, slot_of;
   size_t t_row0, t_rows, t_off, t_count;
-  size_t gperm, q, da, db, gh, dgp, dxp;
+  size_t gperm, xp, dhp, q, da, db, gh, dgp, dxp;
   size_t qs, das, dbs, ghs, dxs;
   size_t lg, dl, slabs;
   size_t total;
@@ -178,6 +179,8 @@ BwdLayout bwd_layout(const Dims& d) {
   L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
   L.t_count = take(4);
   L.gperm = take(R * 4);
+  L.xp = take(R * d.d * 2);
+  L.dhp = take(R * d.d * 2);
   L.q = take(R * d.d_ff * 2);
   L.da = take(R * d.d_ff * 2);
   L.db = take(R * d.d_ff * 2);
@@ -532,8 +535,9 @@ int moe_layer_bwd_kernels(const moe_problem* p, int flags, const char** names, i
   Dims d;
   if (check_problem(p, &d) != MOE_OK) return -1;
   (void)flags;
-  static const char* seq[] = {"hist", "scan", "scatter", "gates", "logits", "q",
-                              "ab_swiglu", "dx", "softmax_bwd", "du", "wgrad", "dcent_sum"};
+  static const char* seq[] = {"hist",        "scan", "scatter", "gather",  "logits",
+                              "q",           "ab_swiglu", "dx", "softmax_bwd", "du",
+                              "wgrad",       "dcent_sum"};
   const int c = (int)(sizeof(seq) / sizeof(seq[0]));
   for (int i = 0; names && i < c && i < max_names; ++i) names[i] = seq[i];
   return c;
@@ -593,7 +597,9 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
                               d.T, d.n, d.k, perm, slot_of, nullptr, nullptr, 0, s));
   MOE_TRY(mark());
   float* gperm = at<float>(ws, L.gperm);
-  MOE_TRY(moe::launch_perm_gates(slot_of, topk_gate, R, gperm, s));
+  uint16_t* xp = at<uint16_t>(ws, L.xp);
+  uint16_t* dhp = at<uint16_t>(ws, L.dhp);
+  MOE_TRY(moe::launch_gather_rows(slot_of, topk_gate, u, dh, d.T, d.k, d.d, xp, dhp, gperm, s));
   MOE_TRY(mark());
 
   // Router logits again (fp32 accumulation of bf16 products).
@@ -604,7 +610,6 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     g.t_count = tl.count;
     g.n_groups = d.n;
     g.max_tiles = tl.max_tiles;
-    g.a_map = perm;
   };
   float* lg = at<float>(ws, L.lg);
   {
@@ -629,7 +634,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   {
     moe::BgSeg g[2] = {};
     rows_seg(g[0]);
-    g[0].A[0] = dh;
+    g[0].A[0] = dhp;
     g[0].lda = d.d;
     g[0].B[0] = w2;
     g[0].ldb = d.d_ff;
@@ -670,7 +675,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   {
     moe::BgSeg g[2] = {};
     rows_seg(g[0]);
-    g[0].A[0] = u;
+    g[0].A[0] = xp;
     g[0].lda = d.d;
     g[0].B[0] = w1;
     g[0].B2 = w3;
@@ -713,7 +718,6 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   {
     moe::BgSeg g[2] = {};
     rows_seg(g[0]);
-    g[0].a_map = nullptr;  // grouped rows are dense here
     g[0].A[0] = da;
     g[0].A[1] = db;
     g[0].lda = d.d_ff;
@@ -781,47 +785,47 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   // Weight gradients (one output per expert, reduced over its rows) and the
   // centroid gradient's per-chunk partial sums, in one launch.
   float* slabs = at<float>(ws, L.slabs);
+  auto wseg = [&](moe::BgSeg& x, const void* A, int64_t lda, const void* B, const void* B2,
+                  int64_t ldb, int M, int N, const int32_t* koff, int kchunk, int K, int G,
+                  float* C, float* C2, int64_t ldc) {
+    x.A[0] = A;
+    x.lda = lda;
+    x.a_lim = (int)lda;
+    x.B[0] = B;
+    x.B2 = B2;
+    x.ldb = ldb;
+    x.b_lim = (int)ldb;
+    x.npass = 1;
+    x.M = M;
+    x.N = N;
+    x.koff = koff;
+    x.kchunk = kchunk;
+    x.K = K;
+    x.G = G;
+    x.C = C;
+    x.C2 = C2;
+    x.ldc = ldc;
+    x.c_gstride = (int64_t)M * N;
+  };
   {
     moe::BgSeg g[7] = {};
     int c = 0;
-    auto wseg = [&](const void* A, int64_t lda, int a_lim, const int32_t* amap, const void* B,
-                    int64_t ldb, int b_lim, const int32_t* bmap, int M, int N,
-                    const int32_t* koff, int kchunk, int K, int G, float* C) {
-      moe::BgSeg& x = g[c++];
-      x.A[0] = A;
-      x.lda = lda;
-      x.a_lim = a_lim;
-      x.a_map = amap;
-      x.B[0] = B;
-      x.ldb = ldb;
-      x.b_lim = b_lim;
-      x.b_map = bmap;
-      x.npass = 1;
-      x.M = M;
-      x.N = N;
-      x.koff = koff;
-      x.kchunk = kchunk;
-      x.K = K;
-      x.G = G;
-      x.C = C;
-      x.ldc = N;
-      x.c_gstride = (int64_t)M * N;
-    };
     // dW1 = da^T x, dW3 = db^T x, dW2 = (g dh)^T hid per expert
-    wseg(da, d.d_ff, d.d_ff, nullptr, u, d.d, d.d, perm, d.d_ff, d.d, offsets, 0, 0, d.n, dw1);
-    wseg(db, d.d_ff, d.d_ff, nullptr, u, d.d, d.d, perm, d.d_ff, d.d, offsets, 0, 0, d.n, dw3);
-    wseg(dh, d.d, d.d, perm, gh, d.d_ff, d.d_ff, nullptr, d.d, d.d_ff, offsets, 0, 0, d.n, dw2);
+    wseg(g[c++], da, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw1, nullptr, d.d);
+    wseg(g[c++], db, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw3, nullptr, d.d);
+    wseg(g[c++], dhp, d.d, gh, nullptr, d.d_ff, d.d, d.d_ff, offsets, 0, 0, d.n, dw2, nullptr,
+         d.d_ff);
     if (shared) {
-      wseg(das, fs, fs, nullptr, u, d.d, d.d, nullptr, fs, d.d, nullptr, (int)d.T, (int)d.T, 1,
-           dws1);
-      wseg(dbs, fs, fs, nullptr, u, d.d, d.d, nullptr, fs, d.d, nullptr, (int)d.T, (int)d.T, 1,
-           dws3);
-      wseg(dh, d.d, d.d, nullptr, ghs, fs, fs, nullptr, d.d, fs, nullptr, (int)d.T, (int)d.T, 1,
-           dws2);
+      wseg(g[c++], das, fs, u, nullptr, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws1,
+           nullptr, d.d);
+      wseg(g[c++], dbs, fs, u, nullptr, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws3,
+           nullptr, d.d);
+      wseg(g[c++], dh, d.d, ghs, nullptr, fs, d.d, fs, nullptr, (int)d.T, (int)d.T, 1, dws2,
+           nullptr, fs);
     }
-    // dE = dl^T u over token chunks
-    wseg(dl, L.ldl, L.ldl, nullptr, u, d.d, d.d, nullptr, d.n, d.d, nullptr, L.kchunk, (int)d.T,
-         L.G, slabs);
+    // dE = dl^T u over token chunks: M = n, N = d
+    wseg(g[c++], dl, L.ldl, u, nullptr, d.d, d.n, d.d, nullptr, L.kchunk, (int)d.T, L.G, slabs,
+         nullptr, d.d);
     MOE_TRY(moe::launch_bg(moe::BG_WGRAD, g, c, s));
   }
   MOE_TRY(mark());

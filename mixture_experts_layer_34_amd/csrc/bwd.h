@@ -45,6 +45,7 @@ struct BgSeg {
   int kchunk;
   int G;
   void* C;
+  void* C2;  // second output of a dual product (its accumulators against B2)
   int64_t ldc;
   int64_t c_gstride;
   // SwiGLU-backward epilogue (rows grouping, dual product): q, da, db, gh
@@ -73,14 +74,19 @@ enum BgKind {
   BG_PROJ = 1,    // rows, K-strided B, bf16 out (q = dh W2, dx = da W1 + db W3)
   BG_SWIGLU = 2,  // rows, K-contiguous dual B, SwiGLU-backward epilogue
   BG_DU = 3,      // rows, K-strided B, du epilogue
-  BG_WGRAD = 4    // k grouping, both operands K-strided, fp32 out
+  BG_WGRAD = 4,   // k grouping, both operands K-strided, fp32 out
+  BG_WGRAD2 = 5   // k grouping, K-strided, dual B, fp32 out stored transposed
+                  // (C[n][m], C2[n][m])
 };
 
 hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s);
 
-// gperm[slot_of[t][j]] = topk_gate[t][j]
-hipError_t launch_perm_gates(const int32_t* slot_of, const float* topk_gate, int64_t R,
-                             float* gperm, hipStream_t s);
+// Rows of u and dh in grouped order and the gate of each grouped row:
+// xp[slot_of[t][j]] = u[t], dhp[slot_of[t][j]] = dh[t],
+// gperm[slot_of[t][j]] = topk_gate[t][j]  (bf16 rows of d elements)
+hipError_t launch_gather_rows(const int32_t* slot_of, const float* topk_gate, const void* u,
+                              const void* dh, int64_t T, int k, int d, void* xp, void* dhp,
+                              float* gperm, hipStream_t s);
 
 // Per token: softmax of the logits lg [T][ldl] (fp32), the gate gradients
 // sum_p dgp[slot][p], the balance term alpha f_i / T, and the softmax

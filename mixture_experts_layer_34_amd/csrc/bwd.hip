@@ -16,11 +16,12 @@ namespace moe {
 namespace {
 
 constexpr int BM = kBgTile, BN = kBgTile, BK = kBgK;
-constexpr int LDK = BK + 8;               // LDS row pitch (elements)
-constexpr int TILE_EL = BM * LDK + 32 * (BM / 16);  // one staged operand tile (see rb)
+constexpr int LDK = BK + 8;  // LDS row pitch (elements)
+constexpr int BAND = 32;     // extra elements before every band of 16 rows
+constexpr int TILE_EL = BM * LDK + BAND * (BM / 16);  // one staged operand tile (see rb)
 constexpr int NT = 256;
 
-enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3 };
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3, EPI_F32T = 4 };
 
 // LDS position of tile row m (elements).  With 36-word rows, the MFMA
 // fragment reads (16 lanes on 16 consecutive rows, 16 bytes each) fall on
@@ -28,7 +29,7 @@ enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3 };
 // modulo the 64 banks) also spread the transposing store of a K-strided
 // operand, where the 32 lanes of a half-wave write 8-byte pieces of 4 rows
 // 8 apart in each of 8 K groups.
-__device__ __forceinline__ int rb(int m) { return m * LDK + 32 * (m >> 4); }
+__device__ __forceinline__ int rb(int m) { return m * LDK + BAND * (m >> 4); }
 
 struct BgArgs {
   BgSeg seg[kBgMaxSeg];
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
     kc_init(br, tid, g.N - n0, nullptr, n0, g.ldb);
     if constexpr (DUAL) br2 = br;
   }
+  (void)br2;
 
   f32x16 acc[2][2], acc2[DUAL ? 2 : 1][DUAL ? 2 : 1];
 #pragma unroll
@@ -218,7 +220,10 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   }
 
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
-  int buf = 0;
+  // K slices kt+1 .. kt+PF wait in registers (PF sets, filled in turn)
+  // while slice kt is multiplied out of LDS; the dual product has no room
+  // for a second set.
+  constexpr int PF = DUAL ? 1 : 2;
   for (int p = 0; p < g.npass && nk > 0; ++p) {
     const void* Ab = g.A[p];
     const void* Bb = KGRP ? g.B[p]
@@ -226,48 +231,48 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
                                                      (int64_t)e * g.b_gstride);
     const void* B2b = nullptr;
     if constexpr (DUAL)
-      B2b = static_cast<const void*>(static_cast<const uint16_t*>(g.B2) + (int64_t)e * g.b_gstride);
+      B2b = KGRP ? g.B2
+                 : static_cast<const void*>(static_cast<const uint16_t*>(g.B2) +
+                                            (int64_t)e * g.b_gstride);
     const int bklim = KGRP ? ke : g.bk_lim;
 
-    u32x4 ra[4], rbv[4], rb2[DUAL ? 4 : 1];
-    auto load = [&](int kt) {
+    u32x4 ra[PF][4], rbv[PF][4], rb2[PF][DUAL ? 4 : 1];
+    auto load = [&](int kt, int st) {
       const int k0 = kb + kt * BK;
       if constexpr (AKS)
-        ks_load(ra, Ab, g.lda, g.a_map, k0, ke, m0, g.a_lim, tid);
+        ks_load(ra[st], Ab, g.lda, g.a_map, k0, ke, m0, g.a_lim, tid);
       else
-        kc_load(ra, Ab, ar, k0, ke, tid);
+        kc_load(ra[st], Ab, ar, k0, ke, tid);
       if constexpr (BKS) {
-        ks_load(rbv, Bb, g.ldb, KGRP ? g.b_map : nullptr, k0, bklim, n0, g.b_lim, tid);
+        ks_load(rbv[st], Bb, g.ldb, KGRP ? g.b_map : nullptr, k0, bklim, n0, g.b_lim, tid);
+        if constexpr (DUAL)
+          ks_load(rb2[st], B2b, g.ldb, KGRP ? g.b_map : nullptr, k0, bklim, n0, g.b_lim, tid);
       } else {
-        kc_load(rbv, Bb, br, k0, ke, tid);
-        if constexpr (DUAL) kc_load(rb2, B2b, br2, k0, ke, tid);
+        kc_load(rbv[st], Bb, br, k0, ke, tid);
+        if constexpr (DUAL) kc_load(rb2[st], B2b, br2, k0, ke, tid);
       }
     };
-    auto store = [&](int b) {
+    auto store = [&](int st, int b) {
       if constexpr (AKS)
-        ks_store(sA[b], ra, tid);
+        ks_store(sA[b], ra[st], tid);
       else
-        kc_store(sA[b], ra, tid);
+        kc_store(sA[b], ra[st], tid);
       if constexpr (BKS) {
-        ks_store(sB[b], rbv, tid);
+        ks_store(sB[b], rbv[st], tid);
+        if constexpr (DUAL) ks_store(sB2[b], rb2[st], tid);
       } else {
-        kc_store(sB[b], rbv, tid);
-        if constexpr (DUAL) kc_store(sB2[b], rb2, tid);
+        kc_store(sB[b], rbv[st], tid);
+        if constexpr (DUAL) kc_store(sB2[b], rb2[st], tid);
       }
     };
-
-    load(0);
-    store(buf);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load(kt + 1);
+    auto compute = [&](int b) {
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         bf16x8 af[2], bfr[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][fa[i] + kk * 16]);
-          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][fb[i] + kk * 16]);
+          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] + kk * 16]);
+          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] + kk * 16]);
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
           bf16x8 b2[2];
 #pragma unroll
           for (int i = 0; i < 2; ++i)
-            b2[i] = *reinterpret_cast<const bf16x8*>(&sB2[buf][fb[i] + kk * 16]);
+            b2[i] = *reinterpret_cast<const bf16x8*>(&sB2[b][fb[i] + kk * 16]);
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -288,9 +293,27 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(b2[nb], af[mb], acc2[nb][mb], 0, 0, 0);
         }
       }
-      if (kt + 1 < nk) store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
+    };
+
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (j < nk) load(j, j);
+    store(0, 0);
+    __syncthreads();
+    // Unrolled by PF so register sets and LDS buffers are static: slice
+    // kt = base + j sits in set j and LDS buffer kt & 1 (PF is 1 or 2).
+    for (int base = 0; base < nk; base += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int kt = base + j;
+        if (kt < nk) {
+          const int b = PF == 2 ? j : (kt & 1);
+          if (kt + PF < nk) load(kt + PF, j);
+          compute(b);
+          if (kt + 1 < nk) store((j + 1) % PF, b ^ 1);
+          __syncthreads();
+        }
+      }
     }
   }
 
@@ -318,6 +341,30 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
           } else {
             *reinterpret_cast<uint2*>(C + (row * g.ldc + c) * 2) =
                 pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          }
+        }
+    }
+  } else if constexpr (EPI == EPI_F32T) {
+    // C[n][m] (and C2[n][m] from the dual accumulators): lanes hold 32
+    // consecutive m of one n, so each store instruction writes 128 bytes.
+    const int mlim = KGRP ? g.M - m0 : mvalid;
+    float* C = static_cast<float*>(g.C) + (KGRP ? (int64_t)e * g.c_gstride : 0);
+    float* C2 = DUAL ? static_cast<float*>(g.C2) + (KGRP ? (int64_t)e * g.c_gstride : 0) : nullptr;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int ml = wm * 64 + mb * 32 + (lane & 31);
+      if (ml >= mlim) continue;
+      const int64_t m = (int64_t)m0 + ml;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cbase + nb * 32 + 8 * q;
+          if (c >= g.N) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            C[(int64_t)(c + j) * g.ldc + m] = acc[nb][mb][4 * q + j];
+            if constexpr (DUAL) C2[(int64_t)(c + j) * g.ldc + m] = acc2[nb][mb][4 * q + j];
           }
         }
     }
@@ -406,11 +453,23 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   }
 }
 
-__global__ void perm_gates_kernel(const int32_t* __restrict__ slot_of,
-                                  const float* __restrict__ gate, int64_t R,
-                                  float* __restrict__ gperm) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < R) gperm[slot_of[i]] = gate[i];
+// One wave per token: its u and dh rows go to each of its grouped rows.
+__global__ __launch_bounds__(256) void gather_rows_kernel(
+    const int32_t* __restrict__ slot_of, const float* __restrict__ gate,
+    const u32x4* __restrict__ u, const u32x4* __restrict__ dh, int64_t T, int k, int nch,
+    u32x4* __restrict__ xp, u32x4* __restrict__ dhp, float* __restrict__ gperm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  for (int j = lane; j < k; j += 64) gperm[slot_of[t * k + j]] = gate[t * k + j];
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 a = u[t * nch + c], b = dh[t * nch + c];
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = slot_of[t * k + j];
+      xp[r * nch + c] = a;
+      dhp[r * nch + c] = b;
+    }
+  }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -505,7 +564,7 @@ __global__ void slab_sum_kernel(const float4* __restrict__ slabs, int G, int64_t
 
 int seg_blocks(BgKind kind, const BgSeg& g) {
   const int nN = (g.N + BN - 1) / BN;
-  if (kind == BG_WGRAD) return g.G * ((g.M + BM - 1) / BM) * nN;
+  if (kind == BG_WGRAD || kind == BG_WGRAD2) return g.G * ((g.M + BM - 1) / BM) * nN;
   if (g.t_off) return g.max_tiles * nN;
   return (int)((g.rows + BM - 1) / BM) * nN;
 }
@@ -536,15 +595,18 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
     case BG_SWIGLU: return launch_t<false, false, false, EPI_SWIGLU, true>(args, grid, s);
     case BG_DU: return launch_t<false, false, true, EPI_DU, false>(args, grid, s);
     case BG_WGRAD: return launch_t<true, true, true, EPI_F32, false>(args, grid, s);
+    case BG_WGRAD2: return launch_t<true, true, true, EPI_F32T, true>(args, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_perm_gates(const int32_t* slot_of, const float* topk_gate, int64_t R,
-                             float* gperm, hipStream_t s) {
-  const int64_t blocks = (R + 255) / 256;
-  hipLaunchKernelGGL(perm_gates_kernel, dim3((unsigned)blocks), dim3(256), 0, s, slot_of,
-                     topk_gate, R, gperm);
+hipError_t launch_gather_rows(const int32_t* slot_of, const float* topk_gate, const void* u,
+                              const void* dh, int64_t T, int k, int d, void* xp, void* dhp,
+                              float* gperm, hipStream_t s) {
+  const int64_t blocks = (T + 3) / 4;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, slot_of,
+                     topk_gate, static_cast<const u32x4*>(u), static_cast<const u32x4*>(dh), T,
+                     k, d / 8, static_cast<u32x4*>(xp), static_cast<u32x4*>(dhp), gperm);
   return hipGetLastError();
 }
 

@@ -280,5 +280,5 @@ def test_layer_bwd_checks():
 
 def test_layer_bwd_kernel_sequence():
     assert moe.moe_layer_bwd_kernels(p16()) == [
-        "hist", "scan", "scatter", "gates", "logits", "q", "ab_swiglu", "dx", "softmax_bwd",
+        "hist", "scan", "scatter", "gather", "logits", "q", "ab_swiglu", "dx", "softmax_bwd",
         "du", "wgrad", "dcent_sum"]
