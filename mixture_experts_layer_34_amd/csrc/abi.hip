@@ -810,11 +810,8 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   {
     moe::BgSeg g[7] = {};
     int c = 0;
-    // dW1 = da^T x, dW3 = db^T x, dW2 = (g dh)^T hid per expert
-    wseg(g[c++], da, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw1, nullptr, d.d);
-    wseg(g[c++], db, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw3, nullptr, d.d);
-    wseg(g[c++], dhp, d.d, gh, nullptr, d.d_ff, d.d, d.d_ff, offsets, 0, 0, d.n, dw2, nullptr,
-         d.d_ff);
+    // The shared experts' tiles reduce over all T tokens (the routed ones
+    // over one expert's rows): dealt first, so they do not end the launch.
     if (shared) {
       wseg(g[c++], das, fs, u, nullptr, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws1,
            nullptr, d.d);
@@ -823,10 +820,15 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
       wseg(g[c++], dh, d.d, ghs, nullptr, fs, d.d, fs, nullptr, (int)d.T, (int)d.T, 1, dws2,
            nullptr, fs);
     }
+    // dW1 = da^T x, dW3 = db^T x, dW2 = (g dh)^T hid per expert
+    wseg(g[c++], da, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw1, nullptr, d.d);
+    wseg(g[c++], db, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw3, nullptr, d.d);
+    wseg(g[c++], dhp, d.d, gh, nullptr, d.d_ff, d.d, d.d_ff, offsets, 0, 0, d.n, dw2, nullptr,
+         d.d_ff);
     // dE = dl^T u over token chunks: M = n, N = d
     wseg(g[c++], dl, L.ldl, u, nullptr, d.d, d.n, d.d, nullptr, L.kchunk, (int)d.T, L.G, slabs,
          nullptr, d.d);
-    MOE_TRY(moe::launch_bg(moe::BG_WGRAD, g, c, s));
+    MOE_TRY(moe::launch_bg(moe::BG_WGRAD_BIG, g, c, s));
   }
   MOE_TRY(mark());
   MOE_TRY(moe::launch_slab_sum(slabs, L.G, (int64_t)d.n * d.d, dcentroids, s));

@@ -15,8 +15,8 @@ namespace moe {
 //           its own M x N output at C + g * c_gstride (weight gradients,
 //           partial sums over token chunks).
 // Operands live in memory either K-contiguous (element (i, k) at
-// p[map(i) * ld + k]) or K-strided (element (i, k) at p[map(k) * ld + i]);
-// map is the optional row map (null: identity).  Pass p (npass = 1 or 2)
+// p[i * ld + k]) or K-strided (element (i, k) at p[k * ld + i]); rows taken
+// in another order are gathered beforehand.  Pass p (npass = 1 or 2)
 // uses A[p] and B[p]; a second pass adds A[1] B[1] into the same
 // accumulators (dx = da W1 + db W3).
 struct BgSeg {
@@ -25,9 +25,6 @@ struct BgSeg {
   const void* B[2];
   int64_t ldb;
   const void* B2;        // second B of the dual product (a and b of the SwiGLU)
-  const int32_t* a_map;  // rows grouping: memory row of each grouped row of A;
-                         // k grouping: memory row of each K index of A
-  const int32_t* b_map;  // k grouping: memory row of each K index of B
   int64_t b_gstride;     // rows grouping: elements between groups' B
   int npass;
   int M, N, K;           // k grouping: output M x N per group; rows: N, K
@@ -75,8 +72,9 @@ enum BgKind {
   BG_SWIGLU = 2,  // rows, K-contiguous dual B, SwiGLU-backward epilogue
   BG_DU = 3,      // rows, K-strided B, du epilogue
   BG_WGRAD = 4,   // k grouping, both operands K-strided, fp32 out
-  BG_WGRAD2 = 5   // k grouping, K-strided, dual B, fp32 out stored transposed
+  BG_WGRAD2 = 5,  // k grouping, K-strided, dual B, fp32 out stored transposed
                   // (C[n][m], C2[n][m])
+  BG_WGRAD_BIG = 6  // as BG_WGRAD on 256 x 256 tiles
 };
 
 hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s);

@@ -44,15 +44,15 @@ struct KcRows {
   uint32_t ok;      // bit i: row i exists
 };
 
-__device__ __forceinline__ void kc_init(KcRows& R, int tid, int nvalid, const int32_t* map,
-                                        int64_t row0, int64_t ld) {
+__device__ __forceinline__ void kc_init(KcRows& R, int tid, int nvalid, int64_t row0,
+                                        int64_t ld) {
   R.ok = 0;
   const int kc = (tid & 7) * 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + 32 * i;
     const bool v = r < nvalid;
-    const int64_t mr = v ? (map ? (int64_t)map[row0 + r] : row0 + r) : 0;
+    const int64_t mr = v ? row0 + r : 0;
     R.off[i] = (uint32_t)((mr * ld + kc) * 2);
     R.ok |= (v ? 1u : 0u) << i;
   }
@@ -81,34 +81,34 @@ __device__ __forceinline__ void kc_store(uint16_t* s, const u32x4 v[4], int tid)
 
 // ---- K-strided operand: 64 k rows x 128 columns of the tile.  Thread:
 // columns mb*8 .. +7 with mb = 4 wave + (lane & 3), k rows kg*4 .. +3 with
-// kg = lane >> 2 (four lanes read 64 contiguous bytes of a row).
-__device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld,
-                                        const int32_t* map, int kbase, int klim, int col0,
-                                        int clim, int tid) {
+// kg = lane >> 2 (four lanes read 64 contiguous bytes of a row).  Rows are
+// addressed directly: a row map would put a dependent load in front of every
+// load, and the in-order load counter would then wait for all loads in flight.
+__device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld, int kbase,
+                                        int klim, int col0, int clim, int tid) {
   const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
   const int col = col0 + mb * 8;
   const bool cin = col < clim;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int kr = kbase + kg * 4 + kk;
-    if (cin && kr < klim) {
-      const int64_t mr = map ? (int64_t)map[kr] : (int64_t)kr;
-      v[kk] = ld_off<u32x4>(base, (uint32_t)((mr * ld + col) * 2));
-    } else {
+    if (cin && kr < klim)
+      v[kk] = ld_off<u32x4>(base, (uint32_t)(((int64_t)kr * ld + col) * 2));
+    else
       v[kk] = u32x4{0u, 0u, 0u, 0u};
-    }
   }
 }
 
-// Transposes the thread's 4 (k) x 8 (columns) block into LDS rows = columns.
-__device__ __forceinline__ void ks_store(uint16_t* s, const u32x4 v[4], int tid) {
+// Transposes the thread's 4 (k) x 8 (columns) block into LDS rows = columns
+// (rows roff + 0 .. 127 of the staged tile).
+__device__ __forceinline__ void ks_store(uint16_t* s, const u32x4 v[4], int tid, int roff = 0) {
   const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int w = i >> 1, sh = (i & 1) * 16;
     const uint32_t lo = ((v[0][w] >> sh) & 0xFFFFu) | (((v[1][w] >> sh) & 0xFFFFu) << 16);
     const uint32_t hi = ((v[2][w] >> sh) & 0xFFFFu) | (((v[3][w] >> sh) & 0xFFFFu) << 16);
-    *reinterpret_cast<uint2*>(&s[rb(mb * 8 + i) + kg * 4]) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(&s[rb(roff + mb * 8 + i) + kg * 4]) = make_uint2(lo, hi);
   }
 }
 
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 
   // Row maps of the K-contiguous operands (fixed across K slices).
   KcRows ar{}, br{}, br2{};
-  if constexpr (!AKS) kc_init(ar, tid, mvalid, g.a_map, m0, g.lda);
+  if constexpr (!AKS) kc_init(ar, tid, mvalid, m0, g.lda);
   if constexpr (!BKS) {
-    kc_init(br, tid, g.N - n0, nullptr, n0, g.ldb);
+    kc_init(br, tid, g.N - n0, n0, g.ldb);
     if constexpr (DUAL) br2 = br;
   }
   (void)br2;
@@ -240,13 +240,12 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
     auto load = [&](int kt, int st) {
       const int k0 = kb + kt * BK;
       if constexpr (AKS)
-        ks_load(ra[st], Ab, g.lda, g.a_map, k0, ke, m0, g.a_lim, tid);
+        ks_load(ra[st], Ab, g.lda, k0, ke, m0, g.a_lim, tid);
       else
         kc_load(ra[st], Ab, ar, k0, ke, tid);
       if constexpr (BKS) {
-        ks_load(rbv[st], Bb, g.ldb, KGRP ? g.b_map : nullptr, k0, bklim, n0, g.b_lim, tid);
-        if constexpr (DUAL)
-          ks_load(rb2[st], B2b, g.ldb, KGRP ? g.b_map : nullptr, k0, bklim, n0, g.b_lim, tid);
+        ks_load(rbv[st], Bb, g.ldb, k0, bklim, n0, g.b_lim, tid);
+        if constexpr (DUAL) ks_load(rb2[st], B2b, g.ldb, k0, bklim, n0, g.b_lim, tid);
       } else {
         kc_load(rbv[st], Bb, br, k0, ke, tid);
         if constexpr (DUAL) kc_load(rb2[st], B2b, br2, k0, ke, tid);
@@ -453,6 +452,130 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   }
 }
 
+// Weight gradients (k grouping, both operands K-strided, fp32 out) on
+// 256 x 256 tiles: an expert's K range is only its rows (a few hundred), so
+// a tile reuses each staged slice over four times the output of the
+// 128 x 128 kernel, and each wave's 128 x 128 block (16 accumulator blocks,
+// held in AGPRs) takes two MFMAs per fragment read from LDS.  One workgroup
+// per CU (two LDS buffers of two 256-row tiles).
+constexpr int WB = 256;
+constexpr int WTILE_EL = WB * LDK + BAND * (WB / 16);
+
+__global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][WTILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][WTILE_EL];
+
+  const int bid = (int)blockIdx.x;
+  int si = 0;
+  while (si + 1 < args.nseg && bid >= args.start[si + 1]) ++si;
+  const BgSeg& g = args.seg[si];
+  const int L = bid - args.start[si];
+  const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
+  const int e = L / (nM * nN);
+  const int r = L - e * nM * nN;
+  const int nt = r / nM, mt = r - nt * nM;
+  const int m0 = mt * WB, n0 = nt * WB;
+  int kb, ke;
+  if (g.koff) {
+    kb = g.koff[e];
+    ke = g.koff[e + 1];
+  } else {
+    kb = e * g.kchunk;
+    ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[nb][mb][j] = 0.0f;
+  int fa[4], fb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = rb(wm * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+    fb[i] = rb(wn * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+  }
+
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  u32x4 ra[2][4], rbv[2][4];
+  auto load = [&](int kt) {
+    const int k0 = kb + kt * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ks_load(ra[h], g.A[0], g.lda, k0, ke, m0 + 128 * h, g.a_lim, tid);
+      ks_load(rbv[h], g.B[0], g.ldb, k0, ke, n0 + 128 * h, g.b_lim, tid);
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ks_store(sA[b], ra[h], tid, 128 * h);
+      ks_store(sB[b], rbv[h], tid, 128 * h);
+    }
+  };
+  if (nk > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int b = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] + kk * 16]);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] + kk * 16]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(b ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue through LDS, 32 rows of the wave's block at a time: the
+  // accumulator layout puts one row per lane, so direct stores would send
+  // 32-byte pieces of 32 rows per instruction; staged, each store
+  // instruction writes two whole 512-byte rows.
+  constexpr int SP = 128 + 4;  // staging row pitch (floats)
+  float* stage = reinterpret_cast<float*>(&sA[0][0]) + wave * 32 * SP;
+  float* C = static_cast<float*>(g.C) + (int64_t)e * g.c_gstride;
+  const int mrow0 = m0 + wm * 128, ncol0 = n0 + wn * 128;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& a = acc[nb][mb];
+        *reinterpret_cast<float4*>(&stage[(lane & 31) * SP + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
+            make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+      }
+    __syncthreads();
+    const int c = ncol0 + 4 * (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + (lane >> 5);
+      const int m = mrow0 + mb * 32 + row;
+      if (m < g.M && c < g.N)
+        *reinterpret_cast<float4*>(&C[(int64_t)m * g.ldc + c]) =
+            *reinterpret_cast<const float4*>(&stage[row * SP + 4 * (lane & 31)]);
+    }
+    __syncthreads();
+  }
+}
+
 // One wave per token: its u and dh rows go to each of its grouped rows.
 __global__ __launch_bounds__(256) void gather_rows_kernel(
     const int32_t* __restrict__ slot_of, const float* __restrict__ gate,
@@ -565,6 +688,7 @@ __global__ void slab_sum_kernel(const float4* __restrict__ slabs, int G, int64_t
 int seg_blocks(BgKind kind, const BgSeg& g) {
   const int nN = (g.N + BN - 1) / BN;
   if (kind == BG_WGRAD || kind == BG_WGRAD2) return g.G * ((g.M + BM - 1) / BM) * nN;
+  if (kind == BG_WGRAD_BIG) return g.G * ((g.M + WB - 1) / WB) * ((g.N + WB - 1) / WB);
   if (g.t_off) return g.max_tiles * nN;
   return (int)((g.rows + BM - 1) / BM) * nN;
 }
@@ -596,6 +720,9 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
     case BG_DU: return launch_t<false, false, true, EPI_DU, false>(args, grid, s);
     case BG_WGRAD: return launch_t<true, true, true, EPI_F32, false>(args, grid, s);
     case BG_WGRAD2: return launch_t<true, true, true, EPI_F32T, true>(args, grid, s);
+    case BG_WGRAD_BIG:
+      hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(NT), 0, s, args);
+      return hipGetLastError();
   }
   return hipErrorInvalidValue;
 }
