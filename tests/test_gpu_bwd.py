@@ -4,8 +4,9 @@ The oracle's gradients are pinned by finite differences of an independent
 forward (test_oracle_bwd_pins.py).  Its routing inputs (topk_idx, f) come
 from the oracle's own forward, and the GPU receives the same routing, so
 both sides differentiate the same function.  Small workloads compare every
-gradient in full; the 16B-shaped workload compares du on sampled tokens and
-the weight gradients of sampled experts.
+gradient in full; the 16B- and 2B-shaped workloads compare du on sampled
+tokens and the weight gradients of sampled experts.  A HIP-graph capture of
+the backward replays to the eager bits.
 """
 import numpy as np
 import pytest
@@ -160,3 +161,74 @@ def test_bwd_16b_sampled():
     check_all(got, want, ["du", "dw1", "dw3", "dw2"])
     for kk in ("dcent", "dws1", "dws3", "dws2"):
         assert np.isfinite(got[kk]).all(), kk
+
+
+def test_bwd_2b_sampled():
+    """The 2B-shaped layer (T = 8192, d = 1280, 63 routed experts + 1 shared,
+    top-7, alpha = 0.01): d and d_ff = 896 are ragged against the 256-wide
+    weight-gradient tiles.  du on sampled tokens, weight gradients of the
+    most and the least loaded expert."""
+    name = "2b"
+    cfg = ALL[name]
+    inp = inputs(name)
+    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    dh = moe_synth.make_upstream_grad(cfg, seed=1)
+    dh32 = (dh.astype(np.uint32) << 16).view(np.float32)
+    alpha = moe_synth.BALANCE_ALPHA["2b"]
+    toks = sample_tokens(cfg.T, 16)
+    cnt = np.bincount(r["topk_idx"].ravel(), minlength=cfg.n)
+    experts = np.array([int(cnt.argmax()), int(np.where(cnt > 0, cnt, cnt.max() + 1).argmin())])
+    want = oracle.layer_bwd(inp, cfg.N, cfg.m, cfg.K, cfg.K_s, r["topk_idx"], r["f"], dh32, alpha,
+                            toks=toks, want_dcent=False, experts=experts, want_shared=False)
+    got = run_bwd(cfg, inp, r, dh, alpha)
+    got["du"] = got["du"][toks]
+    for kk in ("dw1", "dw3", "dw2"):
+        got[kk] = got[kk][experts]
+    check_all(got, want, ["du", "dw1", "dw3", "dw2"])
+
+
+def test_bwd_graph_replays():
+    """moe_layer_bwd captured as a HIP graph gives the eager bits on every
+    replay, with an eager call on the same workspace between replays and junk
+    written to the outputs before each."""
+    name = "ragged_bf16"
+    cfg = ALL[name]
+    inp = inputs(name)
+    d = dev()
+    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    dh = moe_synth.make_upstream_grad(cfg, seed=1)
+    want = run_bwd(cfg, inp, r, dh, 0.37)
+    p = prob(cfg)
+    t = {k: to_device(inp[k], d) for k in ("u", "centroids", "w1", "w3", "w2", "ws1", "ws3", "ws2")}
+    idx = torch.from_numpy(r["topk_idx"]).to(d)
+    gate = torch.from_numpy(r["topk_gate"]).to(d)
+    f = torch.from_numpy(r["f"]).to(d)
+    dht = to_device(dh, d)
+    out = {k: torch.empty(v.shape, dtype=torch.float32, device=d) for k, v in want.items()}
+    ws = torch.empty(moe.moe_bwd_workspace_bytes(p), dtype=torch.uint8, device=d)
+    call = lambda: moe.moe_layer_bwd(p, t["u"], t["centroids"], t["w1"], t["w3"], t["w2"],
+                                     t["ws1"], t["ws3"], t["ws2"], idx, gate, f, dht, 0.37,
+                                     out["du"], out["dcent"], out["dw1"], out["dw3"], out["dw2"],
+                                     out["dws1"], out["dws3"], out["dws2"], 0, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # first call outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i, eager_between in enumerate((False, True, False)):
+        for v in out.values():
+            v.fill_(-3.0)
+        if eager_between:
+            call()
+            torch.cuda.synchronize()
+            for v in out.values():
+                v.fill_(-3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in want:
+            got = out[k].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), want[k].view(np.uint32)), (i, k)
