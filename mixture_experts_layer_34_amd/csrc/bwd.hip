@@ -33,9 +33,34 @@ __device__ __forceinline__ int rb(int m) { return m * LDK + BAND * (m >> 4); }
 
 struct BgArgs {
   BgSeg seg[kBgMaxSeg];
-  int start[kBgMaxSeg + 1];  // first workgroup of each segment
+  int bound[kBgMaxSeg];  // tiles of each segment (an upper bound for a tile list)
   int nseg;
 };
+
+// Workgroup -> (segment, logical tile).  Workgroups are dealt round-robin
+// over the 8 XCDs; each XCD takes an even share of every segment's tiles, in
+// segment order, as one contiguous range of logical tiles (grouped by expert,
+// then column tile), so the tiles that share activation rows and weight
+// tiles run on one XCD and meet in its L2.  Returns false for workgroups
+// beyond the live tiles.
+__device__ __forceinline__ bool xcd_pick(const BgArgs& a, int tile, int& si, int& L) {
+  constexpr int kXcd = 8;
+  const int bid = (int)blockIdx.x, x = bid % kXcd;
+  int i = bid / kXcd;
+  for (int s = 0; s < a.nseg; ++s) {
+    const BgSeg& g = a.seg[s];
+    const int G = g.t_off ? *g.t_count * ((g.N + tile - 1) / tile) : a.bound[s];
+    const int q = G / kXcd, r = G % kXcd;
+    const int share = q + (x < r ? 1 : 0);
+    if (i < share) {
+      si = s;
+      L = x * q + (x < r ? x : r) + i;
+      return true;
+    }
+    i -= share;
+  }
+  return false;
+}
 
 // ---- K-contiguous operand: the tile's 128 rows x 64 k.  Thread chunk
 // tid + 256 i covers row (tid >> 3) + 32 i and k (tid & 7) * 8 .. + 7.
@@ -132,18 +157,15 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][TILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t sB2[DUAL ? 2 : 1][DUAL ? TILE_EL : 8];
 
-  const int bid = (int)blockIdx.x;
-  int si = 0;
-  while (si + 1 < args.nseg && bid >= args.start[si + 1]) ++si;
+  int si = 0, L = 0;
+  if (!xcd_pick(args, BN, si, L)) return;
   const BgSeg& g = args.seg[si];
-  const int L = bid - args.start[si];
   const int nN = (g.N + BN - 1) / BN;
 
   int e = 0, nt, m0, mvalid, kb, ke;
   if constexpr (!KGRP) {
     int mt;
     if (g.t_off) {
-      if (L >= *g.t_count * nN) return;
       int lo = 0, hi = g.n_groups;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -465,11 +487,9 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][WTILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][WTILE_EL];
 
-  const int bid = (int)blockIdx.x;
-  int si = 0;
-  while (si + 1 < args.nseg && bid >= args.start[si + 1]) ++si;
+  int si = 0, L = 0;
+  if (!xcd_pick(args, WB, si, L)) return;
   const BgSeg& g = args.seg[si];
-  const int L = bid - args.start[si];
   const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
   const int e = L / (nM * nN);
   const int r = L - e * nM * nN;
@@ -705,13 +725,12 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
   if (nseg < 1 || nseg > kBgMaxSeg) return hipErrorInvalidValue;
   BgArgs args{};
   args.nseg = nseg;
-  args.start[0] = 0;
+  int grid = 0;
   for (int i = 0; i < nseg; ++i) {
     args.seg[i] = segs[i];
-    args.start[i + 1] = args.start[i] + seg_blocks(kind, segs[i]);
+    args.bound[i] = seg_blocks(kind, segs[i]);
+    grid += 8 * ((args.bound[i] + 7) / 8);  // each XCD's share of segment i
   }
-  for (int i = nseg + 1; i <= kBgMaxSeg; ++i) args.start[i] = args.start[nseg];
-  const int grid = args.start[nseg];
   if (grid == 0) return hipSuccess;
   switch (kind) {
     case BG_LOGITS: return launch_t<false, false, false, EPI_F32, false>(args, grid, s);
