@@ -785,14 +785,12 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   // Weight gradients (one output per expert, reduced over its rows) and the
   // centroid gradient's per-chunk partial sums, in one launch.
   float* slabs = at<float>(ws, L.slabs);
-  auto wseg = [&](moe::BgSeg& x, const void* A, int64_t lda, const void* B, const void* B2,
-                  int64_t ldb, int M, int N, const int32_t* koff, int kchunk, int K, int G,
-                  float* C, float* C2, int64_t ldc) {
+  auto wseg = [&](moe::BgSeg& x, const void* A, int64_t lda, const void* B, int64_t ldb, int M,
+                  int N, const int32_t* koff, int kchunk, int K, int G, float* C, int64_t ldc) {
     x.A[0] = A;
     x.lda = lda;
     x.a_lim = (int)lda;
     x.B[0] = B;
-    x.B2 = B2;
     x.ldb = ldb;
     x.b_lim = (int)ldb;
     x.npass = 1;
@@ -803,7 +801,6 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     x.K = K;
     x.G = G;
     x.C = C;
-    x.C2 = C2;
     x.ldc = ldc;
     x.c_gstride = (int64_t)M * N;
   };
@@ -813,22 +810,17 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     // The shared experts' tiles reduce over all T tokens (the routed ones
     // over one expert's rows): dealt first, so they do not end the launch.
     if (shared) {
-      wseg(g[c++], das, fs, u, nullptr, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws1,
-           nullptr, d.d);
-      wseg(g[c++], dbs, fs, u, nullptr, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws3,
-           nullptr, d.d);
-      wseg(g[c++], dh, d.d, ghs, nullptr, fs, d.d, fs, nullptr, (int)d.T, (int)d.T, 1, dws2,
-           nullptr, fs);
+      wseg(g[c++], das, fs, u, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws1, d.d);
+      wseg(g[c++], dbs, fs, u, d.d, fs, d.d, nullptr, (int)d.T, (int)d.T, 1, dws3, d.d);
+      wseg(g[c++], dh, d.d, ghs, fs, d.d, fs, nullptr, (int)d.T, (int)d.T, 1, dws2, fs);
     }
     // dW1 = da^T x, dW3 = db^T x, dW2 = (g dh)^T hid per expert
-    wseg(g[c++], da, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw1, nullptr, d.d);
-    wseg(g[c++], db, d.d_ff, xp, nullptr, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw3, nullptr, d.d);
-    wseg(g[c++], dhp, d.d, gh, nullptr, d.d_ff, d.d, d.d_ff, offsets, 0, 0, d.n, dw2, nullptr,
-         d.d_ff);
+    wseg(g[c++], da, d.d_ff, xp, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw1, d.d);
+    wseg(g[c++], db, d.d_ff, xp, d.d, d.d_ff, d.d, offsets, 0, 0, d.n, dw3, d.d);
+    wseg(g[c++], dhp, d.d, gh, d.d_ff, d.d, d.d_ff, offsets, 0, 0, d.n, dw2, d.d_ff);
     // dE = dl^T u over token chunks: M = n, N = d
-    wseg(g[c++], dl, L.ldl, u, nullptr, d.d, d.n, d.d, nullptr, L.kchunk, (int)d.T, L.G, slabs,
-         nullptr, d.d);
-    MOE_TRY(moe::launch_bg(moe::BG_WGRAD_BIG, g, c, s));
+    wseg(g[c++], dl, L.ldl, u, d.d, d.n, d.d, nullptr, L.kchunk, (int)d.T, L.G, slabs, d.d);
+    MOE_TRY(moe::launch_bg(moe::BG_WGRAD, g, c, s));
   }
   MOE_TRY(mark());
   MOE_TRY(moe::launch_slab_sum(slabs, L.G, (int64_t)d.n * d.d, dcentroids, s));

@@ -42,7 +42,6 @@ struct BgSeg {
   int kchunk;
   int G;
   void* C;
-  void* C2;  // second output of a dual product (its accumulators against B2)
   int64_t ldc;
   int64_t c_gstride;
   // SwiGLU-backward epilogue (rows grouping, dual product): q, da, db, gh
@@ -63,7 +62,7 @@ struct BgSeg {
 };
 
 constexpr int kBgMaxSeg = 8;
-constexpr int kBgTile = 128;  // rows and columns of a tile
+constexpr int kBgTile = 128;  // rows and columns of a rows-grouping tile
 constexpr int kBgK = 64;      // K slice
 
 enum BgKind {
@@ -71,10 +70,7 @@ enum BgKind {
   BG_PROJ = 1,    // rows, K-strided B, bf16 out (q = dh W2, dx = da W1 + db W3)
   BG_SWIGLU = 2,  // rows, K-contiguous dual B, SwiGLU-backward epilogue
   BG_DU = 3,      // rows, K-strided B, du epilogue
-  BG_WGRAD = 4,   // k grouping, both operands K-strided, fp32 out
-  BG_WGRAD2 = 5,  // k grouping, K-strided, dual B, fp32 out stored transposed
-                  // (C[n][m], C2[n][m])
-  BG_WGRAD_BIG = 6  // as BG_WGRAD on 256 x 256 tiles
+  BG_WGRAD = 4    // k grouping, both operands K-strided, fp32 out, 256 x 256 tiles
 };
 
 hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s);

@@ -1,13 +1,15 @@
 // Backward pass of the MoE layer on gfx950.
 //
-// Every product of the backward (the chain rule of SwiGLU experts, the
+// The products of the backward (the chain rule of SwiGLU experts, the
 // gate-weighted combine, the softmax router and the expert-level balance
-// loss) goes through one MFMA kernel: 128 x 128 output tiles, 64-deep K
-// slices staged through LDS with the next slice's global loads in flight,
-// four waves of 64 x 64 each (2 x 2 blocks of 32x32x16 bf16 MFMAs, fp32
-// accumulators).  Operands that are K-strided in memory (weights read
-// against their stored orientation, activations reduced over tokens) are
-// transposed on their way into LDS; see rb() for the bank layout.
+// loss) go through two MFMA kernels.  bg_kernel: rows grouped by expert,
+// 128 x 128 output tiles, 64-deep K slices staged through LDS with the next
+// slices' global loads in flight, four waves of 64 x 64 each (2 x 2 blocks
+// of 32x32x16 bf16 MFMAs, fp32 accumulators).  wgrad_kernel: the weight
+// gradients, each expert reducing over its own rows, on 256 x 256 tiles.
+// Operands that are K-strided in memory (weights read against their stored
+// orientation, activations reduced over tokens) are transposed on their way
+// into LDS; see rb() for the bank layout.
 #include "bwd.h"
 #include "common.h"
 #include "kernels.h"
@@ -21,7 +23,7 @@ constexpr int BAND = 32;     // extra elements before every band of 16 rows
 constexpr int TILE_EL = BM * LDK + BAND * (BM / 16);  // one staged operand tile (see rb)
 constexpr int NT = 256;
 
-enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3, EPI_F32T = 4 };
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3 };
 
 // LDS position of tile row m (elements).  With 36-word rows, the MFMA
 // fragment reads (16 lanes on 16 consecutive rows, 16 bytes each) fall on
@@ -149,9 +151,10 @@ __device__ __forceinline__ void unpack4(uint2 p, float* o) {
   o[3] = bf16_to_f32((uint16_t)(p.y >> 16));
 }
 
-// KGRP: k grouping; AKS / BKS: A / B K-strided in memory; DUAL: second B
-// with its own accumulators (SwiGLU's a and b).
-template <bool KGRP, bool AKS, bool BKS, int EPI, bool DUAL>
+// Rows grouping (the tile list of the forward's grouping, or one group of
+// `rows` rows).  A is K-contiguous; BKS: B K-strided in memory; DUAL: second
+// B with its own accumulators (SwiGLU's a and b).
+template <bool BKS, int EPI, bool DUAL>
 __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][TILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][TILE_EL];
@@ -162,50 +165,31 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   const BgSeg& g = args.seg[si];
   const int nN = (g.N + BN - 1) / BN;
 
-  int e = 0, nt, m0, mvalid, kb, ke;
-  if constexpr (!KGRP) {
-    int mt;
-    if (g.t_off) {
-      int lo = 0, hi = g.n_groups;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (g.t_off[mid] * nN <= L)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      e = lo;
-      const int t0 = g.t_off[e], te = g.t_off[e + 1] - t0;
-      const int local = L - t0 * nN;
-      nt = local / te;
-      mt = t0 + (local - nt * te);
-      m0 = g.t_row0[mt];
-      mvalid = g.t_rows[mt];
-    } else {
-      const int num_m = (int)((g.rows + BM - 1) / BM);
-      nt = L / num_m;
-      mt = L - nt * num_m;
-      m0 = mt * BM;
-      mvalid = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
+  int e = 0, nt, mt, m0, mvalid;
+  if (g.t_off) {
+    int lo = 0, hi = g.n_groups;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g.t_off[mid] * nN <= L)
+        lo = mid;
+      else
+        hi = mid;
     }
-    kb = 0;
-    ke = g.K;
+    e = lo;
+    const int t0 = g.t_off[e], te = g.t_off[e + 1] - t0;
+    const int local = L - t0 * nN;
+    nt = local / te;
+    mt = t0 + (local - nt * te);
+    m0 = g.t_row0[mt];
+    mvalid = g.t_rows[mt];
   } else {
-    const int nM = (g.M + BM - 1) / BM;
-    e = L / (nM * nN);
-    const int r = L - e * nM * nN;
-    nt = r / nM;
-    const int mt = r - nt * nM;
+    const int num_m = (int)((g.rows + BM - 1) / BM);
+    nt = L / num_m;
+    mt = L - nt * num_m;
     m0 = mt * BM;
-    mvalid = g.M - m0 < BM ? g.M - m0 : BM;
-    if (g.koff) {
-      kb = g.koff[e];
-      ke = g.koff[e + 1];
-    } else {
-      kb = e * g.kchunk;
-      ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
-    }
+    mvalid = (int)(g.rows - m0 < BM ? g.rows - m0 : BM);
   }
+  const int kb = 0, ke = g.K;
   const int n0 = nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -213,7 +197,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 
   // Row maps of the K-contiguous operands (fixed across K slices).
   KcRows ar{}, br{}, br2{};
-  if constexpr (!AKS) kc_init(ar, tid, mvalid, m0, g.lda);
+  kc_init(ar, tid, mvalid, m0, g.lda);
   if constexpr (!BKS) {
     kc_init(br, tid, g.N - n0, n0, g.ldb);
     if constexpr (DUAL) br2 = br;
@@ -248,23 +232,18 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   constexpr int PF = DUAL ? 1 : 2;
   for (int p = 0; p < g.npass && nk > 0; ++p) {
     const void* Ab = g.A[p];
-    const void* Bb = KGRP ? g.B[p]
-                          : static_cast<const void*>(static_cast<const uint16_t*>(g.B[p]) +
-                                                     (int64_t)e * g.b_gstride);
+    const void* Bb =
+        static_cast<const void*>(static_cast<const uint16_t*>(g.B[p]) + (int64_t)e * g.b_gstride);
     const void* B2b = nullptr;
     if constexpr (DUAL)
-      B2b = KGRP ? g.B2
-                 : static_cast<const void*>(static_cast<const uint16_t*>(g.B2) +
-                                            (int64_t)e * g.b_gstride);
-    const int bklim = KGRP ? ke : g.bk_lim;
+      B2b = static_cast<const void*>(static_cast<const uint16_t*>(g.B2) +
+                                     (int64_t)e * g.b_gstride);
+    const int bklim = g.bk_lim;
 
     u32x4 ra[PF][4], rbv[PF][4], rb2[PF][DUAL ? 4 : 1];
     auto load = [&](int kt, int st) {
       const int k0 = kb + kt * BK;
-      if constexpr (AKS)
-        ks_load(ra[st], Ab, g.lda, k0, ke, m0, g.a_lim, tid);
-      else
-        kc_load(ra[st], Ab, ar, k0, ke, tid);
+      kc_load(ra[st], Ab, ar, k0, ke, tid);
       if constexpr (BKS) {
         ks_load(rbv[st], Bb, g.ldb, k0, bklim, n0, g.b_lim, tid);
         if constexpr (DUAL) ks_load(rb2[st], B2b, g.ldb, k0, bklim, n0, g.b_lim, tid);
@@ -274,10 +253,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
       }
     };
     auto store = [&](int st, int b) {
-      if constexpr (AKS)
-        ks_store(sA[b], ra[st], tid);
-      else
-        kc_store(sA[b], ra[st], tid);
+      kc_store(sA[b], ra[st], tid);
       if constexpr (BKS) {
         ks_store(sB[b], rbv[st], tid);
         if constexpr (DUAL) ks_store(sB2[b], rb2[st], tid);
@@ -342,8 +318,8 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   // wm*64 + mb*32 + lane % 32 and column wn*64 + nb*32 + 8q + 4 (lane / 32) + j.
   const int cbase = n0 + wn * 64 + 4 * (lane >> 5);
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
-    const int mlim = KGRP ? g.M - m0 : mvalid;
-    char* C = static_cast<char*>(g.C) + (KGRP ? (int64_t)e * g.c_gstride * (EPI == EPI_F32 ? 4 : 2) : 0);
+    const int mlim = mvalid;
+    char* C = static_cast<char*>(g.C);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int ml = wm * 64 + mb * 32 + (lane & 31);
@@ -362,30 +338,6 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
           } else {
             *reinterpret_cast<uint2*>(C + (row * g.ldc + c) * 2) =
                 pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-          }
-        }
-    }
-  } else if constexpr (EPI == EPI_F32T) {
-    // C[n][m] (and C2[n][m] from the dual accumulators): lanes hold 32
-    // consecutive m of one n, so each store instruction writes 128 bytes.
-    const int mlim = KGRP ? g.M - m0 : mvalid;
-    float* C = static_cast<float*>(g.C) + (KGRP ? (int64_t)e * g.c_gstride : 0);
-    float* C2 = DUAL ? static_cast<float*>(g.C2) + (KGRP ? (int64_t)e * g.c_gstride : 0) : nullptr;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int ml = wm * 64 + mb * 32 + (lane & 31);
-      if (ml >= mlim) continue;
-      const int64_t m = (int64_t)m0 + ml;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = cbase + nb * 32 + 8 * q;
-          if (c >= g.N) continue;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            C[(int64_t)(c + j) * g.ldc + m] = acc[nb][mb][4 * q + j];
-            if constexpr (DUAL) C2[(int64_t)(c + j) * g.ldc + m] = acc2[nb][mb][4 * q + j];
           }
         }
     }
@@ -707,15 +659,14 @@ __global__ void slab_sum_kernel(const float4* __restrict__ slabs, int G, int64_t
 
 int seg_blocks(BgKind kind, const BgSeg& g) {
   const int nN = (g.N + BN - 1) / BN;
-  if (kind == BG_WGRAD || kind == BG_WGRAD2) return g.G * ((g.M + BM - 1) / BM) * nN;
-  if (kind == BG_WGRAD_BIG) return g.G * ((g.M + WB - 1) / WB) * ((g.N + WB - 1) / WB);
+  if (kind == BG_WGRAD) return g.G * ((g.M + WB - 1) / WB) * ((g.N + WB - 1) / WB);
   if (g.t_off) return g.max_tiles * nN;
   return (int)((g.rows + BM - 1) / BM) * nN;
 }
 
-template <bool KGRP, bool AKS, bool BKS, int EPI, bool DUAL>
+template <bool BKS, int EPI, bool DUAL>
 hipError_t launch_t(const BgArgs& args, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((bg_kernel<KGRP, AKS, BKS, EPI, DUAL>), dim3(grid), dim3(NT), 0, s, args);
+  hipLaunchKernelGGL((bg_kernel<BKS, EPI, DUAL>), dim3(grid), dim3(NT), 0, s, args);
   return hipGetLastError();
 }
 
@@ -733,13 +684,11 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
   }
   if (grid == 0) return hipSuccess;
   switch (kind) {
-    case BG_LOGITS: return launch_t<false, false, false, EPI_F32, false>(args, grid, s);
-    case BG_PROJ: return launch_t<false, false, true, EPI_BF16, false>(args, grid, s);
-    case BG_SWIGLU: return launch_t<false, false, false, EPI_SWIGLU, true>(args, grid, s);
-    case BG_DU: return launch_t<false, false, true, EPI_DU, false>(args, grid, s);
-    case BG_WGRAD: return launch_t<true, true, true, EPI_F32, false>(args, grid, s);
-    case BG_WGRAD2: return launch_t<true, true, true, EPI_F32T, true>(args, grid, s);
-    case BG_WGRAD_BIG:
+    case BG_LOGITS: return launch_t<false, EPI_F32, false>(args, grid, s);
+    case BG_PROJ: return launch_t<true, EPI_BF16, false>(args, grid, s);
+    case BG_SWIGLU: return launch_t<false, EPI_SWIGLU, true>(args, grid, s);
+    case BG_DU: return launch_t<true, EPI_DU, false>(args, grid, s);
+    case BG_WGRAD:
       hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(NT), 0, s, args);
       return hipGetLastError();
   }
