@@ -226,10 +226,9 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   }
 
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
-  // K slices kt+1 .. kt+PF wait in registers (PF sets, filled in turn)
-  // while slice kt is multiplied out of LDS; the dual product has no room
-  // for a second set.
-  constexpr int PF = DUAL ? 1 : 2;
+  // K slices kt+1 and kt+2 wait in registers (two sets, filled in turn)
+  // while slice kt is multiplied out of LDS.
+  constexpr int PF = 2;
   for (int p = 0; p < g.npass && nk > 0; ++p) {
     const void* Ab = g.A[p];
     const void* Bb =
