@@ -229,6 +229,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   // K slices kt+1 and kt+2 wait in registers (two sets, filled in turn)
   // while slice kt is multiplied out of LDS.
   constexpr int PF = 2;
+  static_assert(PF == 2, "the main loop below is unrolled for two register sets");
   for (int p = 0; p < g.npass && nk > 0; ++p) {
     const void* Ab = g.A[p];
     const void* Bb =
@@ -291,24 +292,25 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
       }
     };
 
-#pragma unroll
-    for (int j = 0; j < PF; ++j)
-      if (j < nk) load(j, j);
+    // The slice count is padded to even (a padded slice loads zeros) and
+    // every step issues its prefetch, clamped to the last slice: a load
+    // under a branch leaves the compiler unsure how many loads are in flight
+    // where the paths merge, and it then waits for all of them.
+    const int nkp = (nk + 1) & ~1;
+    load(0, 0);
+    load(1, 1);
     store(0, 0);
     __syncthreads();
-    // Unrolled by PF so register sets and LDS buffers are static: slice
-    // kt = base + j sits in set j and LDS buffer kt & 1 (PF is 1 or 2).
-    for (int base = 0; base < nk; base += PF) {
+    // Unrolled by two so register sets and LDS buffers are static: slice
+    // kt = base + j sits in set j and LDS buffer j.
+    for (int base = 0; base < nkp; base += 2) {
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int kt = base + j;
-        if (kt < nk) {
-          const int b = PF == 2 ? j : (kt & 1);
-          if (kt + PF < nk) load(kt + PF, j);
-          compute(b);
-          if (kt + 1 < nk) store((j + 1) % PF, b ^ 1);
-          __syncthreads();
-        }
+        load(kt + 2 < nkp ? kt + 2 : nkp - 1, j);
+        compute(j);
+        if (kt + 1 < nkp) store(j ^ 1, j ^ 1);
+        __syncthreads();
       }
     }
   }
