@@ -318,29 +318,57 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   // Epilogue.  Accumulator element 4q + j of block (nb, mb) is row
   // wm*64 + mb*32 + lane % 32 and column wn*64 + nb*32 + 8q + 4 (lane / 32) + j.
   const int cbase = n0 + wn * 64 + 4 * (lane >> 5);
+  (void)cbase;
+  // Plain and du epilogues go through LDS, 32 rows of the wave's block at a
+  // time: in the accumulator layout each lane holds a different row, so
+  // direct accesses would touch 32 rows per instruction; staged, the global
+  // loads and stores run along rows.
+  constexpr int SPF = 64 + 4;  // fp32 staging pitch (floats)
+  constexpr int SPH = 64 + 8;  // bf16 staging pitch (elements)
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
-    const int mlim = mvalid;
     char* C = static_cast<char*>(g.C);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int ml = wm * 64 + mb * 32 + (lane & 31);
-      if (ml >= mlim) continue;
-      const int64_t row = (int64_t)m0 + ml;
+      if constexpr (EPI == EPI_F32) {
+        float* st = reinterpret_cast<float*>(&sA[0][0]) + wave * 32 * SPF;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = cbase + nb * 32 + 8 * q;
-          if (c >= g.N) continue;
-          const f32x16& a = acc[nb][mb];
-          if constexpr (EPI == EPI_F32) {
-            *reinterpret_cast<float4*>(C + (row * g.ldc + c) * 4) =
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[nb][mb];
+            *reinterpret_cast<float4*>(&st[(lane & 31) * SPF + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
                 make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-          } else {
-            *reinterpret_cast<uint2*>(C + (row * g.ldc + c) * 2) =
+          }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 4 * i + (lane >> 4), ml = wm * 64 + mb * 32 + r;
+          const int c = n0 + wn * 64 + 4 * (lane & 15);
+          if (ml < mvalid && c < g.N)
+            *reinterpret_cast<float4*>(C + (((int64_t)m0 + ml) * g.ldc + c) * 4) =
+                *reinterpret_cast<const float4*>(&st[r * SPF + 4 * (lane & 15)]);
+        }
+      } else {
+        uint16_t* st = &sA[0][0] + wave * 32 * SPH;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[nb][mb];
+            *reinterpret_cast<uint2*>(&st[(lane & 31) * SPH + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
                 pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * i + (lane >> 3), ml = wm * 64 + mb * 32 + r;
+          const int c = n0 + wn * 64 + 8 * (lane & 7);
+          if (ml < mvalid && c < g.N)
+            *reinterpret_cast<u32x4*>(C + (((int64_t)m0 + ml) * g.ldc + c) * 2) =
+                *reinterpret_cast<const u32x4*>(&st[r * SPH + 8 * (lane & 7)]);
         }
+      }
+      __syncthreads();
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     const uint16_t* Q = static_cast<const uint16_t*>(g.q);
@@ -390,39 +418,45 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
     const uint16_t* S = static_cast<const uint16_t*>(g.dxs);
     const uint16_t* X = static_cast<const uint16_t*>(g.dxp);
     float* C = static_cast<float*>(g.C);
+    float* st = reinterpret_cast<float*>(&sA[0][0]) + wave * 32 * SPF;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int ml = wm * 64 + mb * 32 + (lane & 31);
-      if (ml >= mvalid) continue;
-      const int64_t t = (int64_t)m0 + ml;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = cbase + nb * 32 + 8 * q;
-          if (c >= g.N) continue;
-          float o[4], tmp[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * q + j];
-          const int64_t at = t * g.ldc + c;
-          if (R) {
-            unpack4(*reinterpret_cast<const uint2*>(&R[at]), tmp);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
-          }
-          if (S) {
-            unpack4(*reinterpret_cast<const uint2*>(&S[at]), tmp);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
-          }
-          for (int s = 0; s < g.k; ++s) {
-            const int64_t r = g.slot_of[t * g.k + s];
-            unpack4(*reinterpret_cast<const uint2*>(&X[r * g.ldc + c]), tmp);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
-          }
-          *reinterpret_cast<float4*>(&C[at]) = make_float4(o[0], o[1], o[2], o[3]);
+          const f32x16& a = acc[nb][mb];
+          *reinterpret_cast<float4*>(&st[(lane & 31) * SPF + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         }
+      __syncthreads();
+      const int c = n0 + wn * 64 + 4 * (lane & 15);
+#pragma unroll 2
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4), ml = wm * 64 + mb * 32 + r;
+        if (ml >= mvalid || c >= g.N) continue;
+        const int64_t t = (int64_t)m0 + ml, at = t * g.ldc + c;
+        const float4 v = *reinterpret_cast<const float4*>(&st[r * SPF + 4 * (lane & 15)]);
+        float o[4] = {v.x, v.y, v.z, v.w}, tmp[4];
+        if (R) {
+          unpack4(*reinterpret_cast<const uint2*>(&R[at]), tmp);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+        }
+        if (S) {
+          unpack4(*reinterpret_cast<const uint2*>(&S[at]), tmp);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+        }
+        for (int sl = 0; sl < g.k; ++sl) {
+          const int64_t rr = g.slot_of[t * g.k + sl];
+          unpack4(*reinterpret_cast<const uint2*>(&X[rr * g.ldc + c]), tmp);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+        }
+        *reinterpret_cast<float4*>(&C[at]) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      __syncthreads();
     }
   }
 }
