@@ -4,8 +4,8 @@ The oracle's gradients are pinned by finite differences of an independent
 forward (test_oracle_bwd_pins.py).  Its routing inputs (topk_idx, f) come
 from the oracle's own forward, and the GPU receives the same routing, so
 both sides differentiate the same function.  Small workloads compare every
-gradient in full; the 16B- and 2B-shaped workloads compare du on sampled
-tokens and the weight gradients of sampled experts.  A HIP-graph capture of
+gradient in full; the 2B-, 16B- and 145B-shaped workloads compare du on
+sampled tokens and the weight gradients of sampled experts.  A HIP-graph capture of
 the backward replays to the eager bits.
 """
 import numpy as np
@@ -138,20 +138,31 @@ def test_bwd_is_deterministic():
         assert np.array_equal(a[kk].view(np.uint32), b[kk].view(np.uint32)), kk
 
 
-def test_bwd_16b_sampled():
-    """The 16B-shaped layer (T = 4096, 64 routed experts, top-6, 2 shared,
-    alpha = 0.001): du on sampled tokens and the weight gradients of the
-    most and the least loaded expert."""
-    name = "16b"
+SAMPLED = {
+    # name: (tokens sampled, balance coefficient)
+    "16b": (24, moe_synth.BALANCE_ALPHA["16b"]),
+    # d = 1280 and d_ff = 896 are ragged against the 256-wide weight-gradient tiles
+    "2b": (16, moe_synth.BALANCE_ALPHA["2b"]),
+    # 4 shared experts (width 5632), d = 4096, Zipf-skewed loads (up to ~2000 rows)
+    "145b": (12, moe_synth.BALANCE_ALPHA["16b"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLED))
+def test_bwd_full_size_sampled(name):
+    """The model-shaped layers: du on sampled tokens and all weight gradients
+    of the most and the least loaded expert; the centroid and shared-expert
+    gradients are checked for finiteness (in full on the small workloads)."""
     cfg = ALL[name]
     inp = inputs(name)
     r = oracle.route(inp["u"], inp["centroids"], cfg.k)
     dh = moe_synth.make_upstream_grad(cfg, seed=1)
     dh32 = (dh.astype(np.uint32) << 16).view(np.float32)
-    alpha = moe_synth.BALANCE_ALPHA["16b"]
-    toks = sample_tokens(cfg.T, 24)
+    ntok, alpha = SAMPLED[name]
+    toks = sample_tokens(cfg.T, ntok)
     cnt = np.bincount(r["topk_idx"].ravel(), minlength=cfg.n)
     experts = np.array([int(cnt.argmax()), int(np.where(cnt > 0, cnt, cnt.max() + 1).argmin())])
+    print(f"{name}: experts {experts.tolist()} with {cnt[experts].tolist()} rows", flush=True)
     want = oracle.layer_bwd(inp, cfg.N, cfg.m, cfg.K, cfg.K_s, r["topk_idx"], r["f"], dh32, alpha,
                             toks=toks, want_dcent=False, experts=experts, want_shared=False)
     got = run_bwd(cfg, inp, r, dh, alpha)
@@ -161,30 +172,6 @@ def test_bwd_16b_sampled():
     check_all(got, want, ["du", "dw1", "dw3", "dw2"])
     for kk in ("dcent", "dws1", "dws3", "dws2"):
         assert np.isfinite(got[kk]).all(), kk
-
-
-def test_bwd_2b_sampled():
-    """The 2B-shaped layer (T = 8192, d = 1280, 63 routed experts + 1 shared,
-    top-7, alpha = 0.01): d and d_ff = 896 are ragged against the 256-wide
-    weight-gradient tiles.  du on sampled tokens, weight gradients of the
-    most and the least loaded expert."""
-    name = "2b"
-    cfg = ALL[name]
-    inp = inputs(name)
-    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
-    dh = moe_synth.make_upstream_grad(cfg, seed=1)
-    dh32 = (dh.astype(np.uint32) << 16).view(np.float32)
-    alpha = moe_synth.BALANCE_ALPHA["2b"]
-    toks = sample_tokens(cfg.T, 16)
-    cnt = np.bincount(r["topk_idx"].ravel(), minlength=cfg.n)
-    experts = np.array([int(cnt.argmax()), int(np.where(cnt > 0, cnt, cnt.max() + 1).argmin())])
-    want = oracle.layer_bwd(inp, cfg.N, cfg.m, cfg.K, cfg.K_s, r["topk_idx"], r["f"], dh32, alpha,
-                            toks=toks, want_dcent=False, experts=experts, want_shared=False)
-    got = run_bwd(cfg, inp, r, dh, alpha)
-    got["du"] = got["du"][toks]
-    for kk in ("dw1", "dw3", "dw2"):
-        got[kk] = got[kk][experts]
-    check_all(got, want, ["du", "dw1", "dw3", "dw2"])
 
 
 def test_bwd_graph_replays():
