@@ -219,6 +219,8 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  * alpha f_i / T, dl = s * (ds - <s, ds>), du += E^T dl, dE_i = sum_t dl_{t,i} u_t.
  *   u, centroids, w1, w3, w2, ws1, ws3, ws2   as moe_layer_fwd (row-major; bf16)
  *   topk_idx [T][k], topk_gate [T][k], f [n]  the forward's routing outputs
+ *                     (an expert id outside [0, n) breaks the contract; such a
+ *                     slot is skipped, as moe_permute leaves it out)
  *   dh [T][d]         upstream gradient (bf16)
  *   alpha             balance-loss coefficient (0: no balance term)
  *   du [T][d], dcentroids [n][d]              out, fp32

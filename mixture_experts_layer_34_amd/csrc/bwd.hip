@@ -450,6 +450,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
         }
         for (int sl = 0; sl < g.k; ++sl) {
           const int64_t rr = g.slot_of[t * g.k + sl];
+          if (rr < 0) continue;  // slot left out by the grouping
           unpack4(*reinterpret_cast<const uint2*>(&X[rr * g.ldc + c]), tmp);
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[j] += tmp[j];
@@ -591,11 +592,17 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  for (int j = lane; j < k; j += 64) gperm[slot_of[t * k + j]] = gate[t * k + j];
+  // slot_of is -1 for an expert id outside [0, n) (the grouping leaves such
+  // slots out); they are skipped here and in the kernels below.
+  for (int j = lane; j < k; j += 64) {
+    const int r = slot_of[t * k + j];
+    if (r >= 0) gperm[r] = gate[t * k + j];
+  }
   for (int c = lane; c < nch; c += 64) {
     const u32x4 a = u[t * nch + c], b = dh[t * nch + c];
     for (int j = 0; j < k; ++j) {
       const int64_t r = slot_of[t * k + j];
+      if (r < 0) continue;
       xp[r * nch + c] = a;
       dhp[r * nch + c] = b;
     }
@@ -655,9 +662,11 @@ __global__ __launch_bounds__(256) void softmax_bwd_kernel(
   if (live) {
     for (int j = lane; j < k; j += 64) {
       const int64_t r = slot_of[t * k + j];
+      const int e = topk_idx[t * k + j];
+      if (r < 0 || e < 0 || e >= n) continue;  // slot left out by the grouping
       float dg = 0.0f;
       for (int p = 0; p < ldgp; ++p) dg += dgp[r * ldgp + p];
-      sds[w][topk_idx[t * k + j]] += dg;  // the kept experts of a token are distinct
+      sds[w][e] += dg;  // the kept experts of a token are distinct
     }
   }
   __syncthreads();

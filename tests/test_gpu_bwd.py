@@ -219,3 +219,28 @@ def test_bwd_graph_replays():
         for k in want:
             got = out[k].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), want[k].view(np.uint32)), (i, k)
+
+
+def test_bwd_skips_expert_ids_out_of_range():
+    """topk_idx entries outside [0, n) break the contract (the forward never
+    writes them); the grouping leaves such slots out and the backward skips
+    them: every output stays finite, and du of the tokens whose slots are all
+    valid is bit-identical to the clean run (each output row is reduced over
+    its own slots only)."""
+    name = "ragged_bf16"
+    cfg = ALL[name]
+    inp = inputs(name)
+    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    dh = moe_synth.make_upstream_grad(cfg, seed=1)
+    clean = run_bwd(cfg, inp, r, dh, 0.37)
+    bad = dict(r)
+    bad["topk_idx"] = r["topk_idx"].copy()
+    hit = np.array([3, 150, 299])
+    bad["topk_idx"][hit[0], 0] = -1
+    bad["topk_idx"][hit[1], 1] = cfg.n
+    bad["topk_idx"][hit[2], cfg.k - 1] = cfg.n + 7
+    got = run_bwd(cfg, inp, bad, dh, 0.37)
+    for kk, v in got.items():
+        assert np.isfinite(v).all(), kk
+    keep = np.setdiff1d(np.arange(cfg.T), hit)
+    assert np.array_equal(got["du"][keep].view(np.uint32), clean["du"][keep].view(np.uint32))
