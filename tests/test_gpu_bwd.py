@@ -107,6 +107,22 @@ def test_bwd_small(name, flags):
         assert not got["dw1"][e].any() and not got["dw2"][e].any()
 
 
+def test_bwd_decode_shape_in_full():
+    """The 16B-shaped layer at 64 tokens (all 64 experts touched by a few rows
+    each, two shared experts of width 2816): every gradient in full."""
+    name = "16b_decode"
+    cfg = ALL[name]
+    inp = inputs(name)
+    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    dh = moe_synth.make_upstream_grad(cfg, seed=1)
+    dh32 = (dh.astype(np.uint32) << 16).view(np.float32)
+    alpha = moe_synth.BALANCE_ALPHA["16b"]
+    want = oracle.layer_bwd(inp, cfg.N, cfg.m, cfg.K, cfg.K_s, r["topk_idx"], r["f"], dh32, alpha,
+                            experts=np.arange(cfg.n))
+    got = run_bwd(cfg, inp, r, dh, alpha)
+    check_all(got, want, ["du", "dcent", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2"])
+
+
 def test_bwd_balance_term_alone():
     """dh = 0 leaves only the balance loss: du and the centroid gradient come
     from the softmax backward of alpha f_i / T alone; every weight gradient is
