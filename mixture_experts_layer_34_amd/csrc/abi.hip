@@ -577,7 +577,6 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     if (!marks) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(marks[mark_i++]), s);
   };
-  const int64_t R = d.T * d.k;
   const int fs = d.K_s * d.d_ff;
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm_token);
