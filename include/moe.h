@@ -217,7 +217,9 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  * db = g dhid * SiLU(a), dx = W1^T da + W3^T db, dW1 = da x^T,
  * dW3 = db x^T, dW2 = g dh (SiLU(a) * b)^T; router: ds_i = dg (kept i) +
  * alpha f_i / T, dl = s * (ds - <s, ds>), du += E^T dl, dE_i = sum_t dl_{t,i} u_t.
- *   u, centroids, w1, w3, w2, ws1, ws3, ws2   as moe_layer_fwd (row-major; bf16)
+ *   u, centroids, w1, w3, w2, ws1, ws3, ws2   as moe_layer_fwd (bf16; row-major, or
+ *                     all six in the layout of moe_pack_weights with
+ *                     MOE_PACKED_WEIGHTS, the same copies the forward reads)
  *   topk_idx [T][k], topk_gate [T][k], f [n]  the forward's routing outputs
  *                     (an expert id outside [0, n) breaks the contract; such a
  *                     slot is skipped, as moe_permute leaves it out)
@@ -229,12 +231,12 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  *   dws1, dws3 [K_s*d_ff][d], dws2 [d][K_s*d_ff]   out, fp32; NULL allowed
  *                     when K_s = 0 or flags has MOE_NO_SHARED
  *   flags             MOE_NO_RESIDUAL / MOE_NO_SHARED as moe_layer_fwd (the
- *                     forward must have used the same flags)
+ *                     forward must have used the same flags); MOE_PACKED_WEIGHTS
  *   ws                workspace of at least moe_bwd_workspace_bytes(p) bytes
  * Intermediates (the SwiGLU gradients, q = W2^T dh, the experts' input
  * gradients, the router's softmax gradient) are rounded to bf16; every
- * product accumulates in fp32.  Requires p->dtype == MOE_BF16; packed
- * weights give MOE_ERR_UNSUPPORTED.
+ * product accumulates in fp32; the result does not depend on the weight
+ * layout.  Requires p->dtype == MOE_BF16.
  */
 moe_status moe_layer_bwd(const moe_problem *p, const void *u, const void *centroids,
                          const void *w1, const void *w3, const void *w2, const void *ws1,

@@ -555,8 +555,10 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
   if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS)) return MOE_ERR_SHAPE;
-  if (p->dtype != MOE_BF16 || (flags & MOE_PACKED_WEIGHTS)) return MOE_ERR_UNSUPPORTED;
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
+  // packed weights: the layout of moe_pack_weights, read by the same kernels
+  const bool packed = (flags & MOE_PACKED_WEIGHTS) != 0;
   if (!u || !centroids || !w1 || !w3 || !w2 || !topk_idx || !topk_gate || !f || !dh || !du ||
       !dcentroids || !dw1 || !dw3 || !dw2)
     return MOE_ERR_NULL;
@@ -659,7 +661,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
       g[1].C = qs;
       g[1].ldc = fs;
     }
-    MOE_TRY(moe::launch_bg(moe::BG_PROJ, g, shared ? 2 : 1, s));
+    MOE_TRY(moe::launch_bg(packed ? moe::BG_PROJ_PACKED : moe::BG_PROJ, g, shared ? 2 : 1, s));
   }
   MOE_TRY(mark());
 
@@ -707,7 +709,8 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
       g[1].db = dbs;
       g[1].gh = ghs;
     }
-    MOE_TRY(moe::launch_bg(moe::BG_SWIGLU, g, shared ? 2 : 1, s));
+    MOE_TRY(moe::launch_bg(packed ? moe::BG_SWIGLU_PACKED : moe::BG_SWIGLU, g, shared ? 2 : 1,
+                           s));
   }
   MOE_TRY(mark());
 
@@ -747,7 +750,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
       g[1].C = dxs;
       g[1].ldc = d.d;
     }
-    MOE_TRY(moe::launch_bg(moe::BG_PROJ, g, shared ? 2 : 1, s));
+    MOE_TRY(moe::launch_bg(packed ? moe::BG_PROJ_PACKED : moe::BG_PROJ, g, shared ? 2 : 1, s));
   }
   MOE_TRY(mark());
 

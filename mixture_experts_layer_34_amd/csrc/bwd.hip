@@ -71,6 +71,18 @@ struct KcRows {
   uint32_t ok;      // bit i: row i exists
 };
 
+// Packed weights (moe_pack_weights): a [rows][K] matrix stored as 32-row
+// bands of 16-wide K blocks of 512 elements, element (r, k) of a block at
+// ((r % 32) + 32 ((k % 16) / 8)) * 8 + k % 8.  Eight consecutive k of one
+// row stay contiguous, which is all the loaders below read.
+__device__ __forceinline__ int64_t packed_at(int64_t r, int k, int64_t K) {
+  return ((r >> 5) * (K >> 4) + (k >> 4)) * 512 + ((r & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
+}
+
+// PK: the operand is a packed weight matrix (K-contiguous in the packed
+// sense); a 64-wide K slice then moves the 16-byte pieces by 64 * 32
+// elements instead of 64.
+template <bool PK = false>
 __device__ __forceinline__ void kc_init(KcRows& R, int tid, int nvalid, int64_t row0,
                                         int64_t ld) {
   R.ok = 0;
@@ -80,18 +92,19 @@ __device__ __forceinline__ void kc_init(KcRows& R, int tid, int nvalid, int64_t 
     const int r = (tid >> 3) + 32 * i;
     const bool v = r < nvalid;
     const int64_t mr = v ? row0 + r : 0;
-    R.off[i] = (uint32_t)((mr * ld + kc) * 2);
+    R.off[i] = (uint32_t)((PK ? packed_at(mr, kc, ld) : mr * ld + kc) * 2);
     R.ok |= (v ? 1u : 0u) << i;
   }
 }
 
+template <bool PK = false>
 __device__ __forceinline__ void kc_load(u32x4 v[4], const void* base, const KcRows& R, int k0,
                                         int klim, int tid) {
   const bool kin = k0 + (tid & 7) * 8 < klim;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (kin && ((R.ok >> i) & 1u))
-      v[i] = ld_off<u32x4>(base, R.off[i] + (uint32_t)k0 * 2u);
+      v[i] = ld_off<u32x4>(base, R.off[i] + (uint32_t)k0 * (PK ? 64u : 2u));
     else
       v[i] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -111,6 +124,7 @@ __device__ __forceinline__ void kc_store(uint16_t* s, const u32x4 v[4], int tid)
 // kg = lane >> 2 (four lanes read 64 contiguous bytes of a row).  Rows are
 // addressed directly: a row map would put a dependent load in front of every
 // load, and the in-order load counter would then wait for all loads in flight.
+template <bool PK = false>
 __device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld, int kbase,
                                         int klim, int col0, int clim, int tid) {
   const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
@@ -120,7 +134,8 @@ __device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld
   for (int kk = 0; kk < 4; ++kk) {
     const int kr = kbase + kg * 4 + kk;
     if (cin && kr < klim)
-      v[kk] = ld_off<u32x4>(base, (uint32_t)(((int64_t)kr * ld + col) * 2));
+      v[kk] = ld_off<u32x4>(
+          base, (uint32_t)((PK ? packed_at(kr, col, ld) : (int64_t)kr * ld + col) * 2));
     else
       v[kk] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -153,8 +168,8 @@ __device__ __forceinline__ void unpack4(uint2 p, float* o) {
 
 // Rows grouping (the tile list of the forward's grouping, or one group of
 // `rows` rows).  A is K-contiguous; BKS: B K-strided in memory; DUAL: second
-// B with its own accumulators (SwiGLU's a and b).
-template <bool BKS, int EPI, bool DUAL>
+// B with its own accumulators (SwiGLU's a and b); PK: B (and B2) packed.
+template <bool BKS, int EPI, bool DUAL, bool PK>
 __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][TILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][TILE_EL];
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   KcRows ar{}, br{}, br2{};
   kc_init(ar, tid, mvalid, m0, g.lda);
   if constexpr (!BKS) {
-    kc_init(br, tid, g.N - n0, n0, g.ldb);
+    kc_init<PK>(br, tid, g.N - n0, n0, g.ldb);
     if constexpr (DUAL) br2 = br;
   }
   (void)br2;
@@ -245,11 +260,11 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
       const int k0 = kb + kt * BK;
       kc_load(ra[st], Ab, ar, k0, ke, tid);
       if constexpr (BKS) {
-        ks_load(rbv[st], Bb, g.ldb, k0, bklim, n0, g.b_lim, tid);
-        if constexpr (DUAL) ks_load(rb2[st], B2b, g.ldb, k0, bklim, n0, g.b_lim, tid);
+        ks_load<PK>(rbv[st], Bb, g.ldb, k0, bklim, n0, g.b_lim, tid);
+        if constexpr (DUAL) ks_load<PK>(rb2[st], B2b, g.ldb, k0, bklim, n0, g.b_lim, tid);
       } else {
-        kc_load(rbv[st], Bb, br, k0, ke, tid);
-        if constexpr (DUAL) kc_load(rb2[st], B2b, br2, k0, ke, tid);
+        kc_load<PK>(rbv[st], Bb, br, k0, ke, tid);
+        if constexpr (DUAL) kc_load<PK>(rb2[st], B2b, br2, k0, ke, tid);
       }
     };
     auto store = [&](int st, int b) {
@@ -708,9 +723,9 @@ int seg_blocks(BgKind kind, const BgSeg& g) {
   return (int)((g.rows + BM - 1) / BM) * nN;
 }
 
-template <bool BKS, int EPI, bool DUAL>
+template <bool BKS, int EPI, bool DUAL, bool PK = false>
 hipError_t launch_t(const BgArgs& args, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((bg_kernel<BKS, EPI, DUAL>), dim3(grid), dim3(NT), 0, s, args);
+  hipLaunchKernelGGL((bg_kernel<BKS, EPI, DUAL, PK>), dim3(grid), dim3(NT), 0, s, args);
   return hipGetLastError();
 }
 
@@ -731,6 +746,8 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
     case BG_LOGITS: return launch_t<false, EPI_F32, false>(args, grid, s);
     case BG_PROJ: return launch_t<true, EPI_BF16, false>(args, grid, s);
     case BG_SWIGLU: return launch_t<false, EPI_SWIGLU, true>(args, grid, s);
+    case BG_PROJ_PACKED: return launch_t<true, EPI_BF16, false, true>(args, grid, s);
+    case BG_SWIGLU_PACKED: return launch_t<false, EPI_SWIGLU, true, true>(args, grid, s);
     case BG_DU: return launch_t<true, EPI_DU, false>(args, grid, s);
     case BG_WGRAD:
       hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(NT), 0, s, args);

@@ -253,7 +253,8 @@ def test_layer_bwd_checks():
     outs = [A] * 8
     call = lambda pp, i, a, o, flags, w: moe.moe_layer_bwd(pp, *i, a, *o, flags, A, w)
     assert status(call, p16(dtype="f32"), ins, 0.0, outs, 0, BIG) == "MOE_ERR_UNSUPPORTED"
-    assert status(call, p, ins, 0.0, outs, moe.MOE_PACKED_WEIGHTS, BIG) == "MOE_ERR_UNSUPPORTED"
+    # packed weights are accepted: the same checks apply
+    assert status(call, p, ins, 0.0, outs, moe.MOE_PACKED_WEIGHTS, 0) == "MOE_ERR_WORKSPACE"
     assert status(call, p, ins, 0.0, outs, 8, BIG) == "MOE_ERR_SHAPE"
     assert status(call, p16(T=0), ins, 0.0, outs, 0, BIG) == "MOE_ERR_SHAPE"
     for i in range(12):

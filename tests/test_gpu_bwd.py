@@ -41,10 +41,18 @@ def prob(cfg):
 
 
 def run_bwd(cfg, inp, route, dh, alpha, flags=0):
-    """moe_layer_bwd on device copies; returns host fp32 arrays."""
+    """moe_layer_bwd on device copies; returns host fp32 arrays.  With
+    MOE_PACKED_WEIGHTS in flags the weights are packed first."""
     d = dev()
     p = prob(cfg)
     t = {k: to_device(inp[k], d) for k in ("u", "centroids", "w1", "w3", "w2", "ws1", "ws3", "ws2")}
+    if flags & moe.MOE_PACKED_WEIGHTS:
+        for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2"):
+            if t[k] is None:
+                continue
+            dst = torch.empty_like(t[k])
+            moe.moe_pack_weights(p, t[k].numel() // t[k].shape[-1], t[k].shape[-1], t[k], dst)
+            t[k] = dst
     idx = torch.from_numpy(route["topk_idx"]).to(d)
     gate = torch.from_numpy(route["topk_gate"]).to(d)
     f = torch.from_numpy(route["f"]).to(d)
@@ -105,6 +113,21 @@ def test_bwd_small(name, flags):
     unused = np.setdiff1d(np.arange(cfg.n), r["topk_idx"].ravel())
     for e in unused:
         assert not got["dw1"][e].any() and not got["dw2"][e].any()
+
+
+@pytest.mark.parametrize("name", BWD_SMALL + ["16b_decode"])
+def test_bwd_packed_weights_give_the_same_bits(name):
+    """The weights in the packed layout of moe_pack_weights (the copies the
+    forward's fast path reads) give bit-identical gradients: the same
+    products in the same order, read from other addresses."""
+    cfg = ALL[name]
+    inp = inputs(name)
+    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    dh = moe_synth.make_upstream_grad(cfg, seed=1)
+    a = run_bwd(cfg, inp, r, dh, 0.37)
+    b = run_bwd(cfg, inp, r, dh, 0.37, moe.MOE_PACKED_WEIGHTS)
+    for kk in a:
+        assert np.array_equal(a[kk].view(np.uint32), b[kk].view(np.uint32)), kk
 
 
 def test_bwd_decode_shape_in_full():
