@@ -13,7 +13,8 @@ Prints one JSON line with tokens/s, the roofline of the dominant kernel
 (timed live with HIP events recorded on the launch stream), per-kernel
 times, the backward pass of the same layer (moe_layer_bwd: time per step,
 per-kernel times and its dominant kernel's roofline), the 64-token decode
-regime's HBM rate, the 2B- and 145B-shaped layers, a granularity sweep (the
+regime's HBM rate, the 2B- and 145B-shaped layers (forward and backward), a
+granularity sweep (the
 16B budget cut into m = 1, 2, 4, 8 finer experts), and the CPU oracle timed
 on a bounded sample of the same workload.
 """
@@ -335,8 +336,9 @@ def gpu_shape_inputs(cfg, seed, torch, moe, copies):
     return {"u": u, "centroids": c}, sets
 
 
-def other_shape(name, cfg, torch, moe, hip, steps, warmup) -> dict:
-    """Layer tokens/s and grouped-GEMM MFMA fraction of one more model shape."""
+def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=None) -> dict:
+    """Layer tokens/s and grouped-GEMM MFMA fraction of one more model shape;
+    with bwd_alpha, also its backward pass on the same (packed) weights."""
     inp, sets = gpu_shape_inputs(cfg, 0, torch, moe, copies=1 if cfg.n * cfg.d_ff * cfg.d > 5e8 else 2)
     layer = Layer(cfg, inp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
     res = time_layer(layer, hip, steps, warmup)
@@ -357,6 +359,12 @@ def other_shape(name, cfg, torch, moe, hip, steps, warmup) -> dict:
         "kernel_us": {k: round(v * 1e3, 2) for k, v in res["kernel_ms"].items()},
         "inputs": "drawn on the GPU (seeded normals of the workload's distributions)",
     }
+    if bwd_alpha is not None:
+        b = backward_regime(torch, moe, hip, args, cfg, None, layer, packed=True, alpha=bwd_alpha,
+                            steps=max(5, steps // 2))
+        out["backward"] = {k: b[k] for k in ("ms_per_step", "tokens_per_s", "gemm_mfma_frac",
+                                             "weight_layout", "roofline")}
+        out["backward"]["kernel_us"] = {k: v["us"] for k, v in b["kernels"].items()}
     del layer, sets, inp
     torch.cuda.empty_cache()
     return out
@@ -420,21 +428,28 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
     }
 
 
-def backward_regime(torch, moe, hip, args, cfg, inp, layer) -> dict:
-    """moe_layer_bwd on the 16B-shaped layer: row-major weights (two copies
-    rotated), the forward's routing, a seeded upstream gradient and the
-    16B balance coefficient.  Time per step, per-kernel times from marks and
-    the roofline of the dominant kernel."""
+def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=None,
+                    steps=None) -> dict:
+    """moe_layer_bwd on a layer after its forward (the forward's routing), a
+    seeded upstream gradient and the balance coefficient (16B's by default).
+    Weights: row-major copies of inp's (two rotated), or with packed=True the
+    packed copies the forward already holds.  Time per step, per-kernel times
+    from marks and the roofline of the dominant kernel."""
     import moe_synth
     from mixture_experts_layer_34_amd.device import to_device
-    log("timing the 16B-shaped backward pass")
+    log(f"timing the backward pass ({cfg.name})")
     p = layer.p
     layer.run(0)
     torch.cuda.synchronize()
-    sets = [{k: to_device(inp[k], "cuda") for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}
-            for _ in range(args.rotate)]
+    if packed:
+        sets = layer.weights
+    else:
+        sets = [{k: to_device(inp[k], "cuda") for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}
+                for _ in range(args.rotate)]
     dh = to_device(moe_synth.make_upstream_grad(cfg, seed=1), "cuda")
-    alpha = moe_synth.BALANCE_ALPHA["16b"]
+    if alpha is None:
+        alpha = moe_synth.BALANCE_ALPHA["16b"]
+    flags = moe.MOE_PACKED_WEIGHTS if packed else 0
     f32 = dict(dtype=torch.float32, device="cuda")
     n, d, f, fs = cfg.n, cfg.d, cfg.d_ff, cfg.K_s * cfg.d_ff
     g = dict(du=torch.empty((cfg.T, d), **f32), dc=torch.empty((n, d), **f32),
@@ -448,13 +463,13 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer) -> dict:
         w = sets[i % len(sets)]
         a = (p, layer.u, layer.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"],
              layer.idx, layer.gate, layer.f, dh, alpha, g["du"], g["dc"], g["dw1"], g["dw3"],
-             g["dw2"], g["dws1"], g["dws3"], g["dws2"], 0, ws)
+             g["dw2"], g["dws1"], g["dws3"], g["dws2"], flags, ws)
         if marks is None:
             moe.moe_layer_bwd(*a, stream=stream)
         else:
             moe.moe_layer_bwd_marked(*a, marks, stream=stream)
 
-    steps = max(10, args.steps // 2)
+    steps = steps or max(10, args.steps // 2)
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
@@ -491,8 +506,8 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer) -> dict:
     gsec = sum(per[nm] for nm in gemm) * 1e-3
     del sets, g, ws
     return {
-        "workload": "DeepSeekMoE 16B-shaped layer backward: gradients of u, centroids and all "
-                    "expert weights, balance loss alpha = 0.001",
+        "workload": f"{cfg.name}-shaped layer backward: gradients of u, centroids and all "
+                    f"expert weights, balance loss alpha = {alpha}",
         "ms_per_step": round(ms, 4),
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
         "flop_per_step": int(sum(w["flop"] for w in work.values())),
@@ -500,7 +515,7 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer) -> dict:
         "gemm_mfma_frac": round(gflop / gsec / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": droof,
         "kernels": kern,
-        "weight_layout": "row-major",
+        "weight_layout": "packed" if packed else "row-major",
     }
 
 
@@ -627,8 +642,9 @@ def main():
         out["other_shapes"] = {}
         for name in ("2b", "145b"):
             log(f"timing the {name}-shaped layer")
-            out["other_shapes"][name] = other_shape(name, moe_synth.CONFIGS[name], torch, moe, hip,
-                                                    max(10, args.steps // 3), 3)
+            out["other_shapes"][name] = other_shape(
+                name, moe_synth.CONFIGS[name], torch, moe, hip, max(10, args.steps // 3), 3, args,
+                moe_synth.BALANCE_ALPHA["2b" if name == "2b" else "16b"])
     if not args.no_granularity:
         # Fine-grained segmentation at a fixed expert budget (total and
         # activated widths constant; m = 1 is GShard's top-2 layer): the cost
