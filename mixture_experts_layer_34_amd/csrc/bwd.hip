@@ -477,6 +477,23 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   }
 }
 
+// Workgroup -> (segment, logical tile) in launch order, so consecutive tiles
+// go round-robin over the XCDs.  Used where tiles differ in length (each
+// expert reduces over its own rows): contiguous per-XCD shares would give
+// the XCD holding the most loaded experts most of the work.
+__device__ __forceinline__ bool linear_pick(const BgArgs& a, int& si, int& L) {
+  int i = (int)blockIdx.x;
+  for (int s = 0; s < a.nseg; ++s) {
+    if (i < a.bound[s]) {
+      si = s;
+      L = i;
+      return true;
+    }
+    i -= a.bound[s];
+  }
+  return false;
+}
+
 // Weight gradients (k grouping, both operands K-strided, fp32 out) on
 // 256 x 256 tiles: an expert's K range is only its rows (a few hundred), so
 // a tile reuses each staged slice over four times the output of the
@@ -491,7 +508,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][WTILE_EL];
 
   int si = 0, L = 0;
-  if (!xcd_pick(args, WB, si, L)) return;
+  if (!linear_pick(args, si, L)) return;
   const BgSeg& g = args.seg[si];
   const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
   const int e = L / (nM * nN);
