@@ -144,8 +144,9 @@ def kernel_work(cfg, n_active: int, es: int = 2) -> dict:
 def bwd_kernel_work(cfg, n_active: int, es: int = 2) -> dict:
     """Algorithmic FLOPs and HBM bytes of each kernel of one moe_layer_bwd
     call (gradients of u, the centroids and all expert weights).  The a, b
-    projections are recomputed, so the routed experts cost 8 products of
-    2 R d d_ff FLOPs against the forward's 3."""
+    projections are recomputed (ab_swiglu), so the routed experts cost 8
+    products of 2 R d d_ff FLOPs against the forward's 3, or read from the
+    forward (swiglu_bwd), 6 products."""
     T, d, f, n, k, ks = cfg.T, cfg.d, cfg.d_ff, cfg.n, cfg.k, cfg.K_s
     R = T * k
     fs = ks * f
@@ -163,6 +164,10 @@ def bwd_kernel_work(cfg, n_active: int, es: int = 2) -> dict:
     w["ab_swiglu"] = dict(flop=4 * R * d * f + 4 * T * d * fs,
                           bytes=2 * (n_active * f + fs) * d * es + (R + T) * d * es
                           + 4 * (R * f + T * fs) * es + R * 8)
+    # with the forward's kept pre-activations: read q, a, b (and the gate),
+    # write da, db, gh and the gate-gradient partials
+    w["swiglu_bwd"] = dict(flop=0, bytes=6 * (R * f + T * fs) * es + R * 4
+                           + R * 2 * ((f + 127) // 128) * 4)
     w["dx"] = dict(flop=4 * R * f * d + 4 * T * fs * d,
                    bytes=2 * (n_active * f + fs) * d * es + 2 * (R * f + T * fs) * es
                    + (R + T) * d * es)
@@ -214,10 +219,11 @@ class Layer:
         self.flags = flags
         self.stream = torch.cuda.current_stream().cuda_stream
 
-    def run(self, i: int, marks=None, stream=None):
+    def run(self, i: int, marks=None, stream=None, extra_flags=0, ws=None):
         w = self.weights[i % len(self.weights)]
         args = (self.p, self.u, self.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"],
-                self.h, self.idx, self.gate, self.counts, self.f, self.P, self.flags, self.ws)
+                self.h, self.idx, self.gate, self.counts, self.f, self.P,
+                self.flags | extra_flags, self.ws if ws is None else ws)
         s = self.stream if stream is None else stream
         if marks is None:
             self.moe.moe_layer_fwd(*args, stream=s)
@@ -429,17 +435,23 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
 
 
 def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=None,
-                    steps=None) -> dict:
+                    steps=None, saved=False) -> dict:
     """moe_layer_bwd on a layer after its forward (the forward's routing), a
     seeded upstream gradient and the balance coefficient (16B's by default).
     Weights: row-major copies of inp's (two rotated), or with packed=True the
-    packed copies the forward already holds.  Time per step, per-kernel times
-    from marks and the roofline of the dominant kernel."""
+    packed copies the forward already holds.  saved=True: the forward keeps
+    its grouping and pre-activations (MOE_SAVE_FOR_BACKWARD) and the backward
+    reads them.  Time per step, per-kernel times from marks, the roofline of
+    the dominant kernel, and a training step (forward + backward) timed as
+    one loop."""
     import moe_synth
     from mixture_experts_layer_34_amd.device import to_device
-    log(f"timing the backward pass ({cfg.name})")
+    log(f"timing the backward pass ({cfg.name}{', saved pre-activations' if saved else ''})")
     p = layer.p
-    layer.run(0)
+    sv = moe.MOE_SAVE_FOR_BACKWARD if saved else 0
+    fws = (torch.empty(moe.moe_train_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+           if saved else None)
+    layer.run(0, extra_flags=sv, ws=fws)
     torch.cuda.synchronize()
     if packed:
         sets = layer.weights
@@ -449,7 +461,7 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
     dh = to_device(moe_synth.make_upstream_grad(cfg, seed=1), "cuda")
     if alpha is None:
         alpha = moe_synth.BALANCE_ALPHA["16b"]
-    flags = moe.MOE_PACKED_WEIGHTS if packed else 0
+    flags = (moe.MOE_PACKED_WEIGHTS if packed else 0) | sv
     f32 = dict(dtype=torch.float32, device="cuda")
     n, d, f, fs = cfg.n, cfg.d, cfg.d_ff, cfg.K_s * cfg.d_ff
     g = dict(du=torch.empty((cfg.T, d), **f32), dc=torch.empty((n, d), **f32),
@@ -462,7 +474,7 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
     def run(i, marks=None):
         w = sets[i % len(sets)]
         a = (p, layer.u, layer.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"],
-             layer.idx, layer.gate, layer.f, dh, alpha, g["du"], g["dc"], g["dw1"], g["dw3"],
+             layer.idx, layer.gate, layer.f, fws, dh, alpha, g["du"], g["dc"], g["dw1"], g["dw3"],
              g["dw2"], g["dws1"], g["dws3"], g["dws2"], flags, ws)
         if marks is None:
             moe.moe_layer_bwd(*a, stream=stream)
@@ -482,7 +494,7 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
     rec(e1, stream)
     torch.cuda.synchronize()
     ms = hip.ms(e0, e1) / steps
-    names = moe.moe_layer_bwd_kernels(p)
+    names = moe.moe_layer_bwd_kernels(p, flags)
     marks = [[hip.event() for _ in range(len(names) + 1)] for _ in range(steps)]
     for i in range(steps):
         run(i, marks[i])
@@ -492,6 +504,19 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
     for row in marks:
         for e in row:
             hip.destroy(e)
+    # the training step: forward (keeping what the backward reads, if saved)
+    # then backward, one loop
+    for i in range(2):
+        layer.run(i, extra_flags=sv, ws=fws)
+        run(i)
+    torch.cuda.synchronize()
+    rec(e0, stream)
+    for i in range(steps):
+        layer.run(i, extra_flags=sv, ws=fws)
+        run(i)
+    rec(e1, stream)
+    torch.cuda.synchronize()
+    train_ms = hip.ms(e0, e1) / steps
     hip.destroy(e0)
     hip.destroy(e1)
     n_active = int((layer.counts.cpu().numpy() > 0).sum())
@@ -504,7 +529,7 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
     gemm = [nm for nm in names if nm in ("q", "ab_swiglu", "dx", "wgrad", "wgrad13", "wgrad2")]
     gflop = sum(work[nm]["flop"] for nm in gemm)
     gsec = sum(per[nm] for nm in gemm) * 1e-3
-    del sets, g, ws
+    del sets, g, ws, fws
     return {
         "workload": f"{cfg.name}-shaped layer backward: gradients of u, centroids and all "
                     f"expert weights, balance loss alpha = {alpha}",
@@ -516,6 +541,8 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
         "roofline": droof,
         "kernels": kern,
         "weight_layout": "packed" if packed else "row-major",
+        "a_b": "kept by the forward (bf16)" if saved else "computed again",
+        "train_step_ms": round(train_ms, 4),
     }
 
 
@@ -634,7 +661,8 @@ def main():
     }
     if not args.no_backward:
         out["backward_16b"] = backward_regime(torch, moe, hip, args, cfg, inp, layer)
-        out["backward_16b"]["train_step_ms"] = round(ms + out["backward_16b"]["ms_per_step"], 4)
+        out["backward_16b_saved"] = backward_regime(torch, moe, hip, args, cfg, inp, layer,
+                                                    saved=True)
     del layer
     if not args.no_decode:
         out["decode_64tok"] = decode_regime(torch, moe, hip, args, inp, sets)

@@ -82,11 +82,16 @@ typedef struct moe_problem {
  * a term for component checks.  MOE_PACKED_WEIGHTS (moe_layer_fwd, moe_grouped_ffn):
  * every expert weight tensor is in the packed layout of moe_pack_weights
  * instead of row-major; bf16 only. */
-enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2, MOE_PACKED_WEIGHTS = 4 };
+enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2, MOE_PACKED_WEIGHTS = 4, MOE_SAVE_FOR_BACKWARD = 8 };
 
 /* Bytes of workspace that suffice for every entry point on this problem;
  * 0 when the problem is invalid. */
 size_t moe_workspace_bytes(const moe_problem *p);
+
+/* Bytes of workspace for moe_layer_fwd with MOE_SAVE_FOR_BACKWARD: the above
+ * plus the kept pre-activations, (T*k + T*K_s) * 2 * d_ff bf16 values; 0 when
+ * the problem is invalid or not bf16. */
+size_t moe_train_workspace_bytes(const moe_problem *p);
 
 /*
  * Router ("Routing in a classic MoE layer" and "Top-k routing, from
@@ -161,7 +166,12 @@ moe_status moe_combine(const moe_problem *p, const void *residual, const void *s
  *   topk_idx, topk_gate, counts, f, P                 out, as moe_route
  *   flags             MOE_NO_RESIDUAL drops +u, MOE_NO_SHARED drops the shared
  *                     experts (component checks only); MOE_PACKED_WEIGHTS: all
- *                     six weight tensors come from moe_pack_weights
+ *                     six weight tensors come from moe_pack_weights;
+ *                     MOE_SAVE_FOR_BACKWARD (bf16): the workspace, of
+ *                     moe_train_workspace_bytes(p) bytes, also keeps the
+ *                     up projection's pre-activations W1 x and W3 x, and
+ *                     keeps the grouping, for moe_layer_bwd (which then
+ *                     skips computing them again); h is the same either way
  */
 moe_status moe_layer_fwd(const moe_problem *p, const void *u, const void *centroids,
                          const void *w1, const void *w3, const void *w2, const void *ws1,
@@ -223,6 +233,11 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  *   topk_idx [T][k], topk_gate [T][k], f [n]  the forward's routing outputs
  *                     (an expert id outside [0, n) breaks the contract; such a
  *                     slot is skipped, as moe_permute leaves it out)
+ *   fwd_ws            the workspace of the forward call that produced them, if
+ *                     that call had MOE_SAVE_FOR_BACKWARD (with nothing run on
+ *                     that workspace since); flags must then include
+ *                     MOE_SAVE_FOR_BACKWARD too.  NULL otherwise: a and b and
+ *                     the grouping are computed again
  *   dh [T][d]         upstream gradient (bf16)
  *   alpha             balance-loss coefficient (0: no balance term)
  *   du [T][d], dcentroids [n][d]              out, fp32
@@ -231,7 +246,8 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  *   dws1, dws3 [K_s*d_ff][d], dws2 [d][K_s*d_ff]   out, fp32; NULL allowed
  *                     when K_s = 0 or flags has MOE_NO_SHARED
  *   flags             MOE_NO_RESIDUAL / MOE_NO_SHARED as moe_layer_fwd (the
- *                     forward must have used the same flags); MOE_PACKED_WEIGHTS
+ *                     forward must have used the same flags); MOE_PACKED_WEIGHTS;
+ *                     MOE_SAVE_FOR_BACKWARD exactly when fwd_ws is given
  *   ws                workspace of at least moe_bwd_workspace_bytes(p) bytes
  * Intermediates (the SwiGLU gradients, q = W2^T dh, the experts' input
  * gradients, the router's softmax gradient) are rounded to bf16; every
@@ -241,7 +257,8 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
 moe_status moe_layer_bwd(const moe_problem *p, const void *u, const void *centroids,
                          const void *w1, const void *w3, const void *w2, const void *ws1,
                          const void *ws3, const void *ws2, const int32_t *topk_idx,
-                         const float *topk_gate, const float *f, const void *dh, float alpha,
+                         const float *topk_gate, const float *f, const void *fwd_ws,
+                         const void *dh, float alpha,
                          float *du, float *dcentroids, float *dw1, float *dw3, float *dw2,
                          float *dws1, float *dws3, float *dws2, int flags, void *ws,
                          size_t ws_bytes, void *stream);
@@ -256,7 +273,8 @@ moe_status moe_layer_bwd_marked(const moe_problem *p, const void *u, const void 
                                 const void *w1, const void *w3, const void *w2,
                                 const void *ws1, const void *ws3, const void *ws2,
                                 const int32_t *topk_idx, const float *topk_gate, const float *f,
-                                const void *dh, float alpha, float *du, float *dcentroids,
+                                const void *fwd_ws, const void *dh, float alpha, float *du,
+                                float *dcentroids,
                                 float *dw1, float *dw3, float *dw2, float *dws1, float *dws3,
                                 float *dws2, int flags, void *ws, size_t ws_bytes, void *stream,
                                 void *const *marks);

@@ -13,7 +13,8 @@ _EXPORTS = ("MOE_BF16", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_NO_RE
             "moe_grouped_ffn", "moe_layer_fwd", "moe_layer_fwd_marked", "moe_layer_kernels",
             "moe_last_hip_error", "moe_pack_weights", "moe_permute", "moe_problem", "moe_route",
             "moe_status_str", "moe_workspace_bytes", "problem", "moe_layer_bwd",
-            "moe_layer_bwd_marked", "moe_layer_bwd_kernels", "moe_bwd_workspace_bytes")
+            "moe_layer_bwd_marked", "moe_layer_bwd_kernels", "moe_bwd_workspace_bytes",
+            "moe_train_workspace_bytes", "MOE_SAVE_FOR_BACKWARD")
 __all__ = list(_EXPORTS)
 
 

@@ -19,7 +19,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_UNSUPPORTED",
                 7: "MOE_ERR_HIP"}
 MOE_F32, MOE_BF16 = 0, 1
-MOE_NO_RESIDUAL, MOE_NO_SHARED, MOE_PACKED_WEIGHTS = 1, 2, 4
+MOE_NO_RESIDUAL, MOE_NO_SHARED, MOE_PACKED_WEIGHTS, MOE_SAVE_FOR_BACKWARD = 1, 2, 4, 8
 MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 64
 
 
@@ -82,7 +82,9 @@ def _load():
     lib.moe_layer_kernels.restype = ctypes.c_int
     lib.moe_bwd_workspace_bytes.argtypes = [PP]
     lib.moe_bwd_workspace_bytes.restype = sz
-    lib.moe_layer_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+    lib.moe_train_workspace_bytes.argtypes = [PP]
+    lib.moe_train_workspace_bytes.restype = sz
+    lib.moe_layer_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                   P, P, P, P, P, P, P, P, ctypes.c_int, P, sz, P]
     lib.moe_layer_bwd.restype = st
     lib.moe_layer_bwd_marked.argtypes = lib.moe_layer_bwd.argtypes + [P]
@@ -210,24 +212,30 @@ def moe_bwd_workspace_bytes(p: moe_problem) -> int:
     return int(lib.moe_bwd_workspace_bytes(ctypes.byref(p)))
 
 
-def moe_layer_bwd(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, dh, alpha,
-                  du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags, ws, ws_bytes=None,
+def moe_train_workspace_bytes(p: moe_problem) -> int:
+    return int(lib.moe_train_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_layer_bwd(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, fwd_ws, dh,
+                  alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags, ws, ws_bytes=None,
                   stream=None):
     _check("moe_layer_bwd", lib.moe_layer_bwd(
         ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
-        _ptr(ws3), _ptr(ws2), _ptr(topk_idx), _ptr(topk_gate), _ptr(f), _ptr(dh), float(alpha),
+        _ptr(ws3), _ptr(ws2), _ptr(topk_idx), _ptr(topk_gate), _ptr(f), _ptr(fwd_ws), _ptr(dh),
+        float(alpha),
         _ptr(du), _ptr(dcentroids), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3),
         _ptr(dws2), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
 
 
-def moe_layer_bwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, dh,
-                         alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags, ws, marks,
-                         ws_bytes=None, stream=None):
+def moe_layer_bwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f,
+                         fwd_ws, dh, alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags,
+                         ws, marks, ws_bytes=None, stream=None):
     """marks: sequence of hipEvent_t handles (ints), len >= kernels + 1."""
     arr = None if marks is None else (ctypes.c_void_p * len(marks))(*marks)
     _check("moe_layer_bwd_marked", lib.moe_layer_bwd_marked(
         ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
-        _ptr(ws3), _ptr(ws2), _ptr(topk_idx), _ptr(topk_gate), _ptr(f), _ptr(dh), float(alpha),
+        _ptr(ws3), _ptr(ws2), _ptr(topk_idx), _ptr(topk_gate), _ptr(f), _ptr(fwd_ws), _ptr(dh),
+        float(alpha),
         _ptr(du), _ptr(dcentroids), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3),
         _ptr(dws2), flags, _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream), arr))
 

@@ -55,6 +55,10 @@ struct Layout {
   size_t t_row0, t_rows, t_off, t_count, lg;
   size_t hbuf, ybuf, hsbuf, sbuf;
   size_t total;
+  // kept for the backward (MOE_SAVE_FOR_BACKWARD): pre-activations W1 x | W3 x
+  // of the routed rows [T*k][2 d_ff] and of the shared experts [T][2 K_s d_ff]
+  size_t pre, pres;
+  size_t total_train;
   int max_tiles;
   size_t hcap;  // elements of hbuf
 };
@@ -92,6 +96,9 @@ Layout layout(const Dims& d) {
   L.hsbuf = take(hs_el * d.esize);
   L.sbuf = take((size_t)d.T * d.d * d.esize);
   L.total = o;
+  L.pre = take(R * 2 * d.d_ff * 2);
+  L.pres = take(hs_el * 2 * 2);
+  L.total_train = o;
   return L;
 }
 
@@ -207,6 +214,12 @@ size_t moe_workspace_bytes(const moe_problem* p) {
   Dims d;
   if (check_problem(p, &d) != MOE_OK) return 0;
   return layout(d).total;
+}
+
+size_t moe_train_workspace_bytes(const moe_problem* p) {
+  Dims d;
+  if (check_problem(p, &d) != MOE_OK || p->dtype != MOE_BF16) return 0;
+  return layout(d).total_train;
 }
 
 const char* moe_status_str(moe_status s) {
@@ -402,10 +415,12 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
-  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS)) return MOE_ERR_SHAPE;
+  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS | MOE_SAVE_FOR_BACKWARD))
+    return MOE_ERR_SHAPE;
   const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
   const bool packed = (flags & MOE_PACKED_WEIGHTS) != 0;
-  if (packed && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool save = (flags & MOE_SAVE_FOR_BACKWARD) != 0;
+  if ((packed || save) && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!u || !centroids || !w1 || !w3 || !w2 || !h || !topk_idx || !topk_gate || !counts || !f ||
       !P)
     return MOE_ERR_NULL;
@@ -417,13 +432,15 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   if (shared && (!aligned(ws1) || !aligned(ws3) || !aligned(ws2))) return MOE_ERR_ALIGN;
   const Layout L = layout(d);
   if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  if (save && ws_bytes < L.total_train) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe::TileList tl = tiles_of(ws, L);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm_token = at<int32_t>(ws, L.perm_token);
   int32_t* slot_of = at<int32_t>(ws, L.slot_of);
-  // Few rows per expert: the weight-streaming FFN.
-  const bool skinny = d.T <= 64 && use_skinny(packed, d.T * d.k, d.n);
+  // Few rows per expert: the weight-streaming FFN (which keeps no
+  // pre-activations, so a forward saving for the backward tiles instead).
+  const bool skinny = !save && d.T <= 64 && use_skinny(packed, d.T * d.k, d.n);
   int mark_i = 0;
   auto mark = [&]() -> hipError_t {
     if (!marks) return hipSuccess;
@@ -482,6 +499,7 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   a.hbuf = at<char>(ws, L.hbuf);
   a.y = at<char>(ws, L.ybuf);
   a.packed = packed;
+  a.preact = save ? at<char>(ws, L.pre) : nullptr;
   void* sbuf = nullptr;
   int nseg = 1;
   if (shared) {
@@ -502,6 +520,7 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
     b.hbuf = at<char>(ws, L.hsbuf);
     b.y = at<char>(ws, L.sbuf);
     b.packed = packed;
+    b.preact = save ? at<char>(ws, L.pres) : nullptr;
     sbuf = b.y;
     nseg = 2;
   }
@@ -534,11 +553,15 @@ size_t moe_bwd_workspace_bytes(const moe_problem* p) {
 int moe_layer_bwd_kernels(const moe_problem* p, int flags, const char** names, int max_names) {
   Dims d;
   if (check_problem(p, &d) != MOE_OK) return -1;
-  (void)flags;
-  static const char* seq[] = {"hist",        "scan", "scatter", "gather",  "logits",
-                              "q",           "ab_swiglu", "dx", "softmax_bwd", "du",
-                              "wgrad",       "dcent_sum"};
-  const int c = (int)(sizeof(seq) / sizeof(seq[0]));
+  static const char* recompute[] = {"hist", "scan",        "scatter", "gather", "logits",
+                                    "q",    "ab_swiglu",   "dx",      "softmax_bwd", "du",
+                                    "wgrad", "dcent_sum"};
+  // with the forward's saved grouping and pre-activations
+  static const char* saved[] = {"gather", "logits", "q", "swiglu_bwd", "dx", "softmax_bwd",
+                                "du", "wgrad", "dcent_sum"};
+  const bool sv = (flags & MOE_SAVE_FOR_BACKWARD) != 0;
+  const char** seq = sv ? saved : recompute;
+  const int c = sv ? 9 : 12;
   for (int i = 0; names && i < c && i < max_names; ++i) names[i] = seq[i];
   return c;
 }
@@ -547,15 +570,20 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
                                 const void* w1, const void* w3, const void* w2,
                                 const void* ws1, const void* ws3, const void* ws2,
                                 const int32_t* topk_idx, const float* topk_gate, const float* f,
-                                const void* dh, float alpha, float* du, float* dcentroids,
-                                float* dw1, float* dw3, float* dw2, float* dws1, float* dws3,
-                                float* dws2, int flags, void* ws, size_t ws_bytes, void* stream,
-                                void* const* marks) {
+                                const void* fwd_ws, const void* dh, float alpha, float* du,
+                                float* dcentroids, float* dw1, float* dw3, float* dw2,
+                                float* dws1, float* dws3, float* dws2, int flags, void* ws,
+                                size_t ws_bytes, void* stream, void* const* marks) {
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
-  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS)) return MOE_ERR_SHAPE;
+  if (flags & ~(MOE_NO_RESIDUAL | MOE_NO_SHARED | MOE_PACKED_WEIGHTS | MOE_SAVE_FOR_BACKWARD))
+    return MOE_ERR_SHAPE;
   if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // the forward's saved grouping and pre-activations: flag and pointer together
+  const bool saved = (flags & MOE_SAVE_FOR_BACKWARD) != 0;
+  if (saved != (fwd_ws != nullptr)) return saved ? MOE_ERR_NULL : MOE_ERR_SHAPE;
+  if (fwd_ws && !aligned(fwd_ws)) return MOE_ERR_ALIGN;
   const bool shared = d.K_s > 0 && !(flags & MOE_NO_SHARED);
   // packed weights: the layout of moe_pack_weights, read by the same kernels
   const bool packed = (flags & MOE_PACKED_WEIGHTS) != 0;
@@ -580,23 +608,29 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     return hipEventRecord(static_cast<hipEvent_t>(marks[mark_i++]), s);
   };
   const int fs = d.K_s * d.d_ff;
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* perm = at<int32_t>(ws, L.perm_token);
-  int32_t* slot_of = at<int32_t>(ws, L.slot_of);
-  const moe::TileList tl{at<int32_t>(ws, L.t_row0), at<int32_t>(ws, L.t_rows),
-                         at<int32_t>(ws, L.t_off), at<int32_t>(ws, L.t_count), L.max_tiles};
+  // The grouping: the forward's (in its workspace) when it saved for the
+  // backward, else rebuilt from topk_idx (stable counting sort by expert).
+  void* gws = saved ? const_cast<void*>(fwd_ws) : ws;
+  const Layout FL = layout(d);
+  int32_t* offsets = at<int32_t>(gws, saved ? FL.offsets : L.offsets);
+  int32_t* perm = at<int32_t>(gws, saved ? FL.perm_token : L.perm_token);
+  int32_t* slot_of = at<int32_t>(gws, saved ? FL.slot_of : L.slot_of);
+  const moe::TileList tl =
+      saved ? tiles_of(gws, FL)
+            : moe::TileList{at<int32_t>(ws, L.t_row0), at<int32_t>(ws, L.t_rows),
+                            at<int32_t>(ws, L.t_off), at<int32_t>(ws, L.t_count), L.max_tiles};
   MOE_TRY(mark());
-
-  // Grouping of the forward's routing (stable counting sort by expert).
-  MOE_TRY(moe::launch_hist(topk_idx, d.T, d.n, d.k, at<int32_t>(ws, L.blk_cnt),
-                           at<int32_t>(ws, L.lrank), s));
-  MOE_TRY(mark());
-  MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), nullptr, d.T, d.n, d.k, nullptr, nullptr,
-                           nullptr, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
-  MOE_TRY(mark());
-  MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
-                              d.T, d.n, d.k, perm, slot_of, nullptr, nullptr, 0, s));
-  MOE_TRY(mark());
+  if (!saved) {
+    MOE_TRY(moe::launch_hist(topk_idx, d.T, d.n, d.k, at<int32_t>(ws, L.blk_cnt),
+                             at<int32_t>(ws, L.lrank), s));
+    MOE_TRY(mark());
+    MOE_TRY(moe::launch_scan(at<int32_t>(ws, L.blk_cnt), nullptr, d.T, d.n, d.k, nullptr,
+                             nullptr, nullptr, offsets, at<int32_t>(ws, L.blk_base), &tl, s));
+    MOE_TRY(mark());
+    MOE_TRY(moe::launch_scatter(topk_idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.blk_base),
+                                d.T, d.n, d.k, perm, slot_of, nullptr, nullptr, 0, s));
+    MOE_TRY(mark());
+  }
   float* gperm = at<float>(ws, L.gperm);
   uint16_t* xp = at<uint16_t>(ws, L.xp);
   uint16_t* dhp = at<uint16_t>(ws, L.dhp);
@@ -665,7 +699,8 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   }
   MOE_TRY(mark());
 
-  // a, b again; SwiGLU backward in the epilogue.
+  // SwiGLU backward: from the forward's kept pre-activations, or with a and b
+  // computed again (and the SwiGLU backward in the GEMM's epilogue).
   uint16_t* da = at<uint16_t>(ws, L.da);
   uint16_t* db = at<uint16_t>(ws, L.db);
   uint16_t* gh = at<uint16_t>(ws, L.gh);
@@ -673,44 +708,52 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   uint16_t* dbs = at<uint16_t>(ws, L.dbs);
   uint16_t* ghs = at<uint16_t>(ws, L.ghs);
   float* dgp = at<float>(ws, L.dgp);
-  {
-    moe::BgSeg g[2] = {};
-    rows_seg(g[0]);
-    g[0].A[0] = xp;
-    g[0].lda = d.d;
-    g[0].B[0] = w1;
-    g[0].B2 = w3;
-    g[0].ldb = d.d;
-    g[0].b_gstride = (int64_t)d.d_ff * d.d;
-    g[0].npass = 1;
-    g[0].N = d.d_ff;
-    g[0].K = d.d;
-    g[0].ldc = d.d_ff;
-    g[0].q = q;
-    g[0].gate = gperm;
-    g[0].da = da;
-    g[0].db = db;
-    g[0].gh = gh;
-    g[0].dgp = dgp;
-    g[0].ldgp = L.ldgp;
-    if (shared) {
-      g[1].A[0] = u;
-      g[1].lda = d.d;
-      g[1].B[0] = ws1;
-      g[1].B2 = ws3;
-      g[1].ldb = d.d;
-      g[1].npass = 1;
-      g[1].N = fs;
-      g[1].K = d.d;
-      g[1].rows = d.T;
-      g[1].ldc = fs;
-      g[1].q = qs;
-      g[1].da = das;
-      g[1].db = dbs;
-      g[1].gh = ghs;
+  if (saved) {
+    MOE_TRY(moe::launch_swiglu_bwd(q, at<uint16_t>(gws, FL.pre), gperm, offsets + d.n,
+                                   d.T * d.k, d.d_ff, da, db, gh, dgp, L.ldgp, s));
+    if (shared)
+      MOE_TRY(moe::launch_swiglu_bwd(qs, at<uint16_t>(gws, FL.pres), nullptr, nullptr, d.T, fs,
+                                     das, dbs, ghs, nullptr, 0, s));
+  } else {
+    {
+      moe::BgSeg g[2] = {};
+      rows_seg(g[0]);
+      g[0].A[0] = xp;
+      g[0].lda = d.d;
+      g[0].B[0] = w1;
+      g[0].B2 = w3;
+      g[0].ldb = d.d;
+      g[0].b_gstride = (int64_t)d.d_ff * d.d;
+      g[0].npass = 1;
+      g[0].N = d.d_ff;
+      g[0].K = d.d;
+      g[0].ldc = d.d_ff;
+      g[0].q = q;
+      g[0].gate = gperm;
+      g[0].da = da;
+      g[0].db = db;
+      g[0].gh = gh;
+      g[0].dgp = dgp;
+      g[0].ldgp = L.ldgp;
+      if (shared) {
+        g[1].A[0] = u;
+        g[1].lda = d.d;
+        g[1].B[0] = ws1;
+        g[1].B2 = ws3;
+        g[1].ldb = d.d;
+        g[1].npass = 1;
+        g[1].N = fs;
+        g[1].K = d.d;
+        g[1].rows = d.T;
+        g[1].ldc = fs;
+        g[1].q = qs;
+        g[1].da = das;
+        g[1].db = dbs;
+        g[1].gh = ghs;
+      }
+      MOE_TRY(moe::launch_bg(packed ? moe::BG_SWIGLU_PACKED : moe::BG_SWIGLU, g, shared ? 2 : 1,
+                             s));
     }
-    MOE_TRY(moe::launch_bg(packed ? moe::BG_SWIGLU_PACKED : moe::BG_SWIGLU, g, shared ? 2 : 1,
-                           s));
   }
   MOE_TRY(mark());
 
@@ -833,13 +876,13 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
 moe_status moe_layer_bwd(const moe_problem* p, const void* u, const void* centroids,
                          const void* w1, const void* w3, const void* w2, const void* ws1,
                          const void* ws3, const void* ws2, const int32_t* topk_idx,
-                         const float* topk_gate, const float* f, const void* dh, float alpha,
-                         float* du, float* dcentroids, float* dw1, float* dw3, float* dw2,
-                         float* dws1, float* dws3, float* dws2, int flags, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         const float* topk_gate, const float* f, const void* fwd_ws,
+                         const void* dh, float alpha, float* du, float* dcentroids, float* dw1,
+                         float* dw3, float* dw2, float* dws1, float* dws3, float* dws2, int flags,
+                         void* ws, size_t ws_bytes, void* stream) {
   return moe_layer_bwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f,
-                              dh, alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2, flags,
-                              ws, ws_bytes, stream, nullptr);
+                              fwd_ws, dh, alpha, du, dcentroids, dw1, dw3, dw2, dws1, dws3, dws2,
+                              flags, ws, ws_bytes, stream, nullptr);
 }
 
 }  // extern "C"

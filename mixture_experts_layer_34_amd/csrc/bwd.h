@@ -84,6 +84,16 @@ hipError_t launch_gather_rows(const int32_t* slot_of, const float* topk_gate, co
                               const void* dh, int64_t T, int k, int d, void* xp, void* dhp,
                               float* gperm, hipStream_t s);
 
+// SwiGLU backward from kept pre-activations pre [rows][2F] (a = W1 x in
+// columns 0..F-1, b = W3 x in F..2F-1, bf16) and q [rows][F] (bf16):
+// da = g q b SiLU'(a), db = g q SiLU(a), gh = g SiLU(a) b (bf16 [rows][F]),
+// g = gate[row] (null: 1).  With dgp: per-row partial sums of <q, SiLU(a) b>
+// over 64-column blocks, dgp [rows][ldgp] (blocks beyond F written zero).
+// Rows at or beyond *nrows (when nrows is not null) are left alone.
+hipError_t launch_swiglu_bwd(const uint16_t* q, const uint16_t* pre, const float* gate,
+                             const int32_t* nrows, int64_t rows, int F, uint16_t* da,
+                             uint16_t* db, uint16_t* gh, float* dgp, int ldgp, hipStream_t s);
+
 // Per token: softmax of the logits lg [T][ldl] (fp32), the gate gradients
 // sum_p dgp[slot][p], the balance term alpha f_i / T, and the softmax
 // backward dl = s (ds - <s, ds>) into dl [T][ldl] (bf16, zero padded).

@@ -616,6 +616,66 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args) {
   }
 }
 
+// SwiGLU backward from kept pre-activations: one wave per row, each lane
+// eight consecutive columns per step (eight lanes cover a 64-column block).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ pre,
+    const float* __restrict__ gate, const int32_t* __restrict__ nrows, int64_t rows, int F,
+    uint16_t* __restrict__ da, uint16_t* __restrict__ db, uint16_t* __restrict__ gh,
+    float* __restrict__ dgp, int ldgp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t lim = nrows ? (int64_t)*nrows : rows;
+  if (r >= lim) return;
+  const float g = gate ? gate[r] : 1.0f;
+  const int nch = F / 8;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    float part = 0.0f;
+    if (c < nch) {
+      const int64_t at = r * F + 8 * c;
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(&q[at]);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(&pre[r * 2 * F + 8 * c]);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(&pre[r * 2 * F + F + 8 * c]);
+      float qf[8], af[8], bf[8];
+      unpack4(make_uint2(qv[0], qv[1]), qf);
+      unpack4(make_uint2(qv[2], qv[3]), qf + 4);
+      unpack4(make_uint2(av[0], av[1]), af);
+      unpack4(make_uint2(av[2], av[3]), af + 4);
+      unpack4(make_uint2(bv[0], bv[1]), bf);
+      unpack4(make_uint2(bv[2], bv[3]), bf + 4);
+      float o[3][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float a = af[j], b = bf[j];
+        const float sg = 1.0f / (1.0f + __expf(-a));
+        const float sl = a * sg;
+        const float dsl = sg * (1.0f + a * (1.0f - sg));
+        const float hid = sl * b;
+        o[0][j] = g * qf[j] * b * dsl;
+        o[1][j] = g * qf[j] * sl;
+        o[2][j] = g * hid;
+        part += qf[j] * hid;
+      }
+      uint16_t* dst[3] = {da, db, gh};
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const uint2 lo = pack4(o[w][0], o[w][1], o[w][2], o[w][3]);
+        const uint2 hi = pack4(o[w][4], o[w][5], o[w][6], o[w][7]);
+        *reinterpret_cast<u32x4*>(&dst[w][at]) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+    if (dgp) {
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 4);
+      if ((lane & 7) == 0 && c < nch) dgp[r * ldgp + c / 8] = part;
+    }
+  }
+  if (dgp)
+    for (int b = (F + 63) / 64 + lane; b < ldgp; b += 64) dgp[r * ldgp + b] = 0.0f;
+}
+
 // One wave per token: its u and dh rows go to each of its grouped rows.
 __global__ __launch_bounds__(256) void gather_rows_kernel(
     const int32_t* __restrict__ slot_of, const float* __restrict__ gate,
@@ -780,6 +840,16 @@ hipError_t launch_gather_rows(const int32_t* slot_of, const float* topk_gate, co
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, slot_of,
                      topk_gate, static_cast<const u32x4*>(u), static_cast<const u32x4*>(dh), T,
                      k, d / 8, static_cast<u32x4*>(xp), static_cast<u32x4*>(dhp), gperm);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const uint16_t* q, const uint16_t* pre, const float* gate,
+                             const int32_t* nrows, int64_t rows, int F, uint16_t* da,
+                             uint16_t* db, uint16_t* gh, float* dgp, int ldgp, hipStream_t s) {
+  const int64_t blocks = (rows + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, pre, gate,
+                     nrows, rows, F, da, db, gh, dgp, ldgp);
   return hipGetLastError();
 }
 

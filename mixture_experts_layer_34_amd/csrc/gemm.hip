@@ -61,6 +61,7 @@ struct GemmSeg {
   int N;                  // output columns per group
   uint16_t* C;
   int64_t ldc;
+  uint16_t* P;            // up, nullable: pre-activations [rows][2N] (W1 x | W3 x)
   int nN;                 // column tiles
   const int32_t* tile_row0;
   const int32_t* tile_rows;
@@ -428,45 +429,56 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
   constexpr int CPR = OC / 8;            // 16-byte chunks per row
   uint16_t* stile = &sB[0];
   const int cbase = nt * OC;
+  // what = 0: the output (SwiGLU for the up projection); with g.P (up only),
+  // what = 1, 2 also keep the pre-activations W1 x and W3 x for a backward
+  // pass, at columns cbase and N + cbase of P.
+  const int nwhat = (UP && g.P) ? 3 : 1;
+  for (int what = 0; what < nwhat; ++what) {
+    uint16_t* dst = what == 0 ? g.C : g.P;
+    const int64_t ldd = what == 0 ? g.ldc : 2 * (int64_t)g.N;
+    const int coff = cbase + (what == 2 ? g.N : 0);
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();
 #pragma unroll
-    for (int mh = 0; mh < 2; ++mh) {
-      const int mi = pass * 2 + mh;
-      if (mi >= mblocks) continue;
-      const int tl = mh * 32 + (lane & 31);
+      for (int mh = 0; mh < 2; ++mh) {
+        const int mi = pass * 2 + mh;
+        if (mi >= mblocks) continue;
+        const int tl = mh * 32 + (lane & 31);
 #pragma unroll
-      for (int nb = 0; nb < (UP ? NBW / 2 : NBW); ++nb) {
+        for (int nb = 0; nb < (UP ? NBW / 2 : NBW); ++nb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nr + nb * 32 + 8 * q + 4 * (lane >> 5);
-          float v[4];
+          for (int q = 0; q < 4; ++q) {
+            const int col = nr + nb * 32 + 8 * q + 4 * (lane >> 5);
+            float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = acc[mi][nb][4 * q + e];
-            if (UP) {
-              const float gate = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-              v[e] = gate * acc[mi][nb + NBW / 2][4 * q + e];
-            } else {
-              v[e] = x;
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[mi][nb][4 * q + e];
+              if (UP) {
+                const float y = acc[mi][nb + NBW / 2][4 * q + e];
+                if (what == 0)
+                  v[e] = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * y;
+                else
+                  v[e] = what == 1 ? x : y;
+              } else {
+                v[e] = x;
+              }
             }
+            bf16x4 pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            *reinterpret_cast<bf16x4*>(&stile[tl * LDO + col]) = pk;
           }
-          bf16x4 pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *reinterpret_cast<bf16x4*>(&stile[tl * LDO + col]) = pk;
         }
       }
-    }
-    __syncthreads();
-    for (int c = tid; c < 64 * CPR; c += kThreads) {
-      const int rl = c / CPR, ch = c - rl * CPR;
-      const int r = pass * 64 + rl;
-      const int col = cbase + ch * 8;
-      if (r < rows && col < g.N) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(&stile[rl * LDO + ch * 8]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&stile[rl * LDO + ch * 8 + 4]);
-        *reinterpret_cast<u32x4*>(g.C + ((int64_t)row0 + r) * g.ldc + col) =
-            u32x4{lo.x, lo.y, hi.x, hi.y};
+      __syncthreads();
+      for (int c = tid; c < 64 * CPR; c += kThreads) {
+        const int rl = c / CPR, ch = c - rl * CPR;
+        const int r = pass * 64 + rl;
+        if (r < rows && cbase + ch * 8 < g.N) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(&stile[rl * LDO + ch * 8]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&stile[rl * LDO + ch * 8 + 4]);
+          *reinterpret_cast<u32x4*>(dst + ((int64_t)row0 + r) * ldd + coff + ch * 8) =
+              u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
       }
     }
   }
@@ -540,6 +552,7 @@ static GemmSeg up_seg(const FfnArgs& a) {
   up.N = a.d_ff_g;
   up.C = (uint16_t*)a.hbuf;
   up.ldc = a.d_ff_g;
+  up.P = (uint16_t*)a.preact;
   up.nN = (a.d_ff_g + Tile<NBW>::UPC - 1) / Tile<NBW>::UPC;
   if (a.tiles) {
     up.tile_row0 = a.tiles->row0;

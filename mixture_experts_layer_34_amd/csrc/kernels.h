@@ -87,6 +87,8 @@ struct FfnArgs {
   void* hbuf;              // [rows][d_ff_g] intermediate
   void* y;                 // [rows][d]
   bool packed;             // weights in the packed layout (bf16 only)
+  void* preact;            // nullable: [rows][2 d_ff_g] bf16 W1 x | W3 x kept for the
+                           // backward (tiled bf16 up projection only)
 };
 
 // Packs a [rows][K] bf16 matrix (rows % 32 == 0, K % 16 == 0) into the

@@ -191,10 +191,16 @@ def test_layer_fwd_checks():
     ws = moe.moe_workspace_bytes(p)
     full = [A] * 14
     # bad flag bits
-    assert status(moe.moe_layer_fwd, p, *full, 8, A, ws) == "MOE_ERR_SHAPE"
+    assert status(moe.moe_layer_fwd, p, *full, 16, A, ws) == "MOE_ERR_SHAPE"
     pf = p16(dtype="f32")
-    assert status(moe.moe_layer_fwd, pf, *full, moe.MOE_PACKED_WEIGHTS, A,
-                  moe.moe_workspace_bytes(pf)) == "MOE_ERR_UNSUPPORTED"
+    for fl in (moe.MOE_PACKED_WEIGHTS, moe.MOE_SAVE_FOR_BACKWARD):
+        assert status(moe.moe_layer_fwd, pf, *full, fl, A,
+                      moe.moe_workspace_bytes(pf)) == "MOE_ERR_UNSUPPORTED"
+    # keeping the pre-activations needs the larger workspace
+    wt = moe.moe_train_workspace_bytes(p)
+    assert wt > ws and wt % 256 == 0 and moe.moe_train_workspace_bytes(pf) == 0
+    assert status(moe.moe_layer_fwd, p, *full, moe.MOE_SAVE_FOR_BACKWARD, A,
+                  ws) == "MOE_ERR_WORKSPACE"
     # shared weights required when K_s > 0 ...
     args = list(full)
     args[5] = None
@@ -247,19 +253,26 @@ def test_layer_bwd_checks():
     ws = moe.moe_bwd_workspace_bytes(p)
     assert ws > 0 and ws % 256 == 0
     assert moe.moe_bwd_workspace_bytes(p16(dtype="f32")) == 0
-    # u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, dh
-    ins = [A] * 12
+    # u, centroids, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_gate, f, fwd_ws, dh
+    ins = [A] * 11 + [None, A]
     # du, dcent, dw1, dw3, dw2, dws1, dws3, dws2
     outs = [A] * 8
     call = lambda pp, i, a, o, flags, w: moe.moe_layer_bwd(pp, *i, a, *o, flags, A, w)
     assert status(call, p16(dtype="f32"), ins, 0.0, outs, 0, BIG) == "MOE_ERR_UNSUPPORTED"
     # packed weights are accepted: the same checks apply
     assert status(call, p, ins, 0.0, outs, moe.MOE_PACKED_WEIGHTS, 0) == "MOE_ERR_WORKSPACE"
-    assert status(call, p, ins, 0.0, outs, 8, BIG) == "MOE_ERR_SHAPE"
+    assert status(call, p, ins, 0.0, outs, 16, BIG) == "MOE_ERR_SHAPE"
     assert status(call, p16(T=0), ins, 0.0, outs, 0, BIG) == "MOE_ERR_SHAPE"
-    for i in range(12):
-        if i in (5, 6, 7):
-            continue  # shared weights: checked below
+    # the forward's kept workspace: given exactly when the flag says so
+    sv = moe.MOE_SAVE_FOR_BACKWARD
+    with_fw = ins[:11] + [A, A]
+    assert status(call, p, ins, 0.0, outs, sv, BIG) == "MOE_ERR_NULL"
+    assert status(call, p, with_fw, 0.0, outs, 0, BIG) == "MOE_ERR_SHAPE"
+    assert status(call, p, ins[:11] + [MIS, A], 0.0, outs, sv, BIG) == "MOE_ERR_ALIGN"
+    assert status(call, p, with_fw, 0.0, outs, sv, 0) == "MOE_ERR_WORKSPACE"
+    for i in range(13):
+        if i in (5, 6, 7, 11):
+            continue  # shared weights: checked below; fwd_ws: above
         bad = list(ins)
         bad[i] = None
         assert status(call, p, bad, 0.0, outs, 0, BIG) == "MOE_ERR_NULL", i
@@ -283,3 +296,6 @@ def test_layer_bwd_kernel_sequence():
     assert moe.moe_layer_bwd_kernels(p16()) == [
         "hist", "scan", "scatter", "gather", "logits", "q", "ab_swiglu", "dx", "softmax_bwd",
         "du", "wgrad", "dcent_sum"]
+    # after a forward that kept its grouping and pre-activations
+    assert moe.moe_layer_bwd_kernels(p16(), moe.MOE_SAVE_FOR_BACKWARD) == [
+        "gather", "logits", "q", "swiglu_bwd", "dx", "softmax_bwd", "du", "wgrad", "dcent_sum"]

@@ -66,7 +66,7 @@ def run_bwd(cfg, inp, route, dh, alpha, flags=0):
         out.update(dws1=z(fs, cfg.d), dws3=z(fs, cfg.d), dws2=z(cfg.d, fs))
     ws = torch.empty(moe.moe_bwd_workspace_bytes(p), dtype=torch.uint8, device=d)
     moe.moe_layer_bwd(p, t["u"], t["centroids"], t["w1"], t["w3"], t["w2"], t["ws1"], t["ws3"],
-                      t["ws2"], idx, gate, f, dht, alpha, out["du"], out["dcent"], out["dw1"],
+                      t["ws2"], idx, gate, f, None, dht, alpha, out["du"], out["dcent"], out["dw1"],
                       out["dw3"], out["dw2"], out.get("dws1"), out.get("dws3"), out.get("dws2"),
                       flags, ws)
     torch.cuda.synchronize()
@@ -233,7 +233,7 @@ def test_bwd_graph_replays():
     out = {k: torch.empty(v.shape, dtype=torch.float32, device=d) for k, v in want.items()}
     ws = torch.empty(moe.moe_bwd_workspace_bytes(p), dtype=torch.uint8, device=d)
     call = lambda: moe.moe_layer_bwd(p, t["u"], t["centroids"], t["w1"], t["w3"], t["w2"],
-                                     t["ws1"], t["ws3"], t["ws2"], idx, gate, f, dht, 0.37,
+                                     t["ws1"], t["ws3"], t["ws2"], idx, gate, f, None, dht, 0.37,
                                      out["du"], out["dcent"], out["dw1"], out["dw3"], out["dw2"],
                                      out["dws1"], out["dws3"], out["dws2"], 0, ws)
     side = torch.cuda.Stream()
