@@ -17,6 +17,10 @@ OBJ = os.path.join(ROOT, "_build", "moe")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "skinny.hip", "bwd.hip"]
 ARCH = "gfx950"
+# Per-file flags.  bwd.hip: no wave-level combining of atomics (it would
+# wait for an atomic's reply where it is issued; the weight-gradient kernel
+# takes its reply much later, under a wait it has anyway).
+EXTRA = {"bwd.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
@@ -34,7 +38,7 @@ def flags() -> list[str]:
 
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

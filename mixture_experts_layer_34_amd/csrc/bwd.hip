@@ -477,77 +477,91 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   }
 }
 
-// Workgroup -> (segment, logical tile) in launch order, so consecutive tiles
-// go round-robin over the XCDs.  Used where tiles differ in length (each
-// expert reduces over its own rows): contiguous per-XCD shares would give
-// the XCD holding the most loaded experts most of the work.
-__device__ __forceinline__ bool linear_pick(const BgArgs& a, int& si, int& L) {
-  int i = (int)blockIdx.x;
-  for (int s = 0; s < a.nseg; ++s) {
-    if (i < a.bound[s]) {
-      si = s;
-      L = i;
-      return true;
-    }
-    i -= a.bound[s];
-  }
-  return false;
-}
-
 // Weight gradients (k grouping, both operands K-strided, fp32 out) on
 // 256 x 256 tiles: an expert's K range is only its rows (a few hundred), so
 // a tile reuses each staged slice over four times the output of the
 // 128 x 128 kernel, and each wave's 128 x 128 block (16 accumulator blocks,
 // held in AGPRs) takes two MFMAs per fragment read from LDS.  One workgroup
-// per CU (two LDS buffers of two 256-row tiles).
+// per CU, persistent: it takes tiles in launch order from a counter (zero at
+// launch), so tiles of unequal length (each expert reduces over its own
+// rows) still balance.  The next tile's first slice is loaded during the
+// current tile's last one and staged before its epilogue, so that the
+// epilogue's stores drain while the next tile's MFMAs run: the load counter
+// counts stores too, and a wait for any load issued after them would
+// otherwise wait for them all.  Expert row offsets are read from LDS for
+// the same reason (a global load of them at a tile's start would wait for
+// the previous tile's stores).
 constexpr int WB = 256;
 constexpr int WTILE_EL = WB * LDK + BAND * (WB / 16);
+constexpr int kWgMaxGroups = 256;
 
-__global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args) {
+struct WTile {
+  int si, e, m0, n0, kb, ke, nk;
+};
+
+// Logical tile t (launch order: segment by segment) -> its coordinates;
+// koff[] holds the one row-offset table the launch's segments share.
+__device__ __forceinline__ WTile wtile_of(const BgArgs& a, const int* koff, int t) {
+  WTile w{};
+  int s = 0;
+  while (s + 1 < a.nseg && t >= a.bound[s]) {
+    t -= a.bound[s];
+    ++s;
+  }
+  const BgSeg& g = a.seg[s];
+  const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
+  w.si = s;
+  w.e = t / (nM * nN);
+  const int r = t - w.e * nM * nN;
+  const int nt = r / nM, mt = r - nt * nM;
+  w.m0 = mt * WB;
+  w.n0 = nt * WB;
+  if (g.koff) {
+    w.kb = koff[w.e];
+    w.ke = koff[w.e + 1];
+  } else {
+    w.kb = w.e * g.kchunk;
+    w.ke = w.kb + g.kchunk < g.K ? w.kb + g.kchunk : g.K;
+  }
+  w.nk = w.ke > w.kb ? (w.ke - w.kb + BK - 1) / BK : 0;
+  return w;
+}
+
+__global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args, int* __restrict__ ctr,
+                                                      int total, int nwg) {
+  // two slice buffers per operand; buffer 1 also stages the epilogue
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][WTILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][WTILE_EL];
+  __shared__ int s_koff[kWgMaxGroups + 1];
+  __shared__ int s_next[2];
 
-  int si = 0, L = 0;
-  if (!linear_pick(args, si, L)) return;
-  const BgSeg& g = args.seg[si];
-  const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
-  const int e = L / (nM * nN);
-  const int r = L - e * nM * nN;
-  const int nt = r / nM, mt = r - nt * nM;
-  const int m0 = mt * WB, n0 = nt * WB;
-  int kb, ke;
-  if (g.koff) {
-    kb = g.koff[e];
-    ke = g.koff[e + 1];
-  } else {
-    kb = e * g.kchunk;
-    ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
-  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[nb][mb][j] = 0.0f;
   int fa[4], fb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     fa[i] = rb(wm * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
     fb[i] = rb(wn * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
   }
+  {
+    const int32_t* koff = nullptr;
+    int ng = 0;
+    for (int s = 0; s < args.nseg; ++s)
+      if (args.seg[s].koff) {
+        koff = args.seg[s].koff;
+        ng = args.seg[s].G;
+      }
+    for (int i = tid; koff && i <= ng; i += NT) s_koff[i] = koff[i];
+  }
 
-  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
   u32x4 ra[2][4], rbv[2][4];
-  auto load = [&](int kt) {
-    const int k0 = kb + kt * BK;
+  auto load = [&](const WTile& w, int kt) {
+    const BgSeg& g = args.seg[w.si];
+    const int k0 = w.kb + kt * BK;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ks_load(ra[h], g.A[0], g.lda, k0, ke, m0 + 128 * h, g.a_lim, tid);
-      ks_load(rbv[h], g.B[0], g.ldb, k0, ke, n0 + 128 * h, g.b_lim, tid);
+      ks_load(ra[h], g.A[0], g.lda, k0, w.ke, w.m0 + 128 * h, g.a_lim, tid);
+      ks_load(rbv[h], g.B[0], g.ldb, k0, w.ke, w.n0 + 128 * h, g.b_lim, tid);
     }
   };
   auto store = [&](int b) {
@@ -557,62 +571,110 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args) {
       ks_store(sB[b], rbv[h], tid, 128 * h);
     }
   };
-  if (nk > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int b = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] + kk * 16]);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] + kk * 16]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store(b ^ 1);
-    __syncthreads();
-  }
 
-  // Epilogue through LDS, 32 rows of the wave's block at a time: the
-  // accumulator layout puts one row per lane, so direct stores would send
-  // 32-byte pieces of 32 rows per instruction; staged, each store
-  // instruction writes two whole 512-byte rows.
-  constexpr int SP = 128 + 4;  // staging row pitch (floats)
-  float* stage = reinterpret_cast<float*>(&sA[0][0]) + wave * 32 * SP;
-  float* C = static_cast<float*>(g.C) + (int64_t)e * g.c_gstride;
-  const int mrow0 = m0 + wm * 128, ncol0 = n0 + wn * 128;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  // Tile j of this workgroup finds tile j + 1's index in s_next[(j + 1) & 1]
+  // and fetches tile j + 2's into s_next[j & 1].
+  if (tid == 0) s_next[1] = nwg + atomicAdd(ctr, 1);
+  __syncthreads();
+  WTile w = wtile_of(args, s_koff, (int)blockIdx.x);
+  load(w, 0);
+  store(0);
+  __syncthreads();
+  for (int j = 0;; ++j) {
+    const int nxt = s_next[(j + 1) & 1];
+    const bool more = nxt < total;
+    // The counter's reply is first used after this tile's K loop, where the
+    // wave waits for its loads anyway (the library builds this file without
+    // the compiler's wave-level atomic combining, which would wait here).
+    int fetched;
+    if (tid == 0 && more) fetched = atomicAdd(ctr, 1);
+    WTile w2{};
+    if (more) w2 = wtile_of(args, s_koff, nxt);
+
+    f32x16 acc[4][4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x16& a = acc[nb][mb];
-        *reinterpret_cast<float4*>(&stage[(lane & 31) * SP + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
-            make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-      }
-    __syncthreads();
-    const int c = ncol0 + 4 * (lane & 31);
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 2 * i + (lane >> 5);
-      const int m = mrow0 + mb * 32 + row;
-      if (m < g.M && c < g.N)
-        *reinterpret_cast<float4*>(&C[(int64_t)m * g.ldc + c]) =
-            *reinterpret_cast<const float4*>(&stage[row * SP + 4 * (lane & 31)]);
+        for (int q = 0; q < 16; ++q) acc[nb][mb][q] = 0.0f;
+
+    auto slice = [&](int b) {
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] + kk * 16]);
+          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] + kk * 16]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            acc[nb][mb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+      }
+    };
+    // (the last slice is peeled off, so that the loop's loads are
+    // unconditional and no wait at its head covers the previous stores)
+    int kt = 0;
+    for (; kt + 1 < w.nk; ++kt) {
+      load(w, kt + 1);
+      slice(kt & 1);
+      store((kt & 1) ^ 1);
+      __syncthreads();
     }
+    // The last slice, with the next tile's first slice in flight; that slice
+    // then goes to buffer 0 (free: the last reads ended at the barrier).
+    // Loaded and stored unconditionally (an empty range loads nothing and
+    // stores zeros nobody reads): a load under one branch and its use under
+    // another make the compiler assume a load still pending, and wait for
+    // the epilogue's stores before the next tile's first load.
+    load(w2, 0);
+    if (w.nk > 0) slice(kt & 1);
     __syncthreads();
+    store(0);
+    if (tid == 0 && more) s_next[j & 1] = nwg + fetched;
+
+    // Epilogue through LDS buffer 1, 32 rows of the wave's block at a time:
+    // the accumulator layout puts one row per lane, so direct stores would
+    // send 32-byte pieces of 32 rows per instruction; staged, each store
+    // instruction writes two whole 512-byte rows.
+    {
+      const BgSeg& g = args.seg[w.si];
+      constexpr int SP = 128 + 4;  // staging row pitch (floats)
+      static_assert(2 * 32 * SP * 4 <= WTILE_EL * 2, "two waves' staging per buffer");
+      float* stage = reinterpret_cast<float*>(wave < 2 ? &sA[1][0] : &sB[1][0]) +
+                     (wave & 1) * 32 * SP;
+      float* C = static_cast<float*>(g.C) + (int64_t)w.e * g.c_gstride;
+      const int mrow0 = w.m0 + wm * 128, ncol0 = w.n0 + wn * 128;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[nb][mb];
+            *reinterpret_cast<float4*>(
+                &stage[(lane & 31) * SP + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          }
+        __syncthreads();
+        const int c = ncol0 + 4 * (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 2 * i + (lane >> 5);
+          const int m = mrow0 + mb * 32 + row;
+          if (m < g.M && c < g.N)
+            *reinterpret_cast<float4*>(&C[(int64_t)m * g.ldc + c]) =
+                *reinterpret_cast<const float4*>(&stage[row * SP + 4 * (lane & 31)]);
+        }
+        __syncthreads();
+      }
+    }
+    if (!more) break;
+    w = w2;
   }
 }
 
@@ -680,9 +742,11 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
 __global__ __launch_bounds__(256) void gather_rows_kernel(
     const int32_t* __restrict__ slot_of, const float* __restrict__ gate,
     const u32x4* __restrict__ u, const u32x4* __restrict__ dh, int64_t T, int k, int nch,
-    u32x4* __restrict__ xp, u32x4* __restrict__ dhp, float* __restrict__ gperm) {
+    u32x4* __restrict__ xp, u32x4* __restrict__ dhp, float* __restrict__ gperm,
+    int* __restrict__ clear) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (clear && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0;
   if (t >= T) return;
   // slot_of is -1 for an expert id outside [0, n) (the grouping leaves such
   // slots out); they are skipped here and in the kernels below.
@@ -800,6 +864,25 @@ int seg_blocks(BgKind kind, const BgSeg& g) {
   return (int)((g.rows + BM - 1) / BM) * nN;
 }
 
+// Compute units of the current device (one persistent weight-gradient
+// workgroup each), looked up once per device.
+hipError_t cu_count(int* out) {
+  static int cached[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cached[dev] == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (v <= 0) return hipErrorInvalidDevice;
+    cached[dev] = v;
+  }
+  *out = cached[dev];
+  return hipSuccess;
+}
+
 template <bool BKS, int EPI, bool DUAL, bool PK = false>
 hipError_t launch_t(const BgArgs& args, int grid, hipStream_t s) {
   hipLaunchKernelGGL((bg_kernel<BKS, EPI, DUAL, PK>), dim3(grid), dim3(NT), 0, s, args);
@@ -808,17 +891,34 @@ hipError_t launch_t(const BgArgs& args, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
+hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s, int* work_ctr) {
   if (nseg < 1 || nseg > kBgMaxSeg) return hipErrorInvalidValue;
   BgArgs args{};
   args.nseg = nseg;
-  int grid = 0;
+  int grid = 0, total = 0;
   for (int i = 0; i < nseg; ++i) {
     args.seg[i] = segs[i];
     args.bound[i] = seg_blocks(kind, segs[i]);
     grid += 8 * ((args.bound[i] + 7) / 8);  // each XCD's share of segment i
+    total += args.bound[i];
   }
   if (grid == 0) return hipSuccess;
+  if (kind == BG_WGRAD) {
+    if (!work_ctr) return hipErrorInvalidValue;
+    // the segments with a row-offset table share one of at most 256 groups
+    const int32_t* koff = nullptr;
+    for (int i = 0; i < nseg; ++i) {
+      if (!segs[i].koff) continue;
+      if ((koff && segs[i].koff != koff) || segs[i].G > kWgMaxGroups) return hipErrorInvalidValue;
+      koff = segs[i].koff;
+    }
+    int cus = 0;
+    const hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const int nwg = total < cus ? total : cus;
+    hipLaunchKernelGGL(wgrad_kernel, dim3(nwg), dim3(NT), 0, s, args, work_ctr, total, nwg);
+    return hipGetLastError();
+  }
   switch (kind) {
     case BG_LOGITS: return launch_t<false, EPI_F32, false>(args, grid, s);
     case BG_PROJ: return launch_t<true, EPI_BF16, false>(args, grid, s);
@@ -826,20 +926,18 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s) {
     case BG_PROJ_PACKED: return launch_t<true, EPI_BF16, false, true>(args, grid, s);
     case BG_SWIGLU_PACKED: return launch_t<false, EPI_SWIGLU, true, true>(args, grid, s);
     case BG_DU: return launch_t<true, EPI_DU, false>(args, grid, s);
-    case BG_WGRAD:
-      hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(NT), 0, s, args);
-      return hipGetLastError();
+    case BG_WGRAD: break;  // above
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gather_rows(const int32_t* slot_of, const float* topk_gate, const void* u,
                               const void* dh, int64_t T, int k, int d, void* xp, void* dhp,
-                              float* gperm, hipStream_t s) {
+                              float* gperm, int* clear, hipStream_t s) {
   const int64_t blocks = (T + 3) / 4;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, slot_of,
                      topk_gate, static_cast<const u32x4*>(u), static_cast<const u32x4*>(dh), T,
-                     k, d / 8, static_cast<u32x4*>(xp), static_cast<u32x4*>(dhp), gperm);
+                     k, d / 8, static_cast<u32x4*>(xp), static_cast<u32x4*>(dhp), gperm, clear);
   return hipGetLastError();
 }
 
