@@ -152,7 +152,7 @@ struct BwdLayout {
   size_t gperm, xp, dhp, q, da, db, gh, dgp, dxp;
   size_t qs, das, dbs, ghs, dxs;
   size_t lg, dl, slabs;
-  size_t wctr;  // the weight-gradient kernel's work counter
+  size_t wctr;  // the weight-gradient kernel's work queues
   size_t total;
   int max_tiles, ldl, ldgp, kchunk, G;
 };
@@ -186,7 +186,7 @@ BwdLayout bwd_layout(const Dims& d) {
   L.t_rows = take((size_t)L.max_tiles * 4);
   L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
   L.t_count = take(4);
-  L.wctr = take(4);
+  L.wctr = take(moe::kWgQueues * 4);
   L.gperm = take(R * 4);
   L.xp = take(R * d.d * 2);
   L.dhp = take(R * d.d * 2);
@@ -636,7 +636,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
   float* gperm = at<float>(ws, L.gperm);
   uint16_t* xp = at<uint16_t>(ws, L.xp);
   uint16_t* dhp = at<uint16_t>(ws, L.dhp);
-  // (also zeroes the weight-gradient launch's work counter)
+  // (also zeroes the weight-gradient launch's work queues)
   int32_t* wctr = at<int32_t>(ws, L.wctr);
   MOE_TRY(moe::launch_gather_rows(slot_of, topk_gate, u, dh, d.T, d.k, d.d, xp, dhp, gperm, wctr,
                                   s));

@@ -75,15 +75,17 @@ enum BgKind {
   BG_SWIGLU_PACKED = 6  // BG_SWIGLU with B and B2 packed
 };
 
-// BG_WGRAD takes work_ctr: an int in device memory that is zero when the
-// launch starts (its workgroups take tiles from it; it is left nonzero).
+// BG_WGRAD takes work_ctr: kWgQueues ints in device memory, zero when the
+// launch starts (the workgroups' tile queues; they are left nonzero).
+constexpr int kWgQueues = 8;
 hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s,
                      int* work_ctr = nullptr);
 
 // Rows of u and dh in grouped order and the gate of each grouped row:
 // xp[slot_of[t][j]] = u[t], dhp[slot_of[t][j]] = dh[t],
 // gperm[slot_of[t][j]] = topk_gate[t][j]  (bf16 rows of d elements); also
-// sets *clear = 0 when clear is not null (a later launch's work counter).
+// zeroes clear[0 .. kWgQueues-1] when clear is not null (a later BG_WGRAD
+// launch's queues).
 hipError_t launch_gather_rows(const int32_t* slot_of, const float* topk_gate, const void* u,
                               const void* dh, int64_t T, int k, int d, void* xp, void* dhp,
                               float* gperm, int* clear, hipStream_t s);

@@ -482,32 +482,111 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 // a tile reuses each staged slice over four times the output of the
 // 128 x 128 kernel, and each wave's 128 x 128 block (16 accumulator blocks,
 // held in AGPRs) takes two MFMAs per fragment read from LDS.  One workgroup
-// per CU, persistent: it takes tiles in launch order from a counter (zero at
-// launch), so tiles of unequal length (each expert reduces over its own
-// rows) still balance.  The next tile's first slice is loaded during the
-// current tile's last one and staged before its epilogue, so that the
-// epilogue's stores drain while the next tile's MFMAs run: the load counter
-// counts stores too, and a wait for any load issued after them would
-// otherwise wait for them all.  Expert row offsets are read from LDS for
-// the same reason (a global load of them at a tile's start would wait for
-// the previous tile's stores).
+// per CU, persistent, taking tiles from work queues.
+//
+// Queues: one per XCD (workgroup b runs on XCD b % 8).  XCD x's queue holds
+// the experts e = x, x + 8, ... of the segments with a row-offset table
+// (all their tiles, expert by expert, so the tiles that read one expert's
+// rows meet in one L2) and an eighth of every other segment's tiles, in
+// segment order otherwise.  A workgroup whose queue is empty takes tiles
+// from the other queues, so tiles of unequal length (each expert reduces
+// over its own rows) still balance.
+//
+// The next tile's first slice is loaded during the current tile's last one
+// and staged before its epilogue, so that the epilogue's stores drain while
+// the next tile's MFMAs run: the load counter counts stores too, and a wait
+// for any load issued after them would otherwise wait for them all.  Expert
+// row offsets are read from LDS for the same reason (a global load of them
+// at a tile's start would wait for the previous tile's stores).
 constexpr int WB = 256;
 constexpr int WTILE_EL = WB * LDK + BAND * (WB / 16);
 constexpr int kWgMaxGroups = 256;
+constexpr int kXcds = kWgQueues;
+// Buffer resource word 3 for raw 32-bit accesses on gfx9, and an offset
+// past any output (outputs stay below 2 GiB).
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufDrop = 0x7ffffff0;
 
 struct WTile {
   int si, e, m0, n0, kb, ke, nk;
 };
 
-// Logical tile t (launch order: segment by segment) -> its coordinates;
-// koff[] holds the one row-offset table the launch's segments share.
-__device__ __forceinline__ WTile wtile_of(const BgArgs& a, const int* koff, int t) {
-  WTile w{};
-  int s = 0;
-  while (s + 1 < a.nseg && t >= a.bound[s]) {
-    t -= a.bound[s];
-    ++s;
+__device__ __forceinline__ int wg_tiles(const BgSeg& g) {
+  return ((g.M + WB - 1) / WB) * ((g.N + WB - 1) / WB);  // per group
+}
+
+// Segments [k0, k1) carry the row-offset table (contiguous, same G; k0 = k1
+// when none does).
+struct WQueues {
+  int k0, k1, per_e;  // per_e: tiles of one expert over those segments
+};
+
+__device__ __forceinline__ WQueues wqueues(const BgArgs& a) {
+  WQueues q{a.nseg, a.nseg, 0};
+  bool found = false;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].koff) {
+      if (!found) q.k0 = s;
+      found = true;
+      q.k1 = s + 1;
+      q.per_e += wg_tiles(a.seg[s]);
+    }
+  return q;
+}
+
+// Tiles in XCD x's queue.
+__device__ __forceinline__ int wq_count(const BgArgs& a, const WQueues& q, int x) {
+  int c = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    if (s >= q.k0 && s < q.k1) continue;
+    const int S = a.bound[s];
+    c += (x + 1) * S / kXcds - x * S / kXcds;
   }
+  if (q.k1 > q.k0) {
+    const int G = a.seg[q.k0].G;
+    c += (G > x ? (G - x + kXcds - 1) / kXcds : 0) * q.per_e;
+  }
+  return c;
+}
+
+// Entry i of XCD x's queue -> segment s and tile t within it (tile t of a
+// segment: group t / (nM nN), then column tile, then row tile).
+__device__ __forceinline__ void wq_tile(const BgArgs& a, const WQueues& q, int x, int i, int& s,
+                                        int& t) {
+  for (s = 0; s < a.nseg; ++s) {
+    if (s == q.k0 && q.k1 > q.k0) {
+      const int G = a.seg[s].G;
+      const int ne = G > x ? (G - x + kXcds - 1) / kXcds : 0;
+      if (i < ne * q.per_e) {
+        const int e = x + kXcds * (i / q.per_e);
+        int r = i - (i / q.per_e) * q.per_e;
+        while (r >= wg_tiles(a.seg[s])) {
+          r -= wg_tiles(a.seg[s]);
+          ++s;
+        }
+        t = e * wg_tiles(a.seg[s]) + r;
+        return;
+      }
+      i -= ne * q.per_e;
+      s = q.k1 - 1;
+      continue;
+    }
+    const int S = a.bound[s];
+    const int lo = x * S / kXcds, c = (x + 1) * S / kXcds - lo;
+    if (i < c) {
+      t = lo + i;
+      return;
+    }
+    i -= c;
+  }
+  s = a.nseg - 1;
+  t = 0;  // not reached for i below wq_count
+}
+
+// Segment s, tile t -> its coordinates; koff[] holds the one row-offset
+// table the launch's segments share.
+__device__ __forceinline__ WTile wtile_of(const BgArgs& a, const int* koff, int s, int t) {
+  WTile w{};
   const BgSeg& g = a.seg[s];
   const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
   w.si = s;
@@ -527,8 +606,11 @@ __device__ __forceinline__ WTile wtile_of(const BgArgs& a, const int* koff, int 
   return w;
 }
 
-__global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args, int* __restrict__ ctr,
-                                                      int total, int nwg) {
+// A queue entry for s_next: XCD in the top bits, -1 for none.
+__device__ __forceinline__ int wq_pack(int x, int i) { return (x << 24) | i; }
+
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void wgrad_kernel(
+    BgArgs args, int* __restrict__ ctr) {
   // two slice buffers per operand; buffer 1 also stages the epilogue
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][WTILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][WTILE_EL];
@@ -543,17 +625,25 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args, int* __restri
     fa[i] = rb(wm * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
     fb[i] = rb(wn * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
   }
-  {
-    const int32_t* koff = nullptr;
-    int ng = 0;
-    for (int s = 0; s < args.nseg; ++s)
-      if (args.seg[s].koff) {
-        koff = args.seg[s].koff;
-        ng = args.seg[s].G;
-      }
-    for (int i = tid; koff && i <= ng; i += NT) s_koff[i] = koff[i];
+  const WQueues wq = wqueues(args);
+  if (wq.k1 > wq.k0) {
+    const int32_t* koff = args.seg[wq.k0].koff;
+    for (int i = tid; i <= args.seg[wq.k0].G; i += NT) s_koff[i] = koff[i];
   }
-
+  // Thread 0 alone talks to the queues: it takes from queue qx, and moves to
+  // the next nonempty queue when qx runs dry.
+  int qx = (int)blockIdx.x % kXcds;
+  auto take_sync = [&](int from) -> int {
+    for (int k = 0; k < kXcds; ++k) {
+      const int x = (from + k) % kXcds;
+      const int i = atomicAdd(&ctr[x], 1);
+      if (i < wq_count(args, wq, x)) {
+        qx = x;
+        return wq_pack(x, i);
+      }
+    }
+    return -1;
+  };
   u32x4 ra[2][4], rbv[2][4];
   auto load = [&](const WTile& w, int kt) {
     const BgSeg& g = args.seg[w.si];
@@ -572,24 +662,37 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args, int* __restri
     }
   };
 
-  // Tile j of this workgroup finds tile j + 1's index in s_next[(j + 1) & 1]
+  // Tile j of this workgroup finds tile j + 1's entry in s_next[(j + 1) & 1]
   // and fetches tile j + 2's into s_next[j & 1].
-  if (tid == 0) s_next[1] = nwg + atomicAdd(ctr, 1);
+  int cur = 0;
+  if (tid == 0) {
+    cur = take_sync(qx);
+    s_next[1] = cur < 0 ? -1 : take_sync(qx);
+    s_next[0] = cur;
+  }
   __syncthreads();
-  WTile w = wtile_of(args, s_koff, (int)blockIdx.x);
+  cur = s_next[0];
+  if (cur < 0) return;  // no tile at all (uniform: every thread read the same)
+  int s0, t0;
+  wq_tile(args, wq, cur >> 24, cur & 0xffffff, s0, t0);
+  WTile w = wtile_of(args, s_koff, s0, t0);
   load(w, 0);
   store(0);
   __syncthreads();
   for (int j = 0;; ++j) {
     const int nxt = s_next[(j + 1) & 1];
-    const bool more = nxt < total;
-    // The counter's reply is first used after this tile's K loop, where the
+    const bool more = nxt >= 0;
+    // The queue's reply is first used after this tile's K loop, where the
     // wave waits for its loads anyway (the library builds this file without
     // the compiler's wave-level atomic combining, which would wait here).
     int fetched;
-    if (tid == 0 && more) fetched = atomicAdd(ctr, 1);
+    if (tid == 0 && more) fetched = atomicAdd(&ctr[qx], 1);
     WTile w2{};
-    if (more) w2 = wtile_of(args, s_koff, nxt);
+    if (more) {
+      int s2, t2;
+      wq_tile(args, wq, nxt >> 24, nxt & 0xffffff, s2, t2);
+      w2 = wtile_of(args, s_koff, s2, t2);
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -635,19 +738,29 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args, int* __restri
     if (w.nk > 0) slice(kt & 1);
     __syncthreads();
     store(0);
-    if (tid == 0 && more) s_next[j & 1] = nwg + fetched;
+    if (tid == 0 && more)
+      s_next[j & 1] =
+          fetched < wq_count(args, wq, qx) ? wq_pack(qx, fetched) : take_sync(qx + 1);
 
     // Epilogue through LDS buffer 1, 32 rows of the wave's block at a time:
     // the accumulator layout puts one row per lane, so direct stores would
     // send 32-byte pieces of 32 rows per instruction; staged, each store
-    // instruction writes two whole 512-byte rows.
+    // instruction writes two whole 512-byte rows.  Each wave stages in its
+    // own region (a wave's LDS accesses complete in order, so fences that
+    // keep the compiler from reordering them suffice); one barrier at the
+    // end keeps the next tile's slice stores out of regions still read.
     {
       const BgSeg& g = args.seg[w.si];
       constexpr int SP = 128 + 4;  // staging row pitch (floats)
       static_assert(2 * 32 * SP * 4 <= WTILE_EL * 2, "two waves' staging per buffer");
       float* stage = reinterpret_cast<float*>(wave < 2 ? &sA[1][0] : &sB[1][0]) +
                      (wave & 1) * 32 * SP;
-      float* C = static_cast<float*>(g.C) + (int64_t)w.e * g.c_gstride;
+      // Stores through a buffer resource over this group's M x ldc output: a
+      // row or column outside the output gets an offset past its end, which
+      // the hardware drops, so the 16 stores of a round need no branches.
+      const int M = g.M, N = g.N, ldc = (int)g.ldc;
+      const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<float*>(g.C) + (int64_t)w.e * g.c_gstride, 0, M * ldc * 4, kBufWord3);
       const int mrow0 = w.m0 + wm * 128, ncol0 = w.n0 + wn * 128;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -660,19 +773,27 @@ __global__ __launch_bounds__(NT, 1) void wgrad_kernel(BgArgs args, int* __restri
                 &stage[(lane & 31) * SP + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
                 make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int c = ncol0 + 4 * (lane & 31);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = 2 * i + (lane >> 5);
           const int m = mrow0 + mb * 32 + row;
-          if (m < g.M && c < g.N)
-            *reinterpret_cast<float4*>(&C[(int64_t)m * g.ldc + c]) =
-                *reinterpret_cast<const float4*>(&stage[row * SP + 4 * (lane & 31)]);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row * SP + 4 * (lane & 31)]);
+          const int off = (m < M && c < N) ? (m * ldc + c) * 4 : kBufDrop;
+          __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, 0);
         }
-        __syncthreads();
+        // all 16 LDS reads in flight at once, then the 16 stores
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x040, 16, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
+    __syncthreads();
     if (!more) break;
     w = w2;
   }
@@ -746,7 +867,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
     int* __restrict__ clear) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (clear && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0;
+  if (clear && blockIdx.x == 0 && threadIdx.x < kWgQueues) clear[threadIdx.x] = 0;
   if (t >= T) return;
   // slot_of is -1 for an expert id outside [0, n) (the grouping leaves such
   // slots out); they are skipped here and in the kernels below.
@@ -905,18 +1026,27 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s, in
   if (grid == 0) return hipSuccess;
   if (kind == BG_WGRAD) {
     if (!work_ctr) return hipErrorInvalidValue;
-    // the segments with a row-offset table share one of at most 256 groups
+    // the segments with a row-offset table are contiguous and share one
+    // table of at most 256 groups
     const int32_t* koff = nullptr;
+    int first = -1, last = -1;
     for (int i = 0; i < nseg; ++i) {
       if (!segs[i].koff) continue;
-      if ((koff && segs[i].koff != koff) || segs[i].G > kWgMaxGroups) return hipErrorInvalidValue;
+      if (koff && (segs[i].koff != koff || segs[i].G != segs[first].G || last != i - 1))
+        return hipErrorInvalidValue;
+      if (segs[i].G > kWgMaxGroups) return hipErrorInvalidValue;
+      if (!koff) first = i;
       koff = segs[i].koff;
+      last = i;
     }
+    // each group's output is addressed by a 32-bit buffer offset
+    for (int i = 0; i < nseg; ++i)
+      if ((int64_t)segs[i].M * segs[i].ldc * 4 >= (int64_t)kBufDrop) return hipErrorInvalidValue;
     int cus = 0;
     const hipError_t e = cu_count(&cus);
     if (e != hipSuccess) return e;
     const int nwg = total < cus ? total : cus;
-    hipLaunchKernelGGL(wgrad_kernel, dim3(nwg), dim3(NT), 0, s, args, work_ctr, total, nwg);
+    hipLaunchKernelGGL(wgrad_kernel, dim3(nwg), dim3(NT), 0, s, args, work_ctr);
     return hipGetLastError();
   }
   switch (kind) {

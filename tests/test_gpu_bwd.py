@@ -205,6 +205,9 @@ def test_bwd_full_size_sampled(name):
     want = oracle.layer_bwd(inp, cfg.N, cfg.m, cfg.K, cfg.K_s, r["topk_idx"], r["f"], dh32, alpha,
                             toks=toks, want_dcent=False, experts=experts, want_shared=False)
     got = run_bwd(cfg, inp, r, dh, alpha)
+    for kk in ("dw1", "dw3", "dw2"):
+        # every expert's tiles were written (the outputs start as NaN)
+        assert np.isfinite(got[kk]).all(), kk
     got["du"] = got["du"][toks]
     for kk in ("dw1", "dw3", "dw2"):
         got[kk] = got[kk][experts]

@@ -196,6 +196,9 @@ def test_train_full_size_sampled(name):
                             toks=toks, want_dcent=False, experts=experts, want_shared=False)
     fwd, got = train_step(cfg, inp, dh, alpha, moe.MOE_PACKED_WEIGHTS)
     assert np.array_equal(fwd["idx"], r["topk_idx"])
+    for kk in ("dw1", "dw3", "dw2"):
+        # every expert's tiles were written (the outputs start as NaN)
+        assert np.isfinite(got[kk]).all(), kk
     got["du"] = got["du"][toks]
     for kk in ("dw1", "dw3", "dw2"):
         got[kk] = got[kk][experts]
