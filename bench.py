@@ -369,8 +369,13 @@ def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=
         b = backward_regime(torch, moe, hip, args, cfg, None, layer, packed=True, alpha=bwd_alpha,
                             steps=max(5, steps // 2))
         out["backward"] = {k: b[k] for k in ("ms_per_step", "tokens_per_s", "gemm_mfma_frac",
-                                             "weight_layout", "roofline")}
+                                             "weight_layout", "roofline", "train_step_ms")}
         out["backward"]["kernel_us"] = {k: v["us"] for k, v in b["kernels"].items()}
+        b = backward_regime(torch, moe, hip, args, cfg, None, layer, packed=True, alpha=bwd_alpha,
+                            steps=max(5, steps // 2), saved=True)
+        out["backward_saved"] = {k: b[k] for k in ("ms_per_step", "tokens_per_s", "a_b",
+                                                   "train_step_ms")}
+        out["backward_saved"]["kernel_us"] = {k: v["us"] for k, v in b["kernels"].items()}
     del layer, sets, inp
     torch.cuda.empty_cache()
     return out
