@@ -205,3 +205,61 @@ def test_train_full_size_sampled(name):
     check(got, want, ["du", "dw1", "dw3", "dw2"])
     for kk in ("dcent", "dws1", "dws3", "dws2"):
         assert np.isfinite(got[kk]).all(), kk
+
+
+def test_train_pair_graph_replays():
+    """The forward with kept pre-activations and the backward on its
+    workspace, captured together as one HIP graph, give the eager bits on
+    every replay (junk in the outputs before each, an eager pair between
+    replays on the same workspaces)."""
+    name = "ragged_bf16"
+    cfg = ALL[name]
+    inp = inputs(name)
+    d = dev()
+    p, t = upload(cfg, inp, True)
+    sv = moe.MOE_PACKED_WEIGHTS | moe.MOE_SAVE_FOR_BACKWARD
+    fws = torch.empty(moe.moe_train_workspace_bytes(p), dtype=torch.uint8, device=d)
+    bws = torch.empty(moe.moe_bwd_workspace_bytes(p), dtype=torch.uint8, device=d)
+    dht = to_device(moe_synth.make_upstream_grad(cfg, seed=1), d)
+    n, ff, fs = cfg.n, cfg.d_ff, cfg.K_s * cfg.d_ff
+    f32 = dict(dtype=torch.float32, device=d)
+    fwd = dict(h=torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=d),
+               idx=torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=d),
+               gate=torch.empty((cfg.T, cfg.k), **f32),
+               counts=torch.empty(n, dtype=torch.int32, device=d),
+               f=torch.empty(n, **f32), P=torch.empty(n, **f32))
+    g = dict(du=torch.empty((cfg.T, cfg.d), **f32), dcent=torch.empty((n, cfg.d), **f32),
+             dw1=torch.empty((n, ff, cfg.d), **f32), dw3=torch.empty((n, ff, cfg.d), **f32),
+             dw2=torch.empty((n, cfg.d, ff), **f32), dws1=torch.empty((fs, cfg.d), **f32),
+             dws3=torch.empty((fs, cfg.d), **f32), dws2=torch.empty((cfg.d, fs), **f32))
+
+    def pair():
+        moe.moe_layer_fwd(p, t["u"], t["centroids"], t["w1"], t["w3"], t["w2"], t["ws1"],
+                          t["ws3"], t["ws2"], fwd["h"], fwd["idx"], fwd["gate"], fwd["counts"],
+                          fwd["f"], fwd["P"], sv, fws)
+        moe.moe_layer_bwd(p, t["u"], t["centroids"], t["w1"], t["w3"], t["w2"], t["ws1"],
+                          t["ws3"], t["ws2"], fwd["idx"], fwd["gate"], fwd["f"], fws, dht, 0.37,
+                          g["du"], g["dcent"], g["dw1"], g["dw3"], g["dw2"], g["dws1"],
+                          g["dws3"], g["dws2"], sv, bws)
+
+    outs = dict(fwd, **g)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pair()  # first call outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pair()
+    for i, eager_between in enumerate((False, True, False)):
+        if eager_between:
+            pair()
+            torch.cuda.synchronize()
+        for v in outs.values():
+            v.fill_(-3)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in want:
+            assert torch.equal(outs[k], want[k]), (i, k)
