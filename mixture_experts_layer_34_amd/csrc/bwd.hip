@@ -448,9 +448,26 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
       const int c = n0 + wn * 64 + 4 * (lane & 15);
 #pragma unroll 2
       for (int i = 0; i < 8; ++i) {
+        // The 16 lanes of a row group share the row; for k <= 16 lane j of
+        // the group loads slot j's grouped row index and the group trades
+        // them by shuffles, so that all k row loads are in flight at once
+        // (one dependent index load per slot would serialise them).
         const int r = 4 * i + (lane >> 4), ml = wm * 64 + mb * 32 + r;
-        if (ml >= mvalid || c >= g.N) continue;
-        const int64_t t = (int64_t)m0 + ml, at = t * g.ldc + c;
+        const bool rok = ml < mvalid;
+        const int64_t t = (int64_t)m0 + (rok ? ml : 0), at = t * g.ldc + c;
+        const bool fast = g.k <= 16;
+        const int mys = (fast && rok && (lane & 15) < g.k) ? g.slot_of[t * g.k + (lane & 15)] : -1;
+        uint2 xv[16];
+        if (fast) {
+#pragma unroll
+          for (int sl = 0; sl < 16; ++sl) {
+            const int rr = __shfl(mys, (lane & 48) | sl);
+            xv[sl] = (sl < g.k && rr >= 0 && c < g.N)
+                         ? *reinterpret_cast<const uint2*>(&X[(int64_t)rr * g.ldc + c])
+                         : make_uint2(0u, 0u);
+          }
+        }
+        if (!rok || c >= g.N) continue;
         const float4 v = *reinterpret_cast<const float4*>(&st[r * SPF + 4 * (lane & 15)]);
         float o[4] = {v.x, v.y, v.z, v.w}, tmp[4];
         if (R) {
@@ -463,12 +480,22 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[j] += tmp[j];
         }
-        for (int sl = 0; sl < g.k; ++sl) {
-          const int64_t rr = g.slot_of[t * g.k + sl];
-          if (rr < 0) continue;  // slot left out by the grouping
-          unpack4(*reinterpret_cast<const uint2*>(&X[rr * g.ldc + c]), tmp);
+        if (fast) {
+          // slots left out by the grouping (index < 0) loaded zeros
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+          for (int sl = 0; sl < 16; ++sl) {
+            unpack4(xv[sl], tmp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+          }
+        } else {
+          for (int sl = 0; sl < g.k; ++sl) {
+            const int64_t rr = g.slot_of[t * g.k + sl];
+            if (rr < 0) continue;  // slot left out by the grouping
+            unpack4(*reinterpret_cast<const uint2*>(&X[rr * g.ldc + c]), tmp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] += tmp[j];
+          }
         }
         *reinterpret_cast<float4*>(&C[at]) = make_float4(o[0], o[1], o[2], o[3]);
       }
