@@ -89,8 +89,8 @@ enum { MOE_NO_RESIDUAL = 1, MOE_NO_SHARED = 2, MOE_PACKED_WEIGHTS = 4, MOE_SAVE_
 size_t moe_workspace_bytes(const moe_problem *p);
 
 /* Bytes of workspace for moe_layer_fwd with MOE_SAVE_FOR_BACKWARD: the above
- * plus the kept pre-activations, (T*k + T*K_s) * 2 * d_ff bf16 values; 0 when
- * the problem is invalid or not bf16. */
+ * plus the kept pre-activations, (T*k + T*K_s) * 2 * d_ff bf16 values, and
+ * the router's fp32 logits; 0 when the problem is invalid or not bf16. */
 size_t moe_train_workspace_bytes(const moe_problem *p);
 
 /*
@@ -169,9 +169,10 @@ moe_status moe_combine(const moe_problem *p, const void *residual, const void *s
  *                     six weight tensors come from moe_pack_weights;
  *                     MOE_SAVE_FOR_BACKWARD (bf16): the workspace, of
  *                     moe_train_workspace_bytes(p) bytes, also keeps the
- *                     up projection's pre-activations W1 x and W3 x, and
- *                     keeps the grouping, for moe_layer_bwd (which then
- *                     skips computing them again); h is the same either way
+ *                     up projection's pre-activations W1 x and W3 x, the
+ *                     router's logits and the grouping, for moe_layer_bwd
+ *                     (which then skips computing them again); h is the
+ *                     same either way
  */
 moe_status moe_layer_fwd(const moe_problem *p, const void *u, const void *centroids,
                          const void *w1, const void *w3, const void *w2, const void *ws1,

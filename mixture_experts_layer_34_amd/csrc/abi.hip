@@ -58,6 +58,8 @@ struct Layout {
   // kept for the backward (MOE_SAVE_FOR_BACKWARD): pre-activations W1 x | W3 x
   // of the routed rows [T*k][2 d_ff] and of the shared experts [T][2 K_s d_ff]
   size_t pre, pres;
+  size_t lgs;  // and the router's logits [T][n rounded up to 8] fp32 (batches the
+               // small-batch router does not cover: that one keeps them in lg)
   size_t total_train;
   int max_tiles;
   size_t hcap;  // elements of hbuf
@@ -98,6 +100,7 @@ Layout layout(const Dims& d) {
   L.total = o;
   L.pre = take(R * 2 * d.d_ff * 2);
   L.pres = take(hs_el * 2 * 2);
+  L.lgs = take((size_t)d.T * ((d.n + 7) & ~7) * 4);
   L.total_train = o;
   return L;
 }
@@ -463,7 +466,8 @@ moe_status moe_layer_fwd_marked(const moe_problem* p, const void* u, const void*
   } else {
     MOE_TRY(moe::launch_route(p->dtype, u, centroids, d.T, d.d, d.n, d.k, topk_idx, topk_gate,
                               at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P),
-                              at<int32_t>(ws, L.lrank), s));
+                              at<int32_t>(ws, L.lrank), s, save ? at<float>(ws, L.lgs) : nullptr,
+                              (d.n + 7) & ~7));
     MOE_TRY(mark());
     if (moe::group_in_one_pass(d.T, d.n)) {
       MOE_TRY(moe::launch_group(at<int32_t>(ws, L.blk_cnt), at<float>(ws, L.blk_P), d.T, d.n,
@@ -559,11 +563,11 @@ int moe_layer_bwd_kernels(const moe_problem* p, int flags, const char** names, i
                                     "q",    "ab_swiglu",   "dx",      "softmax_bwd", "du",
                                     "wgrad", "dcent_sum"};
   // with the forward's saved grouping and pre-activations
-  static const char* saved[] = {"gather", "logits", "q", "swiglu_bwd", "dx", "softmax_bwd",
+  static const char* saved[] = {"gather", "q", "swiglu_bwd", "dx", "softmax_bwd",
                                 "du", "wgrad", "dcent_sum"};
   const bool sv = (flags & MOE_SAVE_FOR_BACKWARD) != 0;
   const char** seq = sv ? saved : recompute;
-  const int c = sv ? 9 : 12;
+  const int c = sv ? 8 : 12;
   for (int i = 0; names && i < c && i < max_names; ++i) names[i] = seq[i];
   return c;
 }
@@ -651,8 +655,15 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     g.n_groups = d.n;
     g.max_tiles = tl.max_tiles;
   };
-  float* lg = at<float>(ws, L.lg);
-  {
+  // The router's logits: kept by a forward that saved for the backward
+  // (its small-batch router keeps them at pitch n), else computed again.
+  const float* lg = at<float>(ws, L.lg);
+  int ldlg = L.ldl;
+  if (saved) {
+    const bool small = moe::route_small(p->dtype, d.T);
+    lg = at<float>(gws, small ? FL.lg : FL.lgs);
+    ldlg = small ? d.n : L.ldl;
+  } else {
     moe::BgSeg g{};
     g.A[0] = u;
     g.lda = d.d;
@@ -662,11 +673,11 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     g.N = d.n;
     g.K = d.d;
     g.rows = d.T;
-    g.C = lg;
+    g.C = at<float>(ws, L.lg);
     g.ldc = L.ldl;
     MOE_TRY(moe::launch_bg(moe::BG_LOGITS, &g, 1, s));
+    MOE_TRY(mark());
   }
-  MOE_TRY(mark());
 
   // q = dh W2 for every grouped row (ungated), and for the shared experts.
   uint16_t* q = at<uint16_t>(ws, L.q);
@@ -804,7 +815,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
 
   // Softmax backward with the gate gradients and the balance term.
   uint16_t* dl = at<uint16_t>(ws, L.dl);
-  MOE_TRY(moe::launch_softmax_bwd(lg, L.ldl, d.T, d.n, d.k, topk_idx, slot_of, dgp, L.ldgp, f,
+  MOE_TRY(moe::launch_softmax_bwd(lg, ldlg, L.ldl, d.T, d.n, d.k, topk_idx, slot_of, dgp, L.ldgp, f,
                                   alpha, dl, s));
   MOE_TRY(mark());
 

@@ -100,10 +100,10 @@ hipError_t launch_swiglu_bwd(const uint16_t* q, const uint16_t* pre, const float
                              const int32_t* nrows, int64_t rows, int F, uint16_t* da,
                              uint16_t* db, uint16_t* gh, float* dgp, int ldgp, hipStream_t s);
 
-// Per token: softmax of the logits lg [T][ldl] (fp32), the gate gradients
+// Per token: softmax of the logits lg [T][ldlg] (fp32), the gate gradients
 // sum_p dgp[slot][p], the balance term alpha f_i / T, and the softmax
 // backward dl = s (ds - <s, ds>) into dl [T][ldl] (bf16, zero padded).
-hipError_t launch_softmax_bwd(const float* lg, int ldl, int64_t T, int n, int k,
+hipError_t launch_softmax_bwd(const float* lg, int ldlg, int ldl, int64_t T, int n, int k,
                               const int32_t* topk_idx, const int32_t* slot_of, const float* dgp,
                               int ldgp, const float* f, float alpha, uint16_t* dl, hipStream_t s);
 

@@ -928,7 +928,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // One wave per token, four tokens per workgroup; lanes own experts
 // lane + 64 q.
 __global__ __launch_bounds__(256) void softmax_bwd_kernel(
-    const float* __restrict__ lg, int ldl, int64_t T, int n, int k,
+    const float* __restrict__ lg, int ldlg, int ldl, int64_t T, int n, int k,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_of,
     const float* __restrict__ dgp, int ldgp, const float* __restrict__ f, float alpha,
     uint16_t* __restrict__ dl) {
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(256) void softmax_bwd_kernel(
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int i = lane + 64 * q;
-    s[q] = (live && i < n) ? lg[t * ldl + i] : -3.0e38f;
+    s[q] = (live && i < n) ? lg[t * ldlg + i] : -3.0e38f;
     mx = fmaxf(mx, s[q]);
   }
   mx = wave_max(mx);
@@ -1108,12 +1108,12 @@ hipError_t launch_swiglu_bwd(const uint16_t* q, const uint16_t* pre, const float
   return hipGetLastError();
 }
 
-hipError_t launch_softmax_bwd(const float* lg, int ldl, int64_t T, int n, int k,
+hipError_t launch_softmax_bwd(const float* lg, int ldlg, int ldl, int64_t T, int n, int k,
                               const int32_t* topk_idx, const int32_t* slot_of, const float* dgp,
                               int ldgp, const float* f, float alpha, uint16_t* dl, hipStream_t s) {
   const int64_t blocks = (T + 3) / 4;
-  hipLaunchKernelGGL(softmax_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, s, lg, ldl, T, n,
-                     k, topk_idx, slot_of, dgp, ldgp, f, alpha, dl);
+  hipLaunchKernelGGL(softmax_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, s, lg, ldlg, ldl,
+                     T, n, k, topk_idx, slot_of, dgp, ldgp, f, alpha, dl);
   return hipGetLastError();
 }
 

@@ -24,10 +24,12 @@ struct TileList {
 };
 
 // Router: logits, softmax, top-k, per-block P partial sums, per-block
-// histogram and per-(token, slot) rank inside its block.
+// histogram and per-(token, slot) rank inside its block.  bf16 with lg_out:
+// also the fp32 logits, lg_out [T][ld_out] (ld_out >= n, zero padded).
 hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, int d, int n,
                         int k, int32_t* topk_idx, float* topk_gate, int32_t* blk_cnt,
-                        float* blk_P, int32_t* lrank, hipStream_t s);
+                        float* blk_P, int32_t* lrank, hipStream_t s, float* lg_out = nullptr,
+                        int ld_out = 0);
 
 // Routing and grouping of batches of at most 64 tokens (bf16) in two
 // launches: logits over (token block x 16 experts) workgroups into lg

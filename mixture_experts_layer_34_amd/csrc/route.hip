@@ -438,7 +438,8 @@ template <int NB, bool STAGED>
 __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ u, const uint16_t* __restrict__ cent, int64_t T, int d, int n,
     int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-    int32_t* __restrict__ blk_cnt, float* __restrict__ blk_P, int32_t* __restrict__ lrank) {
+    int32_t* __restrict__ blk_cnt, float* __restrict__ blk_P, int32_t* __restrict__ lrank,
+    float* __restrict__ lg_out, int ld_out) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const RouteSmem s = carve(smem, n);
   const int64_t blk = blockIdx.x;
@@ -447,6 +448,13 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
   else
     logits_bf16<NB>(u, cent, T, d, n, blk, s);
   __syncthreads();
+  if (lg_out) {  // the logits for a backward pass, rows padded with zeros to ld_out
+    for (int i = threadIdx.x; i < kRouteTok * ld_out; i += kThreads) {
+      const int tl = i / ld_out, e = i - tl * ld_out;
+      const int64_t t = blk * kRouteTok + tl;
+      if (t < T) lg_out[t * ld_out + e] = e < n ? s.lg[tl * s.ldl + e] : 0.0f;
+    }
+  }
   route_tail<NB>(T, n, k, blk, s, topk_idx, topk_gate, blk_cnt, blk_P, lrank);
 }
 
@@ -997,7 +1005,7 @@ __global__ __launch_bounds__(kTileThreads) void tiles_kernel(const int32_t* __re
 
 hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, int d, int n,
                         int k, int32_t* topk_idx, float* topk_gate, int32_t* blk_cnt,
-                        float* blk_P, int32_t* lrank, hipStream_t s) {
+                        float* blk_P, int32_t* lrank, hipStream_t s, float* lg_out, int ld_out) {
   const int B = (int)((T + kRouteTok - 1) / kRouteTok);
   const size_t sm = route_smem_bytes(n, k);
   const int nb = (n + 15) / 16;
@@ -1034,7 +1042,7 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
     }                                                                                          \
     hipLaunchKernelGGL((route_bf16_kernel<NBV, STG>), dim3(B), dim3(kThreads), smv, s,         \
                        (const uint16_t*)u, (const uint16_t*)cent, T, d, n, k, topk_idx,        \
-                       topk_gate, blk_cnt, blk_P, lrank);                                      \
+                       topk_gate, blk_cnt, blk_P, lrank, lg_out, ld_out);                      \
   }
   // Staged loads while a wave's hidden range fits one round (d <= 2048) and
   // the operand regions fit LDS (n <= 64).
