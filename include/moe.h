@@ -237,8 +237,11 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  *   fwd_ws            the workspace of the forward call that produced them, if
  *                     that call had MOE_SAVE_FOR_BACKWARD (with nothing run on
  *                     that workspace since); flags must then include
- *                     MOE_SAVE_FOR_BACKWARD too.  NULL otherwise: a and b and
- *                     the grouping are computed again
+ *                     MOE_SAVE_FOR_BACKWARD too; the same weights and u must
+ *                     be passed.  NULL otherwise: a and b, the router's logits
+ *                     and the grouping are computed again.  Status codes:
+ *                     MOE_ERR_NULL for the flag without fwd_ws, MOE_ERR_SHAPE
+ *                     for fwd_ws without the flag, MOE_ERR_ALIGN if misaligned
  *   dh [T][d]         upstream gradient (bf16)
  *   alpha             balance-loss coefficient (0: no balance term)
  *   du [T][d], dcentroids [n][d]              out, fp32
