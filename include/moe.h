@@ -61,8 +61,8 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /*
  * The pages' statement of the problem.  Valid when
- *   T >= 1;  T*k*d, T*k*d_ff and T*K_s*d_ff < 2^31;  d, d_ff >= 32 and
- *   multiples of 32;
+ *   T >= 1;  T*k*d, T*k*d_ff, T*K_s*d_ff, d*d_ff and K_s*d_ff*d < 2^31;
+ *   d, d_ff >= 32 and multiples of 32;
  *   N, m, K >= 1;  K_s >= 0;  n = m*N <= MOE_MAX_EXPERTS;
  *   1 <= k = m*K - K_s <= min(n, MOE_MAX_TOPK).
  * Only the products m*N and m*K enter the result.
@@ -94,11 +94,13 @@ size_t moe_workspace_bytes(const moe_problem *p);
 size_t moe_train_workspace_bytes(const moe_problem *p);
 
 /*
- * Router ("Routing in a classic MoE layer" and "Top-k routing, from
- * affinities to gates"; statistics from "Expert-level balance loss").
+ * Router: the affinities and the TopK gate of the equation in "Routing in a
+ * classic MoE layer" (the selection as in "Top-k routing, from affinities to
+ * gates"); the statistics f_i and P_i of "Expert-level balance loss".
  *   u [T][d], centroids [n][d]                        in
- *   topk_idx [T][k]   kept experts, descending logit u^T e_i, equal logits
- *                     in ascending expert index (the sketch's stable sort)
+ *   topk_idx [T][k]   kept experts, descending logit u^T e_i; equal logits
+ *                     keep the lower expert index first (this library's tie
+ *                     rule: the equation's set form leaves ties open)
  *   topk_gate [T][k]  s of the kept experts (fp32)
  *   counts [n]        tokens that kept expert i
  *   f [n]             (float)(count_i * n) / (float)(k * T)
@@ -110,9 +112,10 @@ moe_status moe_route(const moe_problem *p, const void *u, const void *centroids,
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Grouping of the T*k (token, slot) pairs by expert (the page's note that a
- * production layer groups tokens per expert), expert-major with ascending
- * token inside each expert (a stable counting sort).
+ * Grouping of the T*k (token, slot) pairs by expert, after the note closing
+ * "Top-k routing, from affinities to gates" that a production layer groups
+ * tokens per expert; expert-major with ascending token inside each expert
+ * (a stable counting sort).
  *   u [T][d], topk_idx [T][k]                         in
  *   offsets [n+1]     first grouped row of each expert, offsets[n] = T*k
  *   perm_token [T*k]  token of each grouped row
@@ -124,7 +127,12 @@ moe_status moe_permute(const moe_problem *p, const void *u, const int32_t *topk_
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Grouped SwiGLU FFN: rows offsets[g] .. offsets[g+1]-1 of x go through
+ * Grouped SwiGLU FFN, the experts FFN_i of the equation in "Routing in a
+ * classic MoE layer" run the way the note closing "Top-k routing, from
+ * affinities to gates" describes a production layer: tokens grouped per
+ * expert, each expert's weight matrices applied to its group at once (and the
+ * always-on shared experts of "What the 16B configuration looks like" as one
+ * dense group).  Rows offsets[g] .. offsets[g+1]-1 of x go through
  * expert g: y = W2_g (SiLU(W1_g x) * (W3_g x)).  The intermediate is rounded
  * to the dtype (bf16) between the two products; accumulation is fp32.
  *   n_groups          1 .. MOE_MAX_EXPERTS
@@ -136,8 +144,8 @@ moe_status moe_permute(const moe_problem *p, const void *u, const int32_t *topk_
  * Routed experts: n_groups = n, rows = T*k, d_ff_group = d_ff.  Shared
  * experts as one dense SwiGLU (their sum): n_groups = 1, rows = T,
  * d_ff_group = K_s*d_ff, offsets = {0, T}.
- * d_ff_group must be a multiple of 32 with rows*d_ff_group fitting the
- * workspace of moe_workspace_bytes(p).  flags: 0 or MOE_PACKED_WEIGHTS.
+ * d_ff_group must be a multiple of 32 with d_ff_group*d < 2^31 and
+ * rows*d_ff_group fitting the workspace of moe_workspace_bytes(p).  flags: 0 or MOE_PACKED_WEIGHTS.
  */
 moe_status moe_grouped_ffn(const moe_problem *p, int32_t n_groups, int64_t rows,
                            const int32_t *offsets, const void *x, const void *w1,
@@ -156,7 +164,11 @@ moe_status moe_combine(const moe_problem *p, const void *residual, const void *s
                        void *h, void *stream);
 
 /*
- * The whole layer: route, group, routed experts, shared experts, combine.
+ * The whole layer: the equation of "Routing in a classic MoE layer"
+ * (affinities, TopK gates, h = sum_i g_i FFN_i(u) + u) with the fine-grained
+ * experts and the always-on shared experts of "What the 16B configuration
+ * looks like", and the statistics of "Expert-level balance loss": route,
+ * group, routed experts, shared experts, combine.
  *   u [T][d], centroids [n][d]
  *   w1, w3 [n][d_ff][d], w2 [n][d][d_ff]              routed experts
  *   ws1, ws3 [K_s*d_ff][d], ws2 [d][K_s*d_ff]         shared experts (expert q
@@ -256,7 +268,11 @@ int moe_layer_kernels(const moe_problem *p, int flags, const char **names, int m
  * Intermediates (the SwiGLU gradients, q = W2^T dh, the experts' input
  * gradients, the router's softmax gradient) are rounded to bf16; every
  * product accumulates in fp32; the result does not depend on the weight
- * layout.  Requires p->dtype == MOE_BF16.
+ * layout.  Requires p->dtype == MOE_BF16, and beyond the limits of
+ * moe_problem: T * (n rounded up to 8) < 2^31, and d_ff*d, K_s*d_ff*d and
+ * n*d below 2^29 - 4 (each gradient output of one expert, of the shared
+ * experts, of the centroids, in fp32 bytes, stays below 2^31 - 16);
+ * MOE_ERR_SHAPE otherwise, before anything is enqueued.
  */
 moe_status moe_layer_bwd(const moe_problem *p, const void *u, const void *centroids,
                          const void *w1, const void *w3, const void *w2, const void *ws1,

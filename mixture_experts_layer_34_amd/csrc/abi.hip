@@ -37,6 +37,10 @@ moe_status check_problem(const moe_problem* p, Dims* out) {
       p->T * (int64_t)p->K_s * p->d_ff >= big)
     return MOE_ERR_SHAPE;
   if ((int64_t)p->K_s * p->d_ff > INT32_MAX / 2) return MOE_ERR_SHAPE;
+  // ... and so does every weight matrix: one expert's [d_ff][d] and the
+  // shared experts' dense view [K_s*d_ff][d].
+  if ((int64_t)p->d * p->d_ff >= big || (int64_t)p->K_s * p->d_ff * p->d >= big)
+    return MOE_ERR_SHAPE;
   out->T = p->T;
   out->d = p->d;
   out->d_ff = p->d_ff;
@@ -301,7 +305,7 @@ moe_status moe_grouped_ffn(const moe_problem* p, int32_t n_groups, int64_t rows,
   const bool packed = (flags & MOE_PACKED_WEIGHTS) != 0;
   if (packed && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (n_groups < 1 || n_groups > MOE_MAX_EXPERTS || rows < 1 || d_ff_group < 32 ||
-      d_ff_group % 32 != 0)
+      d_ff_group % 32 != 0 || (int64_t)d_ff_group * d.d >= ((int64_t)1 << 31))
     return MOE_ERR_SHAPE;
   if (!offsets || !x || !w1 || !w3 || !w2 || !y) return MOE_ERR_NULL;
   if (!aligned(offsets) || !aligned(x) || !aligned(w1) || !aligned(w3) || !aligned(w2) ||
@@ -605,6 +609,15 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
                  !aligned(dws3) || !aligned(dws2)))
     return MOE_ERR_ALIGN;
   const BwdLayout L = bwd_layout(d);
+  // Sizes the backward's kernels address with 32-bit offsets, checked here so
+  // that nothing is enqueued on error: the softmax gradient [T][ldl] bf16 is
+  // read with byte offsets, and every gradient output (fp32 [d_ff][d] per
+  // expert, the shared experts' [K_s*d_ff][d], the centroids' [n][d] per
+  // token chunk) through a buffer resource of fewer than 2^31 bytes.
+  const int64_t out_lim = moe::kBwdOutBytes;
+  if (d.T * L.ldl >= ((int64_t)1 << 31) || (int64_t)d.d_ff * d.d * 4 >= out_lim ||
+      (int64_t)d.K_s * d.d_ff * d.d * 4 >= out_lim || (int64_t)d.n * d.d * 4 >= out_lim)
+    return MOE_ERR_SHAPE;
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws)) return MOE_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -62,6 +62,9 @@ struct BgSeg {
 };
 
 constexpr int kBgMaxSeg = 8;
+// Bytes of one BG_WGRAD output group (M * ldc * 4) must stay below this: the
+// epilogue stores through a buffer resource and drops offsets at or past it.
+constexpr int kBwdOutBytes = 0x7ffffff0;
 constexpr int kBgTile = 128;  // rows and columns of a rows-grouping tile
 constexpr int kBgK = 64;      // K slice
 

@@ -532,7 +532,7 @@ constexpr int kXcds = kWgQueues;
 // Buffer resource word 3 for raw 32-bit accesses on gfx9, and an offset
 // past any output (outputs stay below 2 GiB).
 constexpr int kBufWord3 = 0x00020000;
-constexpr int kBufDrop = 0x7ffffff0;
+constexpr int kBufDrop = kBwdOutBytes;
 
 struct WTile {
   int si, e, m0, n0, kb, ke, nk;

@@ -30,6 +30,7 @@ _STREAM = {"u": 1, "centroids": 2, "w1": 3, "w3": 4, "w2": 5,
            "ws1": 6, "ws3": 7, "ws2": 8, "redraw": 9, "dh": 10}
 
 MARGIN = 1e-4
+EPS32 = 2.0 ** -24  # unit roundoff of fp32
 
 
 @dataclasses.dataclass(frozen=True)
@@ -46,6 +47,7 @@ class MoEConfig:
     cent_std: float | None = None   # None: 1/sqrt(d)
     w_std: float = 0.02
     zipf_s: float | None = None     # Zipf exponent on centroid row norms
+    tie_pairs: bool = False         # centroid row 2j+1 repeats row 2j: exact logit ties
 
     @property
     def n(self) -> int:
@@ -142,48 +144,81 @@ def _weights(rng: np.random.Generator, groups: int, rows: int, cols: int,
     return out
 
 
+def certified_margin(d: int, max_abs_logit: float) -> float:
+    """Smallest top-k gap the inputs must keep: 1e-4, or eight times the
+    typical difference between two fp32 summation orders of a length-d dot
+    product near the largest logit (random-walk rounding, eps sqrt(d) |l|),
+    whichever is larger.  bf16 products are exact in fp32, so only the order
+    of the sums differs between two correct fp32 implementations."""
+    return max(MARGIN, 8.0 * EPS32 * math.sqrt(d) * max_abs_logit)
+
+
+def twin_groups(c32: np.ndarray) -> np.ndarray:
+    """Group id per centroid row: equal rows (bit for bit) share an id."""
+    _, gid = np.unique(np.ascontiguousarray(c32).view(np.uint32), axis=0, return_inverse=True)
+    return np.asarray(gid).reshape(-1)
+
+
 def margin_violations(u32: np.ndarray, c32: np.ndarray, k: int,
                       margin: float = MARGIN) -> np.ndarray:
     """Tokens whose top-(k+1) fp64 logits have an adjacent gap <= margin.
 
     Returns a boolean mask over tokens.  With k = n only the order gaps inside
-    the top k are checked.
+    the top k are checked.  Experts with identical centroid rows tie exactly in
+    any summation order (the tie rule decides between them), so a gap between
+    two such experts is not a violation.
     """
     n = c32.shape[0]
     lg = u32.astype(np.float64) @ c32.astype(np.float64).T
     top = min(k + 1, n)
-    part = -np.sort(-lg, axis=1)[:, :top]
     if top < 2:
         return np.zeros(u32.shape[0], dtype=bool)
+    order = np.argsort(-lg, axis=1, kind="stable")[:, :top]
+    part = np.take_along_axis(lg, order, axis=1)
     gaps = part[:, :-1] - part[:, 1:]
-    return (gaps <= margin).any(axis=1)
+    g = twin_groups(c32)[order]
+    twin = g[:, :-1] == g[:, 1:]
+    return ((gaps <= margin) & ~twin).any(axis=1)
+
+
+def max_abs_logit(u32: np.ndarray, c32: np.ndarray) -> float:
+    return float(np.abs(u32.astype(np.float64) @ c32.astype(np.float64).T).max())
 
 
 def make_router_inputs(cfg: MoEConfig, seed: int = 0, certify: bool = True):
-    """u [T,d] and centroids [n,d] in storage type, plus the redraw count."""
+    """u [T,d] and centroids [n,d] in storage type, plus the redraw count.
+
+    With certify, every token's top-(k+1) logits keep adjacent gaps above
+    certified_margin (tokens that do not are redrawn from their own stream)."""
     T, d, n = cfg.T, cfg.d, cfg.n
     u = _store(_normal(_rng(seed, "u"), (T, d), 1.0), cfg.dtype)
     cstd = cfg.cent_std if cfg.cent_std is not None else 1.0 / math.sqrt(d)
     c = _normal(_rng(seed, "centroids"), (n, d), cstd)
     if cfg.zipf_s is not None:
         c *= zipf_row_scale(n, cfg.zipf_s).astype(np.float32)[:, None]
+    if cfg.tie_pairs:
+        c[1::2] = c[0:n - 1:2]
     cent = _store(c, cfg.dtype)
     redraws = 0
     if certify:
         c32 = as_f32(cent)
         rr = _rng(seed, "redraw")
-        bad = margin_violations(as_f32(u), c32, cfg.k)
         rounds = 0
-        while bad.any():
-            idx = np.nonzero(bad)[0]
-            redraws += idx.size
-            u[idx] = _store(_normal(rr, (idx.size, d), 1.0), cfg.dtype)
-            sub = margin_violations(as_f32(u[idx]), c32, cfg.k)
-            bad = np.zeros(T, dtype=bool)
-            bad[idx[sub]] = True
-            rounds += 1
-            if rounds > 1000:
-                raise RuntimeError("margin certification did not converge")
+        while True:
+            margin = certified_margin(d, max_abs_logit(as_f32(u), c32))
+            bad = margin_violations(as_f32(u), c32, cfg.k, margin)
+            if not bad.any():
+                break
+            while bad.any():
+                idx = np.nonzero(bad)[0]
+                redraws += idx.size
+                u[idx] = _store(_normal(rr, (idx.size, d), 1.0), cfg.dtype)
+                sub = margin_violations(as_f32(u[idx]), c32, cfg.k, margin)
+                bad = np.zeros(T, dtype=bool)
+                bad[idx[sub]] = True
+                rounds += 1
+                if rounds > 1000:
+                    raise RuntimeError("margin certification did not converge")
     return u, cent, redraws
 
 

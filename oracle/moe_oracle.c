@@ -18,8 +18,9 @@
  *       g_i = s_i if s_i is among the k largest, else 0 (no renormalisation,
  *       as the note under "Top-k routing, from affinities to gates" states),
  *       h   = sum_i g_i FFN_i(u) + [shared experts] + u;
- *   - selection order of the "Top-k routing" sketch: experts ordered by
- *     descending affinity logit, ties kept in index order (a stable sort);
+ *   - the k kept experts in descending order of their logit (selection on
+ *     the logits equals selection on s, the softmax being monotone); equal
+ *     logits keep the lower expert index first (this project's tie rule);
  *   - balance statistics of section "Expert-level balance loss": f_i from the
  *     share of tokens that picked expert i, P_i the mean affinity s_i;
  *   - expert FFN = SwiGLU ("GLU Variants Improve Transformer", cited on the
@@ -70,12 +71,17 @@ static float orc_logit(const void *u, const void *cent, int64_t t, int i, int d,
 }
 
 /*
- * Routing for one token.  logit[n] in; s[n] = softmax, order[n] = expert
- * indices sorted by descending logit, ties by ascending index (stable
- * insertion sort; selection on the logit equals selection on s because the
- * softmax is monotone).
+ * Routing of one token (section "Routing in a classic MoE layer": s_i =
+ * softmax_i(u^T e_i) over all n routed experts, g_i = s_i for the k largest
+ * s_i, 0 otherwise).  logit[n] in.  s[n] = the softmax, formed with the
+ * largest logit subtracted from every logit (the same quotient, no
+ * overflow).  sel[k] = the kept experts, chosen in k rounds: each round keeps
+ * the largest logit not kept yet.  The softmax is monotone, so these are the
+ * k largest s_i, in descending order.  Equal logits: the lower expert index
+ * is kept first (this project's tie rule; the pages' set form leaves ties
+ * open, the rule makes the set and its order unique).  taken[n] is scratch.
  */
-static void orc_route_token(const float *logit, int n, float *s, int *order) {
+static void orc_route_token(const float *logit, int n, int k, float *s, int *sel, char *taken) {
   float mx = logit[0];
   for (int i = 1; i < n; ++i)
     if (logit[i] > mx) mx = logit[i];
@@ -85,13 +91,13 @@ static void orc_route_token(const float *logit, int n, float *s, int *order) {
     z += s[i];
   }
   for (int i = 0; i < n; ++i) s[i] = s[i] / z;
-  for (int i = 0; i < n; ++i) {
-    int p = i;
-    while (p > 0 && logit[order[p - 1]] < logit[i]) {
-      order[p] = order[p - 1];
-      --p;
-    }
-    order[p] = i;
+  for (int i = 0; i < n; ++i) taken[i] = 0;
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    for (int i = 0; i < n; ++i)
+      if (!taken[i] && (best < 0 || logit[i] > logit[best])) best = i;
+    taken[best] = 1;
+    sel[j] = best;
   }
 }
 
@@ -117,10 +123,11 @@ int oracle_route(int64_t T, int d, int n, int k, int dtype, const void *u, const
 #pragma omp parallel
   {
     float *lg = (float *)malloc(sizeof(float) * n);
-    int *order = (int *)malloc(sizeof(int) * n);
+    int *sel = (int *)malloc(sizeof(int) * k);
+    char *taken = (char *)malloc((size_t)n);
 #pragma omp for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
-      if (!lg || !order) {
+      if (!lg || !sel || !taken) {
 #pragma omp atomic write
         fail = 1;
         continue;
@@ -128,16 +135,17 @@ int oracle_route(int64_t T, int d, int n, int k, int dtype, const void *u, const
       {
         for (int i = 0; i < n; ++i) lg[i] = orc_logit(u, cent, t, i, d, dtype);
         float *s = s_all + (size_t)t * n;
-        orc_route_token(lg, n, s, order);
+        orc_route_token(lg, n, k, s, sel, taken);
         for (int j = 0; j < k; ++j) {
-          topk_idx[(size_t)t * k + j] = order[j];
-          topk_gate[(size_t)t * k + j] = s[order[j]];
+          topk_idx[(size_t)t * k + j] = sel[j];
+          topk_gate[(size_t)t * k + j] = s[sel[j]];
         }
         if (logits) memcpy(logits + (size_t)t * n, lg, sizeof(float) * n);
       }
     }
     free(lg);
-    free(order);
+    free(sel);
+    free(taken);
   }
   if (fail) {
     free(own);
@@ -406,11 +414,13 @@ static void orc_expert_fwd64(int d, int d_ff, const double *x, const void *w1, c
     b[c] = sb;
     hid[c] = sa * orc_sigmoid(sa) * sb;
   }
-  for (int c = 0; c < d_ff; ++c) {
-    double acc = 0.0;
-    for (int i = 0; i < d; ++i)
-      acc += (double)orc_get(w2, o2 + (size_t)c + (size_t)i * ldw2, dtype) * dy[i];
-    dhid[c] = acc;
+  /* dhid[c] = sum_i W2[i][c] dy[i], i ascending for every c (rows of W2 are
+   * walked in storage order) */
+  for (int c = 0; c < d_ff; ++c) dhid[c] = 0.0;
+  for (int i = 0; i < d; ++i) {
+    const double yi = dy[i];
+    for (int c = 0; c < d_ff; ++c)
+      dhid[c] += (double)orc_get(w2, o2 + (size_t)c + (size_t)i * ldw2, dtype) * yi;
   }
 }
 
@@ -426,16 +436,19 @@ static void orc_swiglu_bwd64(int d_ff, double g, const double *a, const double *
   }
 }
 
-/* dx += W1^T da + W3^T db. */
+/* dx += W1^T da + W3^T db: for every j the sum over c runs ascending into
+ * acc [d] (scratch), which is then added to dx; rows of W1 and W3 are walked
+ * in storage order. */
 static void orc_dx64(int d, int d_ff, const void *w1, const void *w3, size_t o13, size_t ldw13,
-                     int dtype, const double *da, const double *db, double *dx) {
-  for (int j = 0; j < d; ++j) {
-    double acc = 0.0;
-    for (int c = 0; c < d_ff; ++c)
-      acc += (double)orc_get(w1, o13 + (size_t)c * ldw13 + j, dtype) * da[c] +
-             (double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * db[c];
-    dx[j] += acc;
+                     int dtype, const double *da, const double *db, double *acc, double *dx) {
+  for (int j = 0; j < d; ++j) acc[j] = 0.0;
+  for (int c = 0; c < d_ff; ++c) {
+    const double ac = da[c], bc = db[c];
+    for (int j = 0; j < d; ++j)
+      acc[j] += (double)orc_get(w1, o13 + (size_t)c * ldw13 + j, dtype) * ac +
+                (double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * bc;
   }
+  for (int j = 0; j < d; ++j) dx[j] += acc[j];
 }
 
 /*
@@ -483,24 +496,31 @@ static int orc_expert_wgrad64(int d, int d_ff, int64_t nr, const int64_t *tok, c
     }
   }
   if (!fail) {
+    /* every output element sums its rows r in ascending order; the loops
+     * over r run outside the contiguous column loops */
 #pragma omp parallel for schedule(static)
-    for (int c = 0; c < d_ff; ++c)
-      for (int j = 0; j < d; ++j) {
-        double s1 = 0.0, s3 = 0.0;
-        for (int64_t r = 0; r < nr; ++r) {
-          s1 += DA[(size_t)r * d_ff + c] * X[(size_t)r * d + j];
-          s3 += DB[(size_t)r * d_ff + c] * X[(size_t)r * d + j];
+    for (int c = 0; c < d_ff; ++c) {
+      double *o1 = dw1 + (size_t)c * d, *o3 = dw3 + (size_t)c * d;
+      for (int j = 0; j < d; ++j) o1[j] = o3[j] = 0.0;
+      for (int64_t r = 0; r < nr; ++r) {
+        const double a = DA[(size_t)r * d_ff + c], b = DB[(size_t)r * d_ff + c];
+        const double *xr = X + (size_t)r * d;
+        for (int j = 0; j < d; ++j) {
+          o1[j] += a * xr[j];
+          o3[j] += b * xr[j];
         }
-        dw1[(size_t)c * d + j] = s1;
-        dw3[(size_t)c * d + j] = s3;
       }
+    }
 #pragma omp parallel for schedule(static)
-    for (int i = 0; i < d; ++i)
-      for (int c = 0; c < d_ff; ++c) {
-        double acc = 0.0;
-        for (int64_t r = 0; r < nr; ++r) acc += DY[(size_t)r * d + i] * HID[(size_t)r * d_ff + c];
-        dw2[(size_t)i * ldw2o + c] = acc;
+    for (int i = 0; i < d; ++i) {
+      double *o2 = dw2 + (size_t)i * ldw2o;
+      for (int c = 0; c < d_ff; ++c) o2[c] = 0.0;
+      for (int64_t r = 0; r < nr; ++r) {
+        const double y = DY[(size_t)r * d + i];
+        const double *hr = HID + (size_t)r * d_ff;
+        for (int c = 0; c < d_ff; ++c) o2[c] += y * hr[c];
       }
+    }
   }
   free(X);
   free(DY);
@@ -557,9 +577,11 @@ int oracle_layer_bwd(int64_t T, int d, int N, int m, int K, int K_s, int d_ff, i
     double *dhid = (double *)malloc(sizeof(double) * (size_t)d_ff);
     double *da = (double *)malloc(sizeof(double) * (size_t)d_ff);
     double *db = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *dxe = (double *)malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrow; ++r) {
-      if (!x || !dy || !dx || !l || !s || !ds || !a || !b || !hid || !dhid || !da || !db) {
+      if (!x || !dy || !dx || !l || !s || !ds || !a || !b || !hid || !dhid || !da || !db ||
+          !dxe) {
 #pragma omp atomic write
         fail = 1;
         continue;
@@ -583,14 +605,14 @@ int oracle_layer_bwd(int64_t T, int d, int N, int m, int K, int K_s, int d_ff, i
         for (int c = 0; c < d_ff; ++c) dg += dhid[c] * hid[c];
         ds[e] += dg;
         orc_swiglu_bwd64(d_ff, g, a, b, dhid, da, db);
-        orc_dx64(d, d_ff, w1, w3, (size_t)e * d_ff * d, (size_t)d, dtype, da, db, dx);
+        orc_dx64(d, d_ff, w1, w3, (size_t)e * d_ff * d, (size_t)d, dtype, da, db, dxe, dx);
       }
       /* shared experts, weight one */
       for (int q = 0; shared && q < K_s; ++q) {
         orc_expert_fwd64(d, d_ff, x, ws1, ws3, (size_t)q * d_ff * d, (size_t)d, ws2,
                          (size_t)q * d_ff, ldws2, dtype, dy, a, b, hid, dhid);
         orc_swiglu_bwd64(d_ff, 1.0, a, b, dhid, da, db);
-        orc_dx64(d, d_ff, ws1, ws3, (size_t)q * d_ff * d, (size_t)d, dtype, da, db, dx);
+        orc_dx64(d, d_ff, ws1, ws3, (size_t)q * d_ff * d, (size_t)d, dtype, da, db, dxe, dx);
       }
       /* softmax backward, then the router's share of du */
       double sds = 0.0;
@@ -623,20 +645,23 @@ int oracle_layer_bwd(int64_t T, int d, int N, int m, int K, int K_s, int d_ff, i
     free(dhid);
     free(da);
     free(db);
+    free(dxe);
   }
   if (fail) {
     free(DL);
     return ORC_ERR_MEM;
   }
   if (dcent) {
+    /* dcent[i][j] sums over t ascending */
 #pragma omp parallel for schedule(static)
-    for (int i = 0; i < n; ++i)
-      for (int j = 0; j < d; ++j) {
-        double acc = 0.0;
-        for (int64_t t = 0; t < T; ++t)
-          acc += DL[(size_t)t * n + i] * (double)orc_get(u, (size_t)t * d + j, dtype);
-        dcent[(size_t)i * d + j] = acc;
+    for (int i = 0; i < n; ++i) {
+      double *o = dcent + (size_t)i * d;
+      for (int j = 0; j < d; ++j) o[j] = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        const double dl = DL[(size_t)t * n + i];
+        for (int j = 0; j < d; ++j) o[j] += dl * (double)orc_get(u, (size_t)t * d + j, dtype);
       }
+    }
     free(DL);
   }
 

@@ -34,6 +34,33 @@ def test_header_declares_the_boundary():
         assert want in names
 
 
+# Section titles of the DeepSeekMoE explainer (deepforge.srivtx.xyz) that
+# define what the boundary's compute entry points do.
+PAGE_SECTIONS = ("Routing in a classic MoE layer", "Top-k routing, from affinities to gates",
+                 "Expert-level balance loss", "What the 16B configuration looks like")
+BOUNDARY = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd")
+
+
+def declaration_comment(name):
+    """The comment block right before the declaration of `name`."""
+    txt = open(HEADER).read()
+    at = re.search(r"\n(moe_status|size_t|int|const char \*)\s*" + name + r"\s*\(", txt)
+    assert at, name
+    head = txt[:at.start()]
+    end = head.rstrip().rfind("*/")
+    start = head.rfind("/*", 0, end)
+    assert end > 0 and start >= 0 and not head[end + 2:].strip(), name
+    return " ".join(head[start:end].replace("*", " ").split())
+
+
+@pytest.mark.parametrize("name", BOUNDARY)
+def test_boundary_declarations_cite_the_pages(name):
+    """Every compute entry point of the boundary names the page section that
+    defines its operation."""
+    block = declaration_comment(name)
+    assert any(f'"{sec}"' in block for sec in PAGE_SECTIONS), (name, block[:200])
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_native.LIB_PATH)
     for name in declared_functions():
@@ -85,6 +112,8 @@ def test_last_hip_error_starts_clear():
     (dict(T=1 << 29, N=64, m=1, K=8, K_s=0), "T*k overflows int32"),
     (dict(T=1 << 17, d=4096), "T*k*d reaches 2^31 elements"),
     (dict(T=1 << 18, d=64, d_ff=1408), "T*k*d_ff reaches 2^31 elements"),
+    (dict(T=1, d=65536, d_ff=32768, K_s=0, K=1, m=1, N=1), "d*d_ff reaches 2^31 elements"),
+    (dict(T=1, d=32768, d_ff=16384, K_s=4, K=5, m=1, N=1), "K_s*d_ff*d reaches 2^31"),
 ])
 def test_shape_validation(kw, why):
     p = p16(**kw)
@@ -147,6 +176,7 @@ def test_grouped_ffn_checks():
     assert status(st, p, 64, 0, *ok, 1408, 0, A, A, ws) == "MOE_ERR_SHAPE"
     assert status(st, p, 64, R, *ok, 1400, 0, A, A, ws) == "MOE_ERR_SHAPE"
     assert status(st, p, 64, R, *ok, 1408, 8, A, A, ws) == "MOE_ERR_SHAPE"   # unknown flag
+    assert status(st, p, 1, R, *ok, 1 << 20, 0, A, A, ws) == "MOE_ERR_SHAPE"  # d_ff_group*d
     assert status(st, p, 64, R + 1, *ok, 1408, 0, A, A, ws) == "MOE_ERR_WORKSPACE"
     assert status(st, p, 64, R, *ok, 1408 * 8, 0, A, A, ws) == "MOE_ERR_WORKSPACE"
     for i in range(5):
@@ -290,6 +320,26 @@ def test_layer_bwd_checks():
     assert status(call, p, no_sh_in, 0.0, no_sh_out, moe.MOE_NO_SHARED, ws - 256) == \
         "MOE_ERR_WORKSPACE"
     assert status(call, p, ins, 0.0, outs, 0, 0) == "MOE_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("kw,why", [
+    # T * ceil8(n) reaches 2^31: the bf16 softmax gradient's byte offsets
+    (dict(T=(1 << 31) // 64, d=32, d_ff=32, N=64, m=1, K=1, K_s=0), "T*ldl"),
+    # one expert's fp32 weight gradient reaches 2^31 - 16 bytes
+    (dict(T=64, d=16384, d_ff=32768, K_s=0), "d_ff*d*4"),
+    # the shared experts' fp32 weight gradient does
+    (dict(T=64, d=8192, d_ff=16384, K=2, K_s=4, m=4), "K_s*d_ff*d*4"),
+])
+def test_layer_bwd_rejects_sizes_its_offsets_cannot_reach(kw, why):
+    """Bounds of the backward's 32-bit addressing are checked on the host,
+    before anything is enqueued (MOE_ERR_SHAPE), not at a later launch."""
+    p = p16(**kw)
+    assert moe.moe_workspace_bytes(p) > 0, why  # a valid forward problem
+    ins = [A] * 11 + [None, A]
+    outs = [A] * 8
+    assert status(lambda: moe.moe_layer_bwd(p, *ins, 0.0, *outs, 0, A, BIG)) == \
+        "MOE_ERR_SHAPE", why
+    assert moe.moe_bwd_workspace_bytes(p) > 0, why
 
 
 def test_layer_bwd_kernel_sequence():

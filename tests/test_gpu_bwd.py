@@ -4,9 +4,11 @@ The oracle's gradients are pinned by finite differences of an independent
 forward (test_oracle_bwd_pins.py).  Its routing inputs (topk_idx, f) come
 from the oracle's own forward, and the GPU receives the same routing, so
 both sides differentiate the same function.  Small workloads compare every
-gradient in full; the 2B-, 16B- and 145B-shaped workloads compare du on
-sampled tokens and the weight gradients of sampled experts.  A HIP-graph capture of
-the backward replays to the eager bits.
+gradient in full; the 2B-, 16B- and 145B-shaped workloads compare the
+shared experts' weight gradients in full, the weight gradients of the most
+and the least loaded expert, and du and the centroid gradient over every
+token (2B, 16B) or du on sampled tokens (145B).  A HIP-graph capture of the
+backward replays to the eager bits.
 """
 import numpy as np
 import pytest
@@ -177,33 +179,39 @@ def test_bwd_is_deterministic():
         assert np.array_equal(a[kk].view(np.uint32), b[kk].view(np.uint32)), kk
 
 
-SAMPLED = {
-    # name: (tokens sampled, balance coefficient)
-    "16b": (24, moe_synth.BALANCE_ALPHA["16b"]),
+FULL_BWD = {
+    # name: (balance coefficient, compare every token's du and the centroid
+    # gradient in full (the oracle then runs every token's chain rule),
+    # tokens sampled for du otherwise)
+    "16b": (moe_synth.BALANCE_ALPHA["16b"], True, 0),
     # d = 1280 and d_ff = 896 are ragged against the 256-wide weight-gradient tiles
-    "2b": (16, moe_synth.BALANCE_ALPHA["2b"]),
-    # 4 shared experts (width 5632), d = 4096, Zipf-skewed loads (up to ~2000 rows)
-    "145b": (12, moe_synth.BALANCE_ALPHA["16b"]),
+    "2b": (moe_synth.BALANCE_ALPHA["2b"], True, 0),
+    # 4 shared experts (width 5632, reduced over K = T = 4096 rows), d = 4096,
+    # Zipf-skewed loads (up to ~2000 rows per expert)
+    "145b": (moe_synth.BALANCE_ALPHA["16b"], False, 12),
 }
 
 
-@pytest.mark.parametrize("name", sorted(SAMPLED))
-def test_bwd_full_size_sampled(name):
-    """The model-shaped layers: du on sampled tokens and all weight gradients
-    of the most and the least loaded expert; the centroid and shared-expert
-    gradients are checked for finiteness (in full on the small workloads)."""
+@pytest.mark.parametrize("name", sorted(FULL_BWD))
+def test_bwd_full_size(name):
+    """The model-shaped layers: the shared experts' weight gradients in full,
+    all weight gradients of the most and the least loaded routed expert, and
+    (16B, 2B) du of every token and the centroid gradient in full (the
+    16-32-chunk reduction of the centroid gradient); 145B: du on sampled
+    tokens, the centroid gradient checked for finiteness."""
     cfg = ALL[name]
     inp = inputs(name)
     r = oracle.route(inp["u"], inp["centroids"], cfg.k)
     dh = moe_synth.make_upstream_grad(cfg, seed=1)
     dh32 = (dh.astype(np.uint32) << 16).view(np.float32)
-    ntok, alpha = SAMPLED[name]
-    toks = sample_tokens(cfg.T, ntok)
+    alpha, full, ntok = FULL_BWD[name]
+    toks = np.arange(cfg.T) if full else sample_tokens(cfg.T, ntok)
     cnt = np.bincount(r["topk_idx"].ravel(), minlength=cfg.n)
     experts = np.array([int(cnt.argmax()), int(np.where(cnt > 0, cnt, cnt.max() + 1).argmin())])
     print(f"{name}: experts {experts.tolist()} with {cnt[experts].tolist()} rows", flush=True)
     want = oracle.layer_bwd(inp, cfg.N, cfg.m, cfg.K, cfg.K_s, r["topk_idx"], r["f"], dh32, alpha,
-                            toks=toks, want_dcent=False, experts=experts, want_shared=False)
+                            toks=None if full else toks, want_dcent=full, experts=experts,
+                            want_shared=True)
     got = run_bwd(cfg, inp, r, dh, alpha)
     for kk in ("dw1", "dw3", "dw2"):
         # every expert's tiles were written (the outputs start as NaN)
@@ -211,9 +219,12 @@ def test_bwd_full_size_sampled(name):
     got["du"] = got["du"][toks]
     for kk in ("dw1", "dw3", "dw2"):
         got[kk] = got[kk][experts]
-    check_all(got, want, ["du", "dw1", "dw3", "dw2"])
-    for kk in ("dcent", "dws1", "dws3", "dws2"):
-        assert np.isfinite(got[kk]).all(), kk
+    names = ["du", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2"]
+    if full:
+        names.append("dcent")
+    else:
+        assert np.isfinite(got["dcent"]).all()
+    check_all(got, want, names)
 
 
 def test_bwd_graph_replays():

@@ -4,16 +4,15 @@ Each component gets inputs derived from the oracle (never from the GPU path)
 so a failure names one kernel: routing (bit-exact indices, counts, f),
 grouping (bit-exact), the grouped SwiGLU FFN (per-slot, ungated), the
 shared experts as one dense group, the combine, and the fused layer.
-Small workloads run in full; the full-size ones compare every routing
-output and a sample of tokens for the expert sums.
+Every workload compares every token: routing outputs, per-slot expert
+outputs, the shared sum and the layer output.
 """
 import numpy as np
 import pytest
 
 import moe_synth
 import oracle
-from gpu_helpers import (ALL, FULL, REL_TOL, elem_rel, gate_tol, inputs, p_tol, rel,
-                         sample_tokens)
+from gpu_helpers import ALL, FULL, REL_TOL, elem_rel, gate_tol, inputs, p_tol, rel
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -59,8 +58,8 @@ class Case:
         r.pop("scores")
         self.route = r
         self.perm = oracle.permute(r["topk_idx"], cfg.n)
-        self.toks = sample_tokens(cfg.T, 32) if name in FULL else np.arange(cfg.T)
-        self.layer = oracle.layer(self.inp, cfg.N, cfg.m, cfg.K, cfg.K_s, toks=self.toks)
+        self.toks = np.arange(cfg.T)
+        self.layer = oracle.layer(self.inp, cfg.N, cfg.m, cfg.K, cfg.K_s)
         self.dev = {k: to_device(self.inp[k], "cuda")
                     for k in ("u", "centroids", "w1", "w3", "w2", "ws1", "ws3", "ws2")}
         self._packed = None
@@ -114,8 +113,8 @@ def test_route(case):
     assert np.array_equal(got["topk_idx"], ref["topk_idx"])
     assert np.array_equal(got["counts"], ref["counts"])
     assert np.array_equal(got["f"].view(np.uint32), ref["f"].view(np.uint32))
-    assert elem_rel(got["topk_gate"], ref["topk_gate"]) <= gate_tol(cfg.d, case.max_abs_logit)
-    assert elem_rel(got["P"], ref["P"]) <= p_tol(cfg.T, cfg.d, case.max_abs_logit)
+    assert elem_rel(got["topk_gate"], ref["topk_gate"]) <= gate_tol(cfg.d, cfg.n, case.max_abs_logit)
+    assert elem_rel(got["P"], ref["P"]) <= p_tol(cfg.T, cfg.d, cfg.n, case.max_abs_logit)
 
 
 def test_decode_cases_cover_their_paths(case):
@@ -128,6 +127,25 @@ def test_decode_cases_cover_their_paths(case):
     assert cfg.T <= 64 and cfg.T * cfg.k <= 16 * cfg.n
     if cfg.name == "decode_skew_bf16":
         assert counts.max() > 32
+
+
+def test_edge_cases_exercise_the_rule(case):
+    """The tie workloads really put an exact tie at every token's k-th choice
+    (k odd, twins adjacent: the lower index is kept, its twin dropped) and
+    inside the kept list (a pair in index order); the single-expert
+    workloads give every token gate one."""
+    cfg = case.cfg
+    idx, gate = case.route["topk_idx"], case.route["topk_gate"]
+    if cfg.tie_pairs:
+        assert cfg.k % 2 == 1
+        last = idx[:, cfg.k - 1]
+        assert (last % 2 == 0).all()
+        assert not (idx[:, :cfg.k - 1] == (last + 1)[:, None]).any()
+        assert (idx[:, 1] == idx[:, 0] + 1).all()
+    elif cfg.n == 1:
+        assert (idx == 0).all() and (gate == 1.0).all()
+    else:
+        pytest.skip("not an edge-case workload")
 
 
 @pytest.mark.parametrize("gather", [True, False])
@@ -256,8 +274,8 @@ def test_layer(case, packed):
     assert np.array_equal(out["counts"].cpu().numpy(), o["counts"])
     assert np.array_equal(out["f"].cpu().numpy().view(np.uint32), o["f"].view(np.uint32))
     lmax = case.max_abs_logit
-    assert elem_rel(out["topk_gate"].cpu().numpy(), o["topk_gate"]) <= gate_tol(cfg.d, lmax)
-    assert elem_rel(out["P"].cpu().numpy(), o["P"]) <= p_tol(cfg.T, cfg.d, lmax)
+    assert elem_rel(out["topk_gate"].cpu().numpy(), o["topk_gate"]) <= gate_tol(cfg.d, cfg.n, lmax)
+    assert elem_rel(out["P"].cpu().numpy(), o["P"]) <= p_tol(cfg.T, cfg.d, cfg.n, lmax)
     got = host(out["h"][torch.from_numpy(case.toks).to("cuda")])
     assert rel(got, o["h"]) <= exact_tol(cfg)
 

@@ -16,11 +16,13 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 MUTATIONS = {
     "silu_on_w3_branch": ("hid[c] = orc_silu(a) * b;", "hid[c] = a * orc_silu(b);"),
     "no_residual": ("h[(size_t)r * d + i] = acc + x[i];", "h[(size_t)r * d + i] = acc;"),
-    "ties_to_higher_index": ("logit[order[p - 1]] < logit[i]", "logit[order[p - 1]] <= logit[i]"),
-    "select_smallest": ("logit[order[p - 1]] < logit[i]", "logit[order[p - 1]] > logit[i]"),
+    "ties_to_higher_index": ("(best < 0 || logit[i] > logit[best])",
+                             "(best < 0 || logit[i] >= logit[best])"),
+    "select_smallest": ("(best < 0 || logit[i] > logit[best])",
+                        "(best < 0 || logit[i] < logit[best])"),
     "no_max_subtraction": ("s[i] = expf(logit[i] - mx);", "s[i] = expf(logit[i]);"),
-    "renormalised_gates": ("topk_gate[(size_t)t * k + j] = s[order[j]];",
-                           "topk_gate[(size_t)t * k + j] = s[order[j]] * (float)n / (float)k;"),
+    "renormalised_gates": ("topk_gate[(size_t)t * k + j] = s[sel[j]];",
+                           "topk_gate[(size_t)t * k + j] = s[sel[j]] * (float)n / (float)k;"),
     "w2_transposed": ("orc_get(w2, o2 + (size_t)i * ldw2 + c, dtype)",
                       "orc_get(w2, o2 + (size_t)c * d + i, dtype)"),
     "shared_dropped": ("acc += sh[i];", "acc += 0.0f;"),
@@ -42,12 +44,12 @@ MUTATIONS = {
                                       "ds[i] = alpha * (double)f[i];"),
     "dw2_from_ungated_dy": ("dy[j] = g[r] * (double)dh[(size_t)tok[r] * d + j];",
                             "dy[j] = (double)dh[(size_t)tok[r] * d + j];"),
-    "dx_w3_takes_da": ("(double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * db[c];",
-                       "(double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * da[c];"),
+    "dx_w3_takes_da": ("(double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * bc;",
+                       "(double)orc_get(w3, o13 + (size_t)c * ldw13 + j, dtype) * ac;"),
     "residual_grad_dropped": ("dx[j] = (flags & ORC_BWD_NO_RESIDUAL) ? 0.0 : dy[j];",
                               "dx[j] = 0.0;"),
-    "dcent_transposed_u": ("acc += DL[(size_t)t * n + i] * (double)orc_get(u, (size_t)t * d + j, dtype);",
-                           "acc += DL[(size_t)t * n + i] * (double)orc_get(u, (size_t)j * d + t % d, dtype);"),
+    "dcent_transposed_u": ("o[j] += dl * (double)orc_get(u, (size_t)t * d + j, dtype);",
+                           "o[j] += dl * (double)orc_get(u, (size_t)j * d + t % d, dtype);"),
 }
 
 

@@ -41,6 +41,44 @@ def test_router_inputs_are_certified(name):
     u, c, redraws = moe_synth.make_router_inputs(cfg, seed=0)
     assert u.shape == (cfg.T, cfg.d) and c.shape == (cfg.n, cfg.d)
     assert u.dtype == (np.uint16 if cfg.dtype == "bf16" else np.float32)
-    bad = moe_synth.margin_violations(moe_synth.as_f32(u), moe_synth.as_f32(c), cfg.k)
-    assert not bad.any()
-    assert redraws < cfg.T // 20 + 2
+    u32, c32 = moe_synth.as_f32(u), moe_synth.as_f32(c)
+    margin = moe_synth.certified_margin(cfg.d, moe_synth.max_abs_logit(u32, c32))
+    assert margin >= 1e-4
+    assert not moe_synth.margin_violations(u32, c32, cfg.k, margin).any()
+    # the Zipf-scaled router has logits near 100, so its margin is ~35x the
+    # floor and about a third of its tokens are redrawn; the others far fewer
+    assert redraws < (cfg.T // 2 if cfg.zipf_s else cfg.T // 20 + 2)
+
+
+def test_certified_margin_formula():
+    eps = 2.0 ** -24
+    assert moe_synth.certified_margin(64, 0.5) == 1e-4
+    assert moe_synth.certified_margin(4096, 100.0) == pytest.approx(8 * eps * 64 * 100.0)
+
+
+def test_tie_pairs_are_exact_twins_and_certified():
+    """Duplicated centroid rows give exactly tied logits; the certificate
+    skips those gaps (the tie rule decides) and checks every other one."""
+    cfg = moe_synth.MoEConfig("t", T=200, d=128, N=16, m=1, K=4, K_s=1, d_ff=64,
+                              dtype="bf16", tie_pairs=True)
+    u, c, _ = moe_synth.make_router_inputs(cfg, seed=0)
+    assert np.array_equal(c[1::2], c[0::2])
+    g = moe_synth.twin_groups(moe_synth.as_f32(c))
+    assert np.array_equal(g[0::2], g[1::2]) and len(set(g.tolist())) == cfg.n // 2
+    u32, c32 = moe_synth.as_f32(u), moe_synth.as_f32(c)
+    assert not moe_synth.margin_violations(u32, c32, cfg.k).any()
+    # the same tokens against centroids without twins: the zero gaps count
+    lg = u32.astype(np.float64) @ c32.astype(np.float64).T
+    assert (lg[:, 0::2] == lg[:, 1::2]).all()
+
+
+def test_margin_violation_is_detected():
+    """Two experts whose logits differ by less than the margin for one token."""
+    u = np.zeros((2, 32), np.float32)
+    u[:, 0] = 1.0
+    c = np.zeros((3, 32), np.float32)
+    c[0, 0], c[1, 0], c[2, 0] = 1.0, 1.0 + 5e-5, -1.0
+    u[1, 1] = 1.0
+    c[1, 1] = 1.0  # token 1 sees expert 1 a full unit above expert 0
+    bad = moe_synth.margin_violations(u, c, 1)
+    assert bad.tolist() == [True, False]
