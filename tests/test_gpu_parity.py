@@ -22,6 +22,18 @@ if torch.cuda.is_available():
     from mixture_experts_layer_34_amd.device import to_device, torch_dtype, workspace
 
 NAMES = list(ALL)
+BF16 = [n for n in NAMES if ALL[n].dtype == "bf16"]
+# (workload, packed weights): the packed layout exists for bf16 only
+LAYOUTS = [(n, False) for n in NAMES] + [(n, True) for n in BF16]
+SHARED_LAYOUTS = [(n, p) for n, p in LAYOUTS if ALL[n].K_s > 0]
+DECODE = [n for n in NAMES if n.startswith("decode")]
+EDGE = [n for n in NAMES if ALL[n].tie_pairs or ALL[n].n == 1]
+# graph replay: the small workloads and the 64-token decode shape
+GRAPH = [n for n in NAMES if n not in FULL or n == "16b_decode"]
+
+
+def lid(v):
+    return "packed" if v is True else ("rowmajor" if v is False else str(v))
 
 
 def dev():
@@ -84,8 +96,7 @@ class Case:
 
 
 def packed_flag(case, packed):
-    if packed and case.cfg.dtype != "bf16":
-        pytest.skip("packed weights are a bf16 layout")
+    assert not packed or case.cfg.dtype == "bf16"
     return moe.MOE_PACKED_WEIGHTS if packed else 0
 
 
@@ -117,35 +128,37 @@ def test_route(case):
     assert elem_rel(got["P"], ref["P"]) <= p_tol(cfg.T, cfg.d, cfg.n, case.max_abs_logit)
 
 
-def test_decode_cases_cover_their_paths(case):
+@pytest.mark.parametrize("name", DECODE)
+def test_decode_cases_cover_their_paths(name):
     """The few-rows workloads really are few rows per expert, and the skewed
     one has an expert above 32 rows (several passes over its weights)."""
-    cfg = case.cfg
-    if not cfg.name.startswith("decode"):
-        pytest.skip("not a decode workload")
-    counts = case.route["counts"]
+    cfg = ALL[name]
+    inp = inputs(name)
+    counts = oracle.route(inp["u"], inp["centroids"], cfg.k)["counts"]
     assert cfg.T <= 64 and cfg.T * cfg.k <= 16 * cfg.n
     if cfg.name == "decode_skew_bf16":
         assert counts.max() > 32
 
 
-def test_edge_cases_exercise_the_rule(case):
+@pytest.mark.parametrize("name", EDGE)
+def test_edge_cases_exercise_the_rule(name):
     """The tie workloads really put an exact tie at every token's k-th choice
     (k odd, twins adjacent: the lower index is kept, its twin dropped) and
     inside the kept list (a pair in index order); the single-expert
     workloads give every token gate one."""
-    cfg = case.cfg
-    idx, gate = case.route["topk_idx"], case.route["topk_gate"]
+    cfg = ALL[name]
+    inp = inputs(name)
+    r = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    idx, gate = r["topk_idx"], r["topk_gate"]
     if cfg.tie_pairs:
         assert cfg.k % 2 == 1
         last = idx[:, cfg.k - 1]
         assert (last % 2 == 0).all()
         assert not (idx[:, :cfg.k - 1] == (last + 1)[:, None]).any()
         assert (idx[:, 1] == idx[:, 0] + 1).all()
-    elif cfg.n == 1:
-        assert (idx == 0).all() and (gate == 1.0).all()
     else:
-        pytest.skip("not an edge-case workload")
+        assert cfg.n == 1
+        assert (idx == 0).all() and (gate == 1.0).all()
 
 
 @pytest.mark.parametrize("gather", [True, False])
@@ -169,7 +182,7 @@ def test_permute(case, gather):
         assert torch.equal(xp, u[want])
 
 
-@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("case,packed", LAYOUTS, indirect=["case"], ids=lid)
 def test_grouped_ffn_routed(case, packed):
     """y_perm[slot_of[t, j]] = FFN_{idx[t, j]}(u_t), ungated."""
     cfg, p, d = case.cfg, prob(case.cfg), "cuda"
@@ -191,13 +204,11 @@ def test_grouped_ffn_routed(case, packed):
         assert rel(got[:, j], want[:, j]) <= exact_tol(cfg), j
 
 
-@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("case,packed", SHARED_LAYOUTS, indirect=["case"], ids=lid)
 def test_grouped_ffn_shared(case, packed):
     """The K_s shared experts as one dense group of width K_s*d_ff equal the
     oracle's expert-by-expert shared sum."""
     cfg, p, d = case.cfg, prob(case.cfg), "cuda"
-    if cfg.K_s == 0:
-        pytest.skip("no shared experts")
     fl = packed_flag(case, packed)
     w = case.weights(packed)
     s = torch.empty((cfg.T, cfg.d), dtype=torch_dtype(p), device=d)
@@ -209,12 +220,11 @@ def test_grouped_ffn_shared(case, packed):
     assert rel(got, case.layer["S"]) <= exact_tol(cfg)
 
 
+@pytest.mark.parametrize("case", BF16, indirect=True)
 def test_pack_layout(case):
     """moe_pack_weights places element (r, k) of a [rows][K] matrix at
     band r/32, block k/16, offset ((r%32) + 32*((k%16)/8))*8 + k%8."""
     cfg = case.cfg
-    if cfg.dtype != "bf16":
-        pytest.skip("bf16 layout")
     src = case.inp["w2"]
     rows, K = src.shape[0] * src.shape[1], src.shape[2]
     a = src.reshape(rows, K)
@@ -265,7 +275,7 @@ def run_layer(case, flags=0, ws=None):
     return dict(h=h, topk_idx=idx, topk_gate=gate, counts=counts, f=f, P=P)
 
 
-@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("case,packed", LAYOUTS, indirect=["case"], ids=lid)
 def test_layer(case, packed):
     cfg = case.cfg
     out = run_layer(case, packed_flag(case, packed))
@@ -280,7 +290,7 @@ def test_layer(case, packed):
     assert rel(got, o["h"]) <= exact_tol(cfg)
 
 
-@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("case,packed", LAYOUTS, indirect=["case"], ids=lid)
 @pytest.mark.parametrize("flags", ["no_residual", "no_shared_no_residual"])
 def test_layer_components(case, flags, packed):
     """The residual u and the shared experts dominate |h|; dropping them checks
@@ -305,13 +315,12 @@ def test_layer_bitwise_deterministic(case):
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("case", GRAPH, indirect=True)
 def test_layer_graph_replays(case):
     """The layer captured as a HIP graph reproduces the eager bits on every
     replay, back to back and after an eager call on the same workspace, with
     junk written to the outputs before each replay."""
     cfg = case.cfg
-    if case.name in FULL and case.name != "16b_decode":
-        pytest.skip("graph replay is checked on the small and the decode workloads")
     fl = moe.MOE_PACKED_WEIGHTS if cfg.dtype == "bf16" else 0
     want = run_layer(case, fl)
     p, d = prob(cfg), "cuda"
