@@ -36,28 +36,51 @@ def flags() -> list[str]:
             "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", out]
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (device
+# code is built as usual): for CPU tests of the argument validation, with the
+# compiler's ASan runtime preloaded (host_sanitizer_runtime()).
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+            "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def host_sanitizer_runtime() -> str:
+    """Path of the ASan runtime (with the UBSan handlers) hipcc's host
+    compiler links against; preload it to load a host-sanitized libmoe.so."""
+    r = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang ASan runtime not found")
+    return path
+
+
+def _compile(src: str, obj: str = OBJ, extra=()) -> str:
+    out = os.path.join(obj, os.path.splitext(src)[0] + ".o")
+    cmd = ([hipcc()] + flags() + EXTRA.get(src, []) + list(extra) +
+           ["-c", os.path.join(CSRC, src), "-o", out])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, lib: str = LIB, sanitize_host: bool = False) -> str:
+    obj = OBJ + ("_host_san" if sanitize_host else "")
+    extra = HOST_SAN if sanitize_host else []
+    os.makedirs(obj, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, obj, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + list(extra) + \
+        ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

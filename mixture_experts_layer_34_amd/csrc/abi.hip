@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <string.h>
 
 namespace {
 
@@ -232,7 +233,11 @@ size_t moe_train_workspace_bytes(const moe_problem* p) {
 }
 
 const char* moe_status_str(moe_status s) {
-  switch (s) {
+  // A C caller may pass any int; reading an out-of-range value as the enum
+  // type is undefined in C++, so the bits are taken as an int.
+  int v = 0;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "problem sizes out of range";

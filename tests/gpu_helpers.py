@@ -12,7 +12,8 @@ import moe_synth
 #   the two sides moves g_i by a relative ~2 dl.  Two fp32 dot products of
 #   length d summed in different orders differ by about eps sqrt(d) |l|
 #   (random-walk rounding, eps = 2^-24); the bound takes eight times that at
-#   the largest logit.  On top come the two sides' exp and division (a few
+#   the largest logit (the same logit error the inputs' top-k margin
+#   certificate guards against).  On top come the two sides' exp and division (a few
 #   eps) and the sum Z of n positive terms in another order (at most
 #   (n - 1) eps relative): (n + 8) eps.  The floor is the 1e-5 the
 #   acceptance rules name for gates and P.
@@ -24,7 +25,7 @@ EPS = 2.0 ** -24
 
 
 def gate_tol(d: int, n: int, max_abs_logit: float) -> float:
-    return max(GATE_TOL, 8.0 * EPS * d ** 0.5 * max_abs_logit * 2.0 + (n + 8) * EPS)
+    return max(GATE_TOL, 8.0 * EPS * d ** 0.5 * max_abs_logit + (n + 8) * EPS)
 
 
 def p_tol(T: int, d: int, n: int, max_abs_logit: float) -> float:

@@ -124,8 +124,12 @@ def test_route(case):
     assert np.array_equal(got["topk_idx"], ref["topk_idx"])
     assert np.array_equal(got["counts"], ref["counts"])
     assert np.array_equal(got["f"].view(np.uint32), ref["f"].view(np.uint32))
-    assert elem_rel(got["topk_gate"], ref["topk_gate"]) <= gate_tol(cfg.d, cfg.n, case.max_abs_logit)
-    assert elem_rel(got["P"], ref["P"]) <= p_tol(cfg.T, cfg.d, cfg.n, case.max_abs_logit)
+    eg, ep = elem_rel(got["topk_gate"], ref["topk_gate"]), elem_rel(got["P"], ref["P"])
+    tg, tp = gate_tol(cfg.d, cfg.n, case.max_abs_logit), p_tol(cfg.T, cfg.d, cfg.n,
+                                                               case.max_abs_logit)
+    print(f"{case.name}: gate rel {eg:.2e} (bar {tg:.2e}), P rel {ep:.2e} (bar {tp:.2e})")
+    assert eg <= tg
+    assert ep <= tp
 
 
 @pytest.mark.parametrize("name", DECODE)
