@@ -193,6 +193,30 @@ moe_status moe_layer_fwd(const moe_problem *p, const void *u, const void *centro
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_layer_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument; the scratch is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends.  No call allocates; the first call on a
+ * device looks the array's address up there once.  Arguments and results are
+ * those of moe_layer_fwd (the same kernels).
+ *   - MOE_ERR_WORKSPACE: moe_workspace_bytes(p) exceeds the array (at the
+ *     16B shape, T = 64 needs 3.3 MB and about 600 tokens fill it);
+ *   - MOE_ERR_UNSUPPORTED: flags with MOE_SAVE_FOR_BACKWARD (the backward
+ *     could not name the kept workspace), or a stream that belongs to another
+ *     device than the calling thread's current one.
+ * Every call on one device shares that device's array and leaves its
+ * contents there: calls that overlap in time on one device (several streams
+ * or host threads) race; calls ordered on one stream do not.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_fwd_noalloc(const moe_problem *p, const void *u, const void *centroids,
+                                 const void *w1, const void *w3, const void *w2,
+                                 const void *ws1, const void *ws3, const void *ws2, void *h,
+                                 int32_t *topk_idx, float *topk_gate, int32_t *counts, float *f,
+                                 float *P, int flags, void *stream);
+
+/*
  * Weight layout for the grouped FFN's fast path (an implementation choice,
  * made once when weights are loaded; the layer's result does not depend on
  * it).  src is a bf16 matrix [rows][K] row-major; dst (same size, must not

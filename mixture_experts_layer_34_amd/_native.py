@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 MOE_F32, MOE_BF16 = 0, 1
 MOE_NO_RESIDUAL, MOE_NO_SHARED, MOE_PACKED_WEIGHTS, MOE_SAVE_FOR_BACKWARD = 1, 2, 4, 8
 MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 64
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,9 @@ def _load():
     lib.moe_layer_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int,
                                   P, sz, P]
     lib.moe_layer_fwd.restype = st
+    lib.moe_layer_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                          ctypes.c_int, P]
+    lib.moe_layer_fwd_noalloc.restype = st
     lib.moe_layer_fwd_marked.argtypes = lib.moe_layer_fwd.argtypes + [P]
     lib.moe_layer_fwd_marked.restype = st
     lib.moe_layer_kernels.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -196,6 +200,14 @@ def moe_layer_kernels(p, flags=0) -> list:
     names = (ctypes.c_char_p * n)()
     lib.moe_layer_kernels(ctypes.byref(p), flags, names, n)
     return [x.decode() for x in names]
+
+
+def moe_layer_fwd_noalloc(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate,
+                          counts, f, P, flags=0, stream=None):
+    _check("moe_layer_fwd_noalloc", lib.moe_layer_fwd_noalloc(
+        ctypes.byref(p), _ptr(u), _ptr(centroids), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
+        _ptr(ws3), _ptr(ws2), _ptr(h), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(f),
+        _ptr(P), flags, _stream(stream)))
 
 
 def moe_layer_fwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate,

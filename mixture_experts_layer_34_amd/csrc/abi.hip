@@ -10,6 +10,16 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
+// Scratch of moe_layer_fwd_noalloc: a fixed array that every device the
+// library runs on holds from the code object's load until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// its device address is looked up per device (scratch_on_device) and only
+// that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using moe::kRouteTok;
@@ -216,6 +226,40 @@ BwdLayout bwd_layout(const Dims& d) {
   return L;
 }
 
+// Device address of `scratch` on the device that owns `stream` (the
+// calling thread's current device for the null stream; a stream of another
+// device is refused, since the address is looked up with that device
+// current), found once per device with hipGetSymbolAddress and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status scratch_on_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    if ((int)sdev != dev) return MOE_ERR_UNSUPPORTED;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (!ptr || !aligned(ptr)) return MOE_ERR_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +434,24 @@ moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centro
                          void* ws, size_t ws_bytes, void* stream) {
   return moe_layer_fwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate,
                               counts, f, P, flags, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_fwd_noalloc(const moe_problem* p, const void* u, const void* centroids,
+                                 const void* w1, const void* w3, const void* w2,
+                                 const void* ws1, const void* ws3, const void* ws2, void* h,
+                                 int32_t* topk_idx, float* topk_gate, int32_t* counts, float* f,
+                                 float* P, int flags, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  // the backward would need the scratch's address as its fwd_ws
+  if (flags & MOE_SAVE_FOR_BACKWARD) return MOE_ERR_UNSUPPORTED;
+  if (layout(d).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_on_device(static_cast<hipStream_t>(stream), &ws)) != MOE_OK) return st;
+  return moe_layer_fwd_marked(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate,
+                              counts, f, P, flags, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream,
+                              nullptr);
 }
 
 int moe_layer_kernels(const moe_problem* p, int flags, const char** names, int max_names) {

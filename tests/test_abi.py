@@ -247,6 +247,19 @@ def test_layer_fwd_checks():
     assert status(moe.moe_layer_fwd, p, *full, 0, A, ws - 256) == "MOE_ERR_WORKSPACE"
 
 
+def test_noalloc_checks():
+    """moe_layer_fwd_noalloc refuses, on the host, problems whose workspace
+    exceeds its fixed scratch and the flag whose workspace the backward would
+    need to name; bad shapes as moe_layer_fwd."""
+    full = [A] * 14
+    assert status(moe.moe_layer_fwd_noalloc, p16(), *full, 0) == "MOE_ERR_WORKSPACE"
+    small = p16(T=64)
+    assert moe.moe_workspace_bytes(small) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert status(moe.moe_layer_fwd_noalloc, small, *full, moe.MOE_SAVE_FOR_BACKWARD) == \
+        "MOE_ERR_UNSUPPORTED"
+    assert status(moe.moe_layer_fwd_noalloc, p16(T=0), *full, 0) == "MOE_ERR_SHAPE"
+
+
 def test_workspace_grows_with_problem():
     a = moe.moe_workspace_bytes(p16())
     b = moe.moe_workspace_bytes(p16(T=8192))
