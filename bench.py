@@ -13,10 +13,15 @@ Prints one JSON line with tokens/s, the roofline of the dominant kernel
 (timed live with HIP events recorded on the launch stream), per-kernel
 times, the backward pass of the same layer (moe_layer_bwd: time per step,
 per-kernel times and its dominant kernel's roofline), the 64-token decode
-regime's HBM rate, the 2B- and 145B-shaped layers (forward and backward), a
-granularity sweep (the
-16B budget cut into m = 1, 2, 4, 8 finer experts), and the CPU oracle timed
-on a bounded sample of the same workload.
+regime's HBM rate, the 2B- and 145B-shaped layers (forward and backward),
+the small fp32 workload, a granularity sweep (the 16B budget cut into
+m = 1, 2, 4, 8 finer experts), and the CPU oracle timed on a bounded sample of
+the 16B, 2B, 145B, decode and small workloads.  Step times are the mean over
+the timed steps; the per-kernel pass (events between kernels) adds its own
+mean and the median of its per-step times.  The 16B routing is checked
+against the oracle's on every token.  A training step states the weight
+layout of each half and, where the two differ, its time with the per-step
+re-pack and with the forward on row-major weights.
 """
 from __future__ import annotations
 
@@ -201,7 +206,7 @@ class Layer:
     """Device-resident inputs, outputs and workspace of one workload."""
 
     def __init__(self, cfg, inp, weight_sets, moe, torch, flags=0):
-        from mixture_experts_layer_34_amd.device import to_device, workspace
+        from mixture_experts_layer_34_amd.device import to_device, torch_dtype, workspace
         self.moe, self.torch, self.cfg = moe, torch, cfg
         dev = "cuda"
         self.p = moe.problem(cfg.T, cfg.d, cfg.N, cfg.m, cfg.K, cfg.K_s, cfg.d_ff, cfg.dtype)
@@ -209,7 +214,7 @@ class Layer:
         self.c = (inp["centroids"] if isinstance(inp["centroids"], torch.Tensor)
                   else to_device(inp["centroids"], dev))
         self.weights = weight_sets
-        self.h = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((cfg.T, cfg.d), dtype=torch_dtype(self.p), device=dev)
         self.idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
         self.gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
         self.counts = torch.empty(cfg.n, dtype=torch.int32, device=dev)
@@ -290,25 +295,31 @@ def time_layer(layer: Layer, hip: Hip, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     per = {n: 0.0 for n in names}
     marked_total = 0.0
+    step_ms = []
     for i in range(steps):
         for j, n in enumerate(names):
             per[n] += hip.ms(marks[i][j], marks[i][j + 1]) / steps
-        marked_total += hip.ms(marks[i][0], marks[i][-1]) / steps
+        step_ms.append(hip.ms(marks[i][0], marks[i][-1]))
+        marked_total += step_ms[-1] / steps
     for row in marks:
         for e in row:
             hip.destroy(e)
     hip.destroy(e0)
     hip.destroy(e1)
+    step_ms.sort()
+    median = (step_ms[(steps - 1) // 2] + step_ms[steps // 2]) / 2
     return dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, kernel_ms=per,
-                marked_ms_per_step=marked_total, kernels=names)
+                marked_ms_per_step=marked_total, marked_median_ms_per_step=median,
+                kernels=names)
 
 
-def gpu_shape_inputs(cfg, seed, torch, moe, copies):
+def gpu_shape_inputs(cfg, seed, torch, moe, copies, host=None):
     """Inputs of a workload drawn on the GPU (seeded torch normals) with the
     workload's distributions: u ~ N(0,1); centroids ~ N(0, cent_std) (1/sqrt(d)
     by default) with Zipf-scaled rows where the workload says so; weights
     ~ N(0, w_std); bf16, weights packed.  For timing only: unlike the parity
-    inputs, the top-k margins are not certified."""
+    inputs, the top-k margins are not certified.  host (a dict): receives the
+    first copy's row-major values as bf16 bit patterns (for the CPU oracle)."""
     import math
 
     import moe_synth
@@ -333,19 +344,30 @@ def gpu_shape_inputs(cfg, seed, torch, moe, copies):
         st = {"ws1": None, "ws3": None, "ws2": None}
         for name, shape in shapes:
             src = (torch.randn(shape, generator=g, device="cuda") * cfg.w_std).to(bf)
+            if host is not None and not sets:
+                host[name] = src.view(torch.int16).cpu().numpy().view("uint16")
             dst = torch.empty_like(src)
             moe.moe_pack_weights(p, src.numel() // shape[-1], shape[-1], src, dst)
             del src
             st[name] = dst
         sets.append(st)
     torch.cuda.synchronize()
+    if host is not None:
+        host["u"] = u.view(torch.int16).cpu().numpy().view("uint16")
+        host["centroids"] = c.view(torch.int16).cpu().numpy().view("uint16")
+        for name in ("ws1", "ws3", "ws2"):
+            host.setdefault(name, None)
     return {"u": u, "centroids": c}, sets
 
 
-def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=None) -> dict:
+def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=None,
+                cpu_seconds=0.0) -> dict:
     """Layer tokens/s and grouped-GEMM MFMA fraction of one more model shape;
-    with bwd_alpha, also its backward pass on the same (packed) weights."""
-    inp, sets = gpu_shape_inputs(cfg, 0, torch, moe, copies=1 if cfg.n * cfg.d_ff * cfg.d > 5e8 else 2)
+    with bwd_alpha, also its backward pass on the same (packed) weights; with
+    cpu_seconds, the CPU oracle on a bounded sample of the same inputs."""
+    host = {} if cpu_seconds else None
+    inp, sets = gpu_shape_inputs(cfg, 0, torch, moe,
+                                 copies=1 if cfg.n * cfg.d_ff * cfg.d > 5e8 else 2, host=host)
     layer = Layer(cfg, inp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
     res = time_layer(layer, hip, steps, warmup)
     counts = layer.counts.cpu().numpy()
@@ -359,50 +381,64 @@ def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=
                                                           if cfg.zipf_s else ""),
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
         "ms_per_step": round(ms, 4),
+        "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
+        "median_ms_per_step": round(res["marked_median_ms_per_step"], 4),
         "grouped_gemm_tflops": round(gemm_flop / gemm_s / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flop / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "max_expert_rows": int(counts.max()),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in res["kernel_ms"].items()},
         "inputs": "drawn on the GPU (seeded normals of the workload's distributions)",
     }
+    if host:
+        out["cpu_baseline"] = cpu_baseline(cfg, host, cpu_seconds)
+        out["gpu_over_cpu_oracle"] = round(out["tokens_per_s"] / out["cpu_baseline"]["value"], 1)
     if bwd_alpha is not None:
         b = backward_regime(torch, moe, hip, args, cfg, None, layer, packed=True, alpha=bwd_alpha,
                             steps=max(5, steps // 2))
         out["backward"] = {k: b[k] for k in ("ms_per_step", "tokens_per_s", "gemm_mfma_frac",
-                                             "weight_layout", "roofline", "train_step_ms")}
+                                             "weight_layout", "roofline", "train_step")}
         out["backward"]["kernel_us"] = {k: v["us"] for k, v in b["kernels"].items()}
         b = backward_regime(torch, moe, hip, args, cfg, None, layer, packed=True, alpha=bwd_alpha,
                             steps=max(5, steps // 2), saved=True)
         out["backward_saved"] = {k: b[k] for k in ("ms_per_step", "tokens_per_s", "a_b",
-                                                   "train_step_ms")}
+                                                   "train_step")}
         out["backward_saved"]["kernel_us"] = {k: v["us"] for k, v in b["kernels"].items()}
     del layer, sets, inp
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(cfg, inp, seconds: float) -> dict:
+def cpu_baseline(cfg, inp, seconds: float, repeats: int = 1) -> dict:
     """The oracle on the first T_s tokens of the workload as their own batch
-    (the whole batch when it fits the time budget).  The probe is large
-    enough to keep every host thread busy, so its per-token cost holds for
-    the sample."""
+    (the whole batch when it fits the time budget; seconds = 0: the whole
+    batch).  The probe is large enough to keep every host thread busy, so its
+    per-token cost holds for the sample (tokens are dealt to threads
+    dynamically).  repeats > 1: the median of that many
+    runs."""
     import numpy as np
 
     import oracle
     sub = dict(inp)
-    probe = min(cfg.T, 256)
-    sub["u"] = np.ascontiguousarray(inp["u"][:probe])
-    t0 = time.perf_counter()
-    oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
-    per_tok = (time.perf_counter() - t0) / probe
-    ts = int(max(probe, min(cfg.T, seconds / max(per_tok, 1e-9))))
+    if seconds > 0:
+        probe = min(cfg.T, 256, max(64, 4 * oracle.threads()))
+        sub["u"] = np.ascontiguousarray(inp["u"][:probe])
+        t0 = time.perf_counter()
+        oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
+        per_tok = (time.perf_counter() - t0) / probe
+        ts = int(max(probe, min(cfg.T, seconds / max(per_tok, 1e-9))))
+    else:
+        ts = cfg.T
     sub["u"] = np.ascontiguousarray(inp["u"][:ts])
-    t0 = time.perf_counter()
-    oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
-    el = time.perf_counter() - t0
+    runs = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.layer(sub, cfg.N, cfg.m, cfg.K, cfg.K_s)
+        runs.append(time.perf_counter() - t0)
+    el = sorted(runs)[(repeats - 1) // 2]
+    how = f"median of {repeats} runs" if repeats > 1 else "one run"
     return dict(value=round(ts / el, 2), unit="tokens/s", cores=oracle.threads(), kind="oracle",
                 sample=f"first {ts} of {cfg.T} tokens as one batch (routing + all experts), "
-                       f"{el:.1f} s")
+                       f"{el:.2f} s, {how}")
 
 
 def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
@@ -413,10 +449,12 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
     dcfg = moe_synth.CONFIGS["16b_decode"]
     log("timing the 64-token decode regime")
     if sets is None:
-        dinp, sets = gpu_shape_inputs(dcfg, 0, torch, moe, copies=args.rotate)
+        host = {}
+        dinp, sets = gpu_shape_inputs(dcfg, 0, torch, moe, copies=args.rotate, host=host)
     else:
         du, dc, _ = moe_synth.make_router_inputs(dcfg, seed=0)
         dinp = dict(inp, u=du, centroids=dc)
+        host = dinp
     dl = Layer(dcfg, dinp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
     dres = time_layer(dl, hip, max(args.steps, 20), args.warmup)
     gms = time_graph(dl, max(args.steps, 20), args.warmup)
@@ -425,9 +463,11 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
     dbytes = sum(dwork[name]["bytes"] for name in dres["kernels"])  # the launched kernels
     dms = dres["ms_per_step"]
     del dl
-    return {
+    out = {
         "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
         "ms_per_step": round(dms, 4),
+        "marked_ms_per_step": round(dres["marked_ms_per_step"], 4),
+        "median_ms_per_step": round(dres["marked_median_ms_per_step"], 4),
         "algorithmic_bytes": int(dbytes),
         "hbm_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
         "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -437,6 +477,10 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
         "graph_hbm_GBps": round(dbytes / (gms * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in dres["kernel_ms"].items()},
     }
+    if not getattr(args, "no_cpu_baseline", False):
+        out["cpu_baseline"] = cpu_baseline(dcfg, host, 0.0, repeats=5)
+        out["gpu_over_cpu_oracle"] = round(out["tokens_per_s"] / out["cpu_baseline"]["value"], 1)
+    return out
 
 
 def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=None,
@@ -522,6 +566,46 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
     rec(e1, stream)
     torch.cuda.synchronize()
     train_ms = hip.ms(e0, e1) / steps
+    train = {"ms": round(train_ms, 4), "forward_weights": "packed",
+             "backward_weights": "packed" if packed else "row-major"}
+    if not packed:
+        # A weight update changes the row-major weights; the forward's packed
+        # copies then have to be packed again every step ...
+        names6 = [k for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2") if sets[0][k] is not None]
+
+        def repack(i):
+            src, dst = sets[i % len(sets)], layer.weights[i % len(layer.weights)]
+            for k in names6:
+                moe.moe_pack_weights(p, src[k].numel() // src[k].shape[-1], src[k].shape[-1],
+                                     src[k], dst[k], stream=stream)
+        torch.cuda.synchronize()
+        rec(e0, stream)
+        for i in range(steps):
+            layer.run(i, extra_flags=sv, ws=fws)
+            run(i)
+            repack(i)
+        rec(e1, stream)
+        torch.cuda.synchronize()
+        train["ms_with_repack"] = round(hip.ms(e0, e1) / steps, 4)
+        # ... or the forward reads the row-major weights directly.
+        fl_rm = (layer.flags & ~moe.MOE_PACKED_WEIGHTS) | sv
+
+        def fwd_rm(i):
+            w = sets[i % len(sets)]
+            moe.moe_layer_fwd(p, layer.u, layer.c, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"],
+                              w["ws2"], layer.h, layer.idx, layer.gate, layer.counts, layer.f,
+                              layer.P, fl_rm, layer.ws if fws is None else fws, stream=stream)
+        for i in range(2):
+            fwd_rm(i)
+            run(i)
+        torch.cuda.synchronize()
+        rec(e0, stream)
+        for i in range(steps):
+            fwd_rm(i)
+            run(i)
+        rec(e1, stream)
+        torch.cuda.synchronize()
+        train["ms_row_major_forward"] = round(hip.ms(e0, e1) / steps, 4)
     hip.destroy(e0)
     hip.destroy(e1)
     n_active = int((layer.counts.cpu().numpy() > 0).sum())
@@ -547,8 +631,51 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
         "kernels": kern,
         "weight_layout": "packed" if packed else "row-major",
         "a_b": "kept by the forward (bf16)" if saved else "computed again",
-        "train_step_ms": round(train_ms, 4),
+        "train_step": train,
     }
+
+
+def tiny_regime(torch, moe, hip, args) -> dict:
+    """The small fp32 workload the oracle finishes in milliseconds (64
+    tokens, d = 64, 16 routed experts top-3 + 1 shared, d_ff = 32): GPU
+    tokens/s on row-major fp32 weights beside the oracle's on the whole
+    batch."""
+    import moe_synth
+    from mixture_experts_layer_34_amd.device import to_device
+    cfg = moe_synth.CONFIGS["tiny"]
+    inp = moe_synth.make_inputs(cfg, seed=0)
+    sets = [{k: to_device(inp[k], "cuda") for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}]
+    layer = Layer(cfg, inp, sets, moe, torch, 0)
+    res = time_layer(layer, hip, max(args.steps, 50), args.warmup)
+    ms = res["ms_per_step"]
+    out = {
+        "workload": f"tiny: T={cfg.T}, d={cfg.d}, {cfg.n} routed (top-{cfg.k}) + {cfg.K_s} shared,"
+                    f" SwiGLU d_ff={cfg.d_ff}, fp32, row-major weights",
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4),
+        "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
+        "median_ms_per_step": round(res["marked_median_ms_per_step"], 4),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in res["kernel_ms"].items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, 0.0, repeats=21)
+        out["gpu_over_cpu_oracle"] = round(out["tokens_per_s"] / out["cpu_baseline"]["value"], 1)
+    del layer, sets
+    return out
+
+
+def routing_mismatches(cfg, inp, layer) -> dict:
+    """Top-k choices of the timed layer against the oracle's routing of the
+    same inputs (the margin certificate of the inputs makes them unique):
+    tokens whose chosen set differs, and the inputs' margin redraws."""
+    import numpy as np
+
+    import oracle
+    ref = oracle.route(inp["u"], inp["centroids"], cfg.k)
+    got = layer.idx.cpu().numpy()
+    diff = int((np.sort(got, axis=1) != np.sort(ref["topk_idx"], axis=1)).any(axis=1).sum())
+    return {"tokens_compared": int(cfg.T), "tokens_mismatched": diff,
+            "margin_redraws": int(inp.get("redraws", 0))}
 
 
 def main():
@@ -661,9 +788,11 @@ def main():
         "grouped_gemm_mfma_frac": round(gemm_flop / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels": kern,
         "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
+        "median_ms_per_step": round(res["marked_median_ms_per_step"], 4),
         "weight_pack_ms_once": round(pack_ms, 3),
         "wall_ms_per_step": round(res["wall_ms_per_step"], 4),
     }
+    out["routing_check"] = routing_mismatches(cfg, inp, layer)
     if not args.no_backward:
         out["backward_16b"] = backward_regime(torch, moe, hip, args, cfg, inp, layer)
         out["backward_16b_saved"] = backward_regime(torch, moe, hip, args, cfg, inp, layer,
@@ -677,7 +806,10 @@ def main():
             log(f"timing the {name}-shaped layer")
             out["other_shapes"][name] = other_shape(
                 name, moe_synth.CONFIGS[name], torch, moe, hip, max(10, args.steps // 3), 3, args,
-                moe_synth.BALANCE_ALPHA["2b" if name == "2b" else "16b"])
+                moe_synth.BALANCE_ALPHA["2b" if name == "2b" else "16b"],
+                cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 3)
+    log("timing the tiny fp32 workload")
+    out["tiny"] = tiny_regime(torch, moe, hip, args)
     if not args.no_granularity:
         # Fine-grained segmentation at a fixed expert budget (total and
         # activated widths constant; m = 1 is GShard's top-2 layer): the cost
