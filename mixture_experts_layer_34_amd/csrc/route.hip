@@ -79,47 +79,57 @@ __device__ __forceinline__ float row_sum(float v) {
   v += dppf<kHalfMirror>(v);
   return v + dppf<kMirror>(v);
 }
-// Arg-max with ties to the lower index (a total order, so the butterfly
-// gives every lane the same winner).
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = dppf<CTRL>(v);
-  const int oi = dpp<CTRL>(i);
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+// Selection keys: the logit's bits made order-preserving as an unsigned
+// integer (-0 folded into +0 first, so equal values give equal high words)
+// above the complement of the expert index.  Larger key = larger logit, and
+// among equal logits the lower index; 0 is below every real key and marks a
+// taken or absent expert.  Keys are unique, so an unsigned max is the rule's
+// arg-max with no tie branch.
+__device__ __forceinline__ uint64_t topk_key(float v, int i) {
+  uint32_t b = __float_as_uint(v + 0.0f);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
-__device__ __forceinline__ void row_argmax(float& v, int& i) {
-  argmax_step<kQuadX1>(v, i);
-  argmax_step<kQuadX2>(v, i);
-  argmax_step<kHalfMirror>(v, i);
-  argmax_step<kMirror>(v, i);
+__device__ __forceinline__ int topk_key_index(uint64_t key) {
+  return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
+  const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t row_max_key(uint64_t x) {
+  x = umax64(x, dpp64<kQuadX1>(x));
+  x = umax64(x, dpp64<kQuadX2>(x));
+  x = umax64(x, dpp64<kHalfMirror>(x));
+  return umax64(x, dpp64<kMirror>(x));
 }
 
-// Block histogram and in-block ranks.  Lanes 0..15 of every wave stand for
-// the block's 16 tokens; wave w handles the experts e = w, w + 8, ...
+// Block histogram and in-block ranks.  Lanes 0..15 of waves 0..HW-1 stand
+// for the block's 16 tokens; wave w handles the experts e = w, w + HW, ...
+// (the route kernel's upper waves sum P meanwhile: HW = 4 there).
+template <int HW = kWaves>
 __device__ void block_hist_rank(const RouteSmem& s, int n, int k, int64_t blk, int64_t T,
                                 int32_t* blk_cnt, int32_t* lrank) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;
-  if (lane < kRouteTok) {
+  if (wave < HW && lane < kRouteTok) {
     for (int j = 0; j < k; ++j) {
       const int e = s.sidx[lane * k + j];
-      if (e < 0) continue;
-      const uint64_t b = 1ull << (e & 63);
-      switch (e >> 6) {
-        case 0: bits0 |= b; break;
-        case 1: bits1 |= b; break;
-        case 2: bits2 |= b; break;
-        default: bits3 |= b; break;
-      }
+      const uint64_t b = e >= 0 ? 1ull << (e & 63) : 0ull;
+      const int w = e >> 6;
+      bits0 |= w == 0 ? b : 0ull;
+      bits1 |= w == 1 ? b : 0ull;
+      bits2 |= w == 2 ? b : 0ull;
+      bits3 |= w >= 3 ? b : 0ull;
     }
   }
   int* rk = reinterpret_cast<int*>(s.lg);
   const uint64_t below = (1ull << lane) - 1ull;
   const int ldn = blk_ld(n);
-  for (int e = wave; e < n; e += kWaves) {
+  for (int e = wave; wave < HW && e < n; e += HW) {
     const int w = e >> 6;
     const uint64_t word = w == 0 ? bits0 : (w == 1 ? bits1 : (w == 2 ? bits2 : bits3));
     const bool has = (word >> (e & 63)) & 1ull;
@@ -370,30 +380,25 @@ __device__ __forceinline__ void token_topk(const float* row, float* srow, int* s
     z += ev[r];
   }
   z = row_sum(z);
+  // one correctly rounded reciprocal, then a product per expert (one more
+  // rounding than a division, far inside the gates' bar)
+  const float rz = 1.0f / z;
 #pragma unroll
   for (int r = 0; r < NB; ++r)
-    if (q + 16 * r < n) srow[q + 16 * r] = ev[r] / z;
-  // k rounds of a row arg-max; each lane scans its experts in ascending
-  // order, so a strict '>' keeps the lower index among equal logits, and a
-  // taken expert's logit becomes -inf.
+    if (q + 16 * r < n) srow[q + 16 * r] = ev[r] * rz;
+  // k rounds of a row arg-max over the selection keys (larger logit, then
+  // lower index); the winner's key becomes 0 in the lane that holds it.
+  uint64_t key[NB];
+#pragma unroll
+  for (int r = 0; r < NB; ++r) key[r] = q + 16 * r < n ? topk_key(v[r], q + 16 * r) : 0ull;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int r = 0; r < NB; ++r) {
-      if (v[r] > bv) {
-        bv = v[r];
-        bi = q + 16 * r;
-      }
-    }
-    row_argmax(bv, bi);
-    if ((bi & 15) == q) {
-      const int rr = bi >> 4;
+    for (int r = 1; r < NB; ++r) best = umax64(best, key[r]);
+    best = row_max_key(best);
 #pragma unroll
-      for (int r = 0; r < NB; ++r)
-        if (r == rr) v[r] = -INFINITY;
-    }
-    if (q == 0) sidx[j] = valid ? bi : -1;
+    for (int r = 0; r < NB; ++r) key[r] = key[r] == best ? 0ull : key[r];
+    if (q == 0) sidx[j] = valid ? topk_key_index(best) : -1;
   }
   // The row's lanes write the kept experts and their gates together (the
   // rounds above carry no memory wait).
@@ -419,19 +424,22 @@ __device__ void route_tail(int64_t T, int n, int k, int64_t blk, const RouteSmem
                    t, topk_idx, topk_gate);
   }
   __syncthreads();
-  // P partial of this block, tokens ascending.
-  for (int i = tid; i < n; i += kThreads) {
-    float vals[kRouteTok];
-#pragma unroll
-    for (int tl = 0; tl < kRouteTok; ++tl)
-      vals[tl] = blk * kRouteTok + tl < T ? s.sv[tl * s.ldl + i] : 0.f;
+  // P partial of this block, tokens ascending (waves 4..7, while waves 0..3
+  // form the histogram).
+  const int ldn = blk_ld(n);
+  for (int i = tid - kThreads / 2; i >= 0 && i < ldn; i += kThreads / 2) {
     float acc = 0.f;
+    if (i < n) {
+      float vals[kRouteTok];
 #pragma unroll
-    for (int tl = 0; tl < kRouteTok; ++tl) acc += vals[tl];
-    blk_P[blk * blk_ld(n) + i] = acc;
+      for (int tl = 0; tl < kRouteTok; ++tl)
+        vals[tl] = blk * kRouteTok + tl < T ? s.sv[tl * s.ldl + i] : 0.f;
+#pragma unroll
+      for (int tl = 0; tl < kRouteTok; ++tl) acc += vals[tl];
+    }
+    blk_P[blk * ldn + i] = acc;
   }
-  if (tid < blk_ld(n) - n) blk_P[blk * blk_ld(n) + n + tid] = 0.f;
-  block_hist_rank(s, n, k, blk, T, blk_cnt, lrank);
+  block_hist_rank<kWaves / 2>(s, n, k, blk, T, blk_cnt, lrank);
 }
 
 template <int NB, bool STAGED>
@@ -485,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
     s.sidx[p] = (e >= 0 && e < n) ? e : -1;
   }
   __syncthreads();
-  block_hist_rank(s, n, k, blk, T, blk_cnt, lrank);
+  block_hist_rank<kWaves>(s, n, k, blk, T, blk_cnt, lrank);
 }
 
 // ---------------------------------------------------------------- scans
@@ -717,13 +725,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
 // Grouping in one pass of B workgroups, one per route block: every
 // workgroup reads the whole [B][ldn] histogram table (small: a few tens of
-// KB), forms the per-expert totals and its own block's prefix, hence the
-// expert offsets and its block's bases, and scatters its tokens' (t, j)
-// pairs.  Workgroup 0 also writes counts, f, P and offsets, the last
-// workgroup the M-tile list.
+// KB) in one batch of loads, forms the per-expert totals and its own block's
+// prefix, hence the expert offsets and its block's bases, and scatters its
+// tokens' (t, j) pairs.  Workgroup b also sums column b of the P partials
+// (experts b, b + B, ... when n > B), workgroup 0 writes counts, f and
+// offsets, the last workgroup the M-tile list.
 // Every workgroup derives the same totals (exact integer sums), so no
 // workgroup waits for another.
 constexpr int kGroupThreads = 256;
+constexpr int kGroupRows = 16;  // table rows a thread has in flight
 
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(
     const int32_t* __restrict__ blk_cnt, const float* __restrict__ blk_P, int B, int64_t T,
@@ -737,7 +747,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
   __shared__ int s_toff[kMaxExperts + 1];
   __shared__ int wsum[4];
   __shared__ int s_total;
-  const int tid = threadIdx.x, blk = blockIdx.x;
+  __shared__ float s_red[kGroupThreads / 64];
+  const int tid = threadIdx.x, blk = blockIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ldn = blk_ld(n), n4 = ldn >> 2;
   int C = 1;  // row chunks per column: a power of two, n4 * C <= 256
   while (C * 2 * n4 <= kGroupThreads && C * 2 <= 64) C *= 2;
@@ -747,31 +758,32 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
   const int r0 = c * per < B ? c * per : B;
   const int r1 = r0 + per < B ? r0 + per : B;
   const int64_t col = 4 * e4;
-  // Workgroup 0 also sums the P partials, rows ascending inside a chunk,
-  // then a fixed butterfly over chunks; its P rows load in the same batches
-  // as the count rows.
-  const bool with_P = blk == 0 && blk_P;
+  // This block's first (token, slot) pairs and its first P column are loaded
+  // with the table (P rows ascending per thread).
+  int e_first = -1, rank_first = 0;
+  {
+    const int64_t t = (int64_t)blk * kRouteTok + tid / k;
+    if (tid < kRouteTok * k && t < T) {
+      const int64_t p = t * k + tid % k;
+      e_first = topk_idx[p];
+      rank_first = lrank[p];
+    }
+  }
+  const bool with_P = blk_P && P && blk < n;
+  float p_first = 0.f;
+  if (with_P && tid < B) p_first = blk_P[(int64_t)tid * ldn + blk];
   i32x4 tot = {0, 0, 0, 0}, pre = {0, 0, 0, 0};
-  f32x4v ps = {0.f, 0.f, 0.f, 0.f};
   if (act) {
-    // eight rows in flight at a time
-    for (int rb = r0; rb < r1; rb += 8) {
-      i32x4 v[8];
-      f32x4v pv[8];
+    for (int rb = r0; rb < r1; rb += kGroupRows) {
+      i32x4 v[kGroupRows];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool in = rb + i < r1;
-        v[i] = in ? *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)(rb + i) * ldn + col)
-                  : i32x4{0, 0, 0, 0};
-        pv[i] = in && with_P
-                    ? *reinterpret_cast<const f32x4v*>(blk_P + (int64_t)(rb + i) * ldn + col)
-                    : f32x4v{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int i = 0; i < kGroupRows; ++i)
+        v[i] = rb + i < r1 ? *reinterpret_cast<const i32x4*>(blk_cnt + (int64_t)(rb + i) * ldn + col)
+                           : i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kGroupRows; ++i) {
         tot += v[i];
         if (rb + i < blk) pre += v[i];
-        ps += pv[i];  // rows ascending
       }
     }
   }
@@ -790,13 +802,22 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
         s_base[col + q] = pre[q];
       }
   }
-  if (with_P) {
-    for (int m = C >> 1; m >= 1; m >>= 1) ps += shfl_xor4(ps, m, C);
-    if (act && c == 0) {
+  // P_e = (column sum of the block partials) / T: a fixed butterfly inside
+  // each wave, then the waves in order.
+  for (int e = blk; with_P && e < n; e += B) {
+    float pacc = e == blk ? p_first : 0.f;
+    for (int r = e == blk ? tid + kGroupThreads : tid; r < B; r += kGroupThreads)
+      pacc += blk_P[(int64_t)r * ldn + e];
+    for (int m = 32; m >= 1; m >>= 1) pacc += __shfl_xor(pacc, m, 64);
+    if (lane == 0) s_red[wave] = pacc;
+    __syncthreads();
+    if (tid == 0) {
+      float acc = s_red[0];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (col + q < n && P) P[col + q] = ps[q] / (float)T;
+      for (int w = 1; w < kGroupThreads / 64; ++w) acc += s_red[w];
+      P[e] = acc / (float)T;
     }
+    __syncthreads();
   }
   __syncthreads();
   const int cnt_e = tid < n ? s_tot[tid] : 0;
@@ -822,16 +843,17 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
     const int64_t t = (int64_t)blk * kRouteTok + q / k;
     if (t >= T) break;
     const int64_t p = t * k + q % k;
-    const int e = topk_idx[p];
+    const int e = q == tid ? e_first : topk_idx[p];
     int pos = -1;
     if (e >= 0 && e < n) {
-      pos = s_base[e] + lrank[p];
+      pos = s_base[e] + (q == tid ? rank_first : lrank[p]);
       if (pos < 0 || pos >= R) pos = -1;
     }
     slot_of[p] = pos;
     if (pos >= 0) perm_token[pos] = (int32_t)t;
   }
-  // The M-tile list: the last workgroup (workgroup 0 has the P sums).
+  // The M-tile list: the last workgroup (workgroup 0 writes counts, f and
+  // offsets).
   if (blk != B - 1 || !tl.off) return;
   emit_tile_list(tl, n, s_tot, s_off, s_toff, wsum, &s_total, kGroupThreads);
 }
@@ -912,32 +934,35 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
                      topk_idx, topk_gate);
   }
   __syncthreads();
-  // P: the 16 lanes of a DPP row take one expert; lane q sums tokens q,
-  // q + 16, ... ascending, then a fixed butterfly adds the 16 partial sums.
-  for (int e0 = tid >> 4; e0 < n; e0 += kSmallThreads / 16) {
-    const int q = tid & 15;
+  // P (waves 0..7): the 8 lanes of a half row take one expert; lane q sums
+  // tokens q, q + 8, ... ascending, then a fixed butterfly adds the 8
+  // partial sums.  Meanwhile waves 8..15 count and rank.
+  constexpr int kHalf = kSmallThreads / 2;
+  for (int e0 = tid >> 3; tid < kHalf && e0 < n; e0 += kHalf / 8) {
+    const int q = tid & 7;
     float acc = 0.f;
-    for (int t = q; t < T; t += 16) acc += s_sv[t * ldl + e0];
-    acc = row_sum(acc);
+    for (int t = q; t < T; t += 8) acc += s_sv[t * ldl + e0];
+    acc += dppf<kQuadX1>(acc);
+    acc += dppf<kQuadX2>(acc);
+    acc += dppf<kHalfMirror>(acc);
     if (q == 0) P[e0] = acc / (float)T;
   }
-  // Counts and ranks: wave w takes experts w, w + 16, ...; lane = token.
-  {
-    const int lane = tid & 63, wave = tid >> 6;
+  // Counts and ranks: wave 8 + w takes experts w, w + 8, ...; lane = token.
+  if (tid >= kHalf) {
+    const int lane = tid & 63, wave = (tid - kHalf) >> 6;
     uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;  // this token's experts
     if (lane < T)
       for (int j = 0; j < k; ++j) {
         const int e = s_idx[lane * k + j];
         const uint64_t b = 1ull << (e & 63);
-        switch (e >> 6) {
-          case 0: bits0 |= b; break;
-          case 1: bits1 |= b; break;
-          case 2: bits2 |= b; break;
-          default: bits3 |= b; break;
-        }
+        const int w = e >> 6;
+        bits0 |= w == 0 ? b : 0ull;
+        bits1 |= w == 1 ? b : 0ull;
+        bits2 |= w == 2 ? b : 0ull;
+        bits3 |= w >= 3 ? b : 0ull;
       }
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int e = wave; e < n; e += kSmallThreads / 64) {
+    for (int e = wave; e < n; e += kHalf / 64) {
       const int w = e >> 6;
       const uint64_t word = w == 0 ? bits0 : (w == 1 ? bits1 : (w == 2 ? bits2 : bits3));
       const bool has = (word >> (e & 63)) & 1ull;
