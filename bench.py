@@ -449,7 +449,7 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
     dcfg = moe_synth.CONFIGS["16b_decode"]
     log("timing the 64-token decode regime")
     if sets is None:
-        host = {}
+        host = None if getattr(args, "no_cpu_baseline", False) else {}
         dinp, sets = gpu_shape_inputs(dcfg, 0, torch, moe, copies=args.rotate, host=host)
     else:
         du, dc, _ = moe_synth.make_router_inputs(dcfg, seed=0)
@@ -691,6 +691,8 @@ def main():
                     help="skip the 16B-shaped backward pass")
     ap.add_argument("--no-other-shapes", action="store_true",
                     help="skip the 2B- and 145B-shaped layers")
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the small fp32 workload")
     ap.add_argument("--no-granularity", action="store_true",
                     help="skip the granularity sweep (m = 1, 2, 4, 8 at a fixed budget)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -808,8 +810,9 @@ def main():
                 name, moe_synth.CONFIGS[name], torch, moe, hip, max(10, args.steps // 3), 3, args,
                 moe_synth.BALANCE_ALPHA["2b" if name == "2b" else "16b"],
                 cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 3)
-    log("timing the tiny fp32 workload")
-    out["tiny"] = tiny_regime(torch, moe, hip, args)
+    if not args.no_tiny:
+        log("timing the tiny fp32 workload")
+        out["tiny"] = tiny_regime(torch, moe, hip, args)
     if not args.no_granularity:
         # Fine-grained segmentation at a fixed expert budget (total and
         # activated widths constant; m = 1 is GShard's top-2 layer): the cost
