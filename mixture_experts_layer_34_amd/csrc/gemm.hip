@@ -207,87 +207,93 @@ struct PipeLds {
 // Weights in the packed layout (see pack_kernel): each wave loads its own
 // weight fragments straight into registers with coalesced 1 KB loads, two
 // slices ahead; only the activations (shared by the 4 waves) go through LDS.
-// Every slice is 8*NBW steps, one MFMA each, fenced so the compiler keeps
-// this order: MFMA i covers weight band nb = i%NBW, then row block
+// Activations move in pairs of slices: one load instruction covers 8 rows x
+// 128 bytes (a whole cache line per row, where a single slice would use half
+// of each line and leave the other half to be fetched again), staged in
+// registers two slices ahead and stored into one of two LDS pair buffers.
+// Every slice is 8*NBW fenced steps, one MFMA each, fenced so the compiler
+// keeps this order: MFMA i covers weight band nb = i%NBW, then row block
 // mi = (i/NBW)%4, then k half kk = i/(4*NBW) (an accumulator is reused
 // 4*NBW MFMAs later; consecutive MFMAs share the activation fragment).
 //   after the last MFMA of an activation fragment: read the next slice's
 //                fragment into the same registers (one fragment set)
 //   after the last MFMA of a weight fragment (row block 3): reload it with
 //                slice s+2's
-//   step kAst    store the staged activations of slice s+2 into LDS
-//   step kAst+2  load the activations of slice s+4 into that staging set
+//   even slices only, step kAst: store the staged pair p+1 into LDS;
+//                step kAst+2: load pair p+2 into that staging set
 template <bool UP, int NBW>
 struct PipePacked {
   static constexpr int kSteps = 8 * NBW;
   static constexpr int kAst = kSteps - 12 + (NBW == 2 ? 2 : 0);  // 20 (NBW 4), 10 (NBW 2)
+  static constexpr int kPairElems = 2 * BM * LDK;                // one pair buffer
   const GemmSeg& g;
   const uint16_t* bb[NBW];
   uint32_t bo[NBW];
-  uint32_t aoff[2];
-  int ns, lane, lc, lr;
-  uint16_t (*sA)[BM * LDK];
+  uint32_t arow[4];   // byte offset of this lane's 4 activation rows
+  int ns, lane, wave;
+  uint16_t* sA;       // 2 pair buffers x 2 slices x BM x LDK
 
   __device__ __forceinline__ int clampk(int s) const { return s < ns ? s : ns - 1; }
-  __device__ __forceinline__ void aload(u32x4 (&r)[2], int s) const {
-    const uint32_t k0 = (uint32_t)clampk(s) * (BK * 2);
+  // Lane l of load i: row 32*wave + 8*i + l/8, 16-byte piece l%8 of the pair
+  // (slice 2p + piece/4, piece%4 within it).
+  __device__ __forceinline__ void aload(u32x4 (&r)[4], int p) const {
+    const int pc = lane & 7;
+    const uint32_t o = (uint32_t)clampk(2 * p + (pc >> 2)) * (BK * 2) + (pc & 3) * 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) r[i] = ld_off<u32x4>(g.A, aoff[i] + k0);
+    for (int i = 0; i < 4; ++i) r[i] = ld_off<u32x4>(g.A, arow[i] + o);
+  }
+  __device__ __forceinline__ void astore(const u32x4 (&r)[4], int p) const {
+    const int pc = lane & 7;
+    uint16_t* base = sA + (p & 1) * kPairElems + (pc >> 2) * (BM * LDK) + (pc & 3) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&base[(32 * wave + 8 * i + (lane >> 3)) * LDK]) = r[i];
   }
   __device__ __forceinline__ void bload(bf16x8 (&b)[2][NBW], int kk, int nb, int s) const {
     const uint32_t kb = (uint32_t)clampk(s) * 2 + kk;  // 16-wide k block
     b[kk][nb] = ld_off<bf16x8>(bb[nb], bo[nb] + kb * 1024u);
   }
-  __device__ __forceinline__ void astore(const u32x4 (&r)[2], int buf) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&sA[buf][(lr + 64 * i) * LDK + lc * 8]) = r[i];
-  }
-  __device__ __forceinline__ void rfrag(bf16x8 (&a)[2][4], int kk, int mi, int buf) const {
+  // fragment of slice s (pair s/2, half s%2)
+  __device__ __forceinline__ void rfrag(bf16x8 (&a)[2][4], int kk, int mi, int s) const {
     const int ko = kk * 16 + (lane >> 5) * 8;
-    a[kk][mi] = *reinterpret_cast<const bf16x8*>(&sA[buf][(mi * 32 + (lane & 31)) * LDK + ko]);
+    const uint16_t* buf = sA + ((s >> 1) & 1) * kPairElems + (s & 1) * (BM * LDK);
+    a[kk][mi] = *reinterpret_cast<const bf16x8*>(&buf[(mi * 32 + (lane & 31)) * LDK + ko]);
   }
-  // One slice: MFMAs on (a, bc).  Right after its last MFMA an activation
-  // fragment is replaced by the next slice's (one fragment set), and a
-  // weight fragment by slice s+2's; the staged activations rs (slice s+2)
-  // go into LDS buffer `buf` at step kAst, then slice s+4 into rs.
-  __device__ __forceinline__ void slice(int s, int buf, bf16x8 (&a)[2][4], bf16x8 (&bc)[2][NBW],
-                                        u32x4 (&rs)[2], f32x16 (&acc)[4][NBW]) const {
+  template <bool EVEN>
+  __device__ __forceinline__ void slice(int s, bf16x8 (&a)[2][4], bf16x8 (&bc)[2][NBW],
+                                        u32x4 (&rs)[4], f32x16 (&acc)[4][NBW]) const {
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       const int q = i / NBW, nb = i % NBW, kk = q >> 2, mi = q & 3;
       acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[kk][nb], a[kk][mi], acc[mi][nb],
                                                             0, 0, 0);
-      if (nb == NBW - 1) rfrag(a, kk, mi, buf ^ 1);
+      if (nb == NBW - 1) rfrag(a, kk, mi, s + 1);
       if (mi == 3) bload(bc, kk, nb, s + 2);
-      if (i == kAst) astore(rs, buf);
-      if (i == kAst + 2) aload(rs, s + 4);
+      if (EVEN && i == kAst) astore(rs, (s >> 1) + 1);
+      if (EVEN && i == kAst + 2) aload(rs, (s >> 1) + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // Loads of one slice's weights and of the activations four slices on, in
-  // the order a steady-state slice issues them.
-  __device__ __forceinline__ void preload(bf16x8 (&b)[2][NBW], int sb, u32x4 (&r)[2],
-                                          int sa) const {
+  // Loads of one slice's weights (and, for an even slice, of the activation
+  // pair two ahead), in the order a steady-state slice issues them.
+  template <bool EVEN>
+  __device__ __forceinline__ void preload(bf16x8 (&b)[2][NBW], int sb, u32x4 (&r)[4],
+                                          int pa) const {
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       const int q = i / NBW, nb = i % NBW, kk = q >> 2, mi = q & 3;
       if (mi == 3) bload(b, kk, nb, sb);
-      if (i == kAst + 2) aload(r, sa);
+      if (EVEN && i == kAst + 2) aload(r, pa);
     }
   }
   __device__ __forceinline__ void run(f32x16 (&acc)[4][NBW]) const {
-    u32x4 R0[2], R1[2];
+    u32x4 R[4];
     bf16x8 A[2][4], B0[2][NBW], B1[2][NBW];
-    // Issue order mirrors two steady-state slices so the wait counts the
-    // compiler derives at the loop head are the steady-state ones.
-    aload(R0, 0);
-    aload(R1, 1);
-    astore(R0, 0);
-    astore(R1, 1);
+    aload(R, 0);
+    astore(R, 0);
     __builtin_amdgcn_sched_barrier(0);
-    preload(B0, 0, R0, 2);
-    preload(B1, 1, R1, 3);
+    preload<true>(B0, 0, R, 1);
+    preload<false>(B1, 1, R, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 #pragma unroll
@@ -296,9 +302,9 @@ struct PipePacked {
       for (int mi = 0; mi < 4; ++mi) rfrag(A, kk, mi, 0);
     int s = 0;
     for (; s + 2 <= ns; s += 2) {
-      slice(s, 0, A, B0, R0, acc);
+      slice<true>(s, A, B0, R, acc);
       __syncthreads();
-      slice(s + 1, 1, A, B1, R1, acc);
+      slice<false>(s + 1, A, B1, R, acc);
       __syncthreads();
     }
     if (s < ns) {  // odd slice count: MFMAs only
@@ -318,7 +324,8 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
   constexpr int OC = UP ? TL::UPC : TL::BN;  // output columns of the tile
   constexpr int kStage = 64 * (OC + 4);      // epilogue staging tile (elements)
   constexpr int kSB = PACKED ? kStage : (2 * BN * LDK > kStage ? 2 * BN * LDK : kStage);
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+  // packed weights: two pair buffers (4 slices); row-major: two slices
+  __shared__ __attribute__((aligned(16))) uint16_t sA[PACKED ? 4 : 2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kSB];
 
   const int G0 = seg_m_tiles(args.seg[0]) * args.seg[0].nN;
@@ -358,18 +365,15 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lc = tid & 3, lr = tid >> 2;  // 16-byte chunk of a 32-wide row; row 0..63
-  // 32-bit byte offsets from uniform bases (the ABI keeps every operand
-  // below 2^31 elements).
-  uint32_t aoff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = lr + 64 * i;
+  // Activation row r of the tile as a 32-bit byte offset from the uniform
+  // base (the ABI keeps every operand below 2^31 elements); rows past the
+  // tile's end repeat its last row.
+  auto arow_off = [&](int r) -> uint32_t {
     const int rr = r < rows ? r : rows - 1;
     const int64_t grow = (int64_t)row0 + rr;
     const int64_t src = g.a_rows ? (int64_t)g.a_rows[grow] : grow;
-    aoff[i] = ((uint32_t)(src * g.lda) + lc * 8) * 2u;
-  }
+    return (uint32_t)(src * g.lda) * 2u;
+  };
   const uint16_t* b0base = g.B0 + (int64_t)e * g.b_stride;
   const uint16_t* b1base = UP ? g.B1 + (int64_t)e * g.b_stride : b0base;
   // This wave's weight rows inside the tile: up = UPC/4 W1 rows (and the
@@ -392,7 +396,11 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
   if constexpr (PACKED) {
     // Packed weights: 32-row bands of 16-wide k blocks (512 elements each).
     const uint32_t KB = (uint32_t)(g.K / 16);
-    PipePacked<UP, NBW> pipe{g, {}, {}, {aoff[0], aoff[1]}, ns, lane, lc, lr, sA};
+    uint32_t arow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) arow[i] = arow_off(32 * wave + 8 * i + (lane >> 3));
+    PipePacked<UP, NBW> pipe{g, {}, {}, {arow[0], arow[1], arow[2], arow[3]}, ns, lane, wave,
+                             &sA[0][0]};
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       // up: bands 0..NBW/2-1 of W1, then the same bands of W3; down: W2
@@ -404,6 +412,10 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
     pipe.run(acc);
   } else {
     static_assert(NBW == 4, "row-major weights take the 128 x 512 tile");
+    const int lc = tid & 3, lr = tid >> 2;  // 16-byte chunk of a 32-wide row; row 0..63
+    uint32_t aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) aoff[i] = arow_off(lr + 64 * i) + lc * 16u;
     uint32_t boff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
