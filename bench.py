@@ -807,7 +807,7 @@ def main():
         for name in ("2b", "145b"):
             log(f"timing the {name}-shaped layer")
             out["other_shapes"][name] = other_shape(
-                name, moe_synth.CONFIGS[name], torch, moe, hip, max(10, args.steps // 3), 3, args,
+                name, moe_synth.CONFIGS[name], torch, moe, hip, max(20, args.steps), 3, args,
                 moe_synth.BALANCE_ALPHA["2b" if name == "2b" else "16b"],
                 cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 3)
     if not args.no_tiny:
@@ -820,7 +820,7 @@ def main():
         out["granularity_sweep"] = {}
         for name, gcfg in moe_synth.GRANULARITY.items():
             log(f"timing the granularity sweep: {name}")
-            r = other_shape(name, gcfg, torch, moe, hip, max(10, args.steps // 3), 3)
+            r = other_shape(name, gcfg, torch, moe, hip, max(20, args.steps), 3)
             r["m"], r["n_routed"], r["top_k"], r["d_ff"] = gcfg.m, gcfg.n, gcfg.k, gcfg.d_ff
             out["granularity_sweep"][name] = r
     if not args.no_cpu_baseline:
