@@ -18,7 +18,9 @@ the small fp32 workload, a granularity sweep (the 16B budget cut into
 m = 1, 2, 4, 8 finer experts), and the CPU oracle timed on a bounded sample of
 the 16B, 2B, 145B, decode and small workloads.  Step times are the mean over
 the timed steps; the per-kernel pass (events between kernels) adds its own
-mean and the median of its per-step times.  The 16B routing is checked
+mean and the median of its per-step times, and the same K steps timed once
+more after it give the steady-state rate (the card needs ~10-20 ms of
+sustained load to settle, longer than a short warm-up).  The 16B routing is checked
 against the oracle's on every token.  A training step states the weight
 layout of each half and, where the two differ, its time with the per-step
 re-pack and with the forward on row-major weights.
@@ -308,9 +310,22 @@ def time_layer(layer: Layer, hip: Hip, steps: int, warmup: int) -> dict:
     hip.destroy(e1)
     step_ms.sort()
     median = (step_ms[(steps - 1) // 2] + step_ms[steps // 2]) / 2
+    # The same K unmarked steps once more, now that 2K + W steps have run:
+    # the card takes ~10-20 ms of sustained load to settle, so a short
+    # warm-up leaves the first timed steps slower than the steady state.
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    rec(e0, layer.stream)
+    for i in range(steps):
+        layer.run(i)
+    rec(e1, layer.stream)
+    torch.cuda.synchronize()
+    steady = hip.ms(e0, e1) / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
     return dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, kernel_ms=per,
                 marked_ms_per_step=marked_total, marked_median_ms_per_step=median,
-                kernels=names)
+                steady_ms_per_step=steady, kernels=names)
 
 
 def gpu_shape_inputs(cfg, seed, torch, moe, copies, host=None):
@@ -383,6 +398,7 @@ def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=
         "ms_per_step": round(ms, 4),
         "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
         "median_ms_per_step": round(res["marked_median_ms_per_step"], 4),
+        "steady_ms_per_step": round(res["steady_ms_per_step"], 4),
         "grouped_gemm_tflops": round(gemm_flop / gemm_s / 1e12, 1),
         "grouped_gemm_mfma_frac": round(gemm_flop / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "max_expert_rows": int(counts.max()),
@@ -468,6 +484,7 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
         "ms_per_step": round(dms, 4),
         "marked_ms_per_step": round(dres["marked_ms_per_step"], 4),
         "median_ms_per_step": round(dres["marked_median_ms_per_step"], 4),
+        "steady_ms_per_step": round(dres["steady_ms_per_step"], 4),
         "algorithmic_bytes": int(dbytes),
         "hbm_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
         "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -791,6 +808,8 @@ def main():
         "kernels": kern,
         "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
         "median_ms_per_step": round(res["marked_median_ms_per_step"], 4),
+        "steady_ms_per_step": round(res["steady_ms_per_step"], 4),
+        "steady_tokens_per_s": round(cfg.T / (res["steady_ms_per_step"] * 1e-3), 1),
         "weight_pack_ms_once": round(pack_ms, 3),
         "wall_ms_per_step": round(res["wall_ms_per_step"], 4),
     }
