@@ -615,25 +615,14 @@ static hipError_t launch_bf16_t(const FfnArgs* segs, int nseg, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Packed weights: the up projection takes the 128 x 256 tile (d_ff = 1408
-// is 11 of its column tiles, and two workgroups share a CU).  The down
-// projection takes the 128 x 256 tile too, except next to a shared-expert
-// segment (whose tiles are twice as long and dealt first) with d a multiple
-// of 512, where the 128 x 512 tile measured faster (16B- and 145B-shaped
-// layers; without shared experts, and for d = 1280, the narrow tile was).
-// Row-major weights: 128 x 512 for both.
+// Packed weights: both projections take the 128 x 256 tile (d_ff = 1408 is
+// 11 of its column tiles, and two workgroups share a CU, so one's prologue
+// and epilogue overlap the other's MFMAs and the launch tail is half a tile
+// deep).  Row-major weights: 128 x 512 for both.
 template <bool UP>
 static hipError_t launch_bf16(const FfnArgs* segs, int nseg, bool packed, hipStream_t s) {
   if (!packed) return launch_bf16_t<UP, false, 4>(segs, nseg, s);
-  if constexpr (UP) {
-    return launch_bf16_t<true, true, 2>(segs, nseg, s);
-  } else {
-    int live = 0;
-    for (int i = 0; i < nseg; ++i) live += segs[i].rows > 0 ? 1 : 0;
-    if (live == 2 && segs[0].d % Tile<4>::BN == 0)
-      return launch_bf16_t<false, true, 4>(segs, nseg, s);
-    return launch_bf16_t<false, true, 2>(segs, nseg, s);
-  }
+  return launch_bf16_t<UP, true, 2>(segs, nseg, s);
 }
 
 static hipError_t launch_f32(const FfnArgs& a, bool up, hipStream_t s) {
