@@ -48,6 +48,7 @@ class MoEConfig:
     w_std: float = 0.02
     zipf_s: float | None = None     # Zipf exponent on centroid row norms
     tie_pairs: bool = False         # centroid row 2j+1 repeats row 2j: exact logit ties
+    flat_router: bool = False       # every centroid zero: all n logits tie at zero
 
     @property
     def n(self) -> int:
@@ -198,6 +199,8 @@ def make_router_inputs(cfg: MoEConfig, seed: int = 0, certify: bool = True):
         c *= zipf_row_scale(n, cfg.zipf_s).astype(np.float32)[:, None]
     if cfg.tie_pairs:
         c[1::2] = c[0:n - 1:2]
+    if cfg.flat_router:
+        c = np.zeros((n, d), np.float32)  # +0 everywhere: one twin group
     cent = _store(c, cfg.dtype)
     redraws = 0
     if certify:

@@ -112,6 +112,18 @@ SMALL.update({
     "tie_f32": moe_synth.MoEConfig("tie_f32", T=100, d=64, N=8, m=1, K=3, K_s=0, d_ff=32,
                                    dtype="f32", tie_pairs=True, cent_std=0.5),
 })
+# A flat router: every centroid is zero, so all n logits of every token are
+# exactly zero and the tie rule alone picks experts 0 .. k-1 for every token
+# (gates 1/n); k of the experts take every token, the rest none.  On both
+# routers, the weight-streaming FFN and in fp32.
+SMALL.update({
+    "flat_bf16": moe_synth.MoEConfig("flat_bf16", T=200, d=128, N=8, m=2, K=2, K_s=1,
+                                     d_ff=64, dtype="bf16", flat_router=True),
+    "flat_small_bf16": moe_synth.MoEConfig("flat_small_bf16", T=40, d=96, N=8, m=2, K=2,
+                                           K_s=1, d_ff=64, dtype="bf16", flat_router=True),
+    "flat_f32": moe_synth.MoEConfig("flat_f32", T=50, d=64, N=4, m=2, K=2, K_s=0, d_ff=32,
+                                    dtype="f32", flat_router=True),
+})
 # The granularity sweep at a small size: GShard top-2 of 4 experts (m = 1)
 # and the same budget cut eightfold (m = 8: top-16 of 32 experts of width 32).
 SMALL.update({

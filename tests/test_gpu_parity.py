@@ -23,7 +23,7 @@ if torch.cuda.is_available():
 
 NAMES = list(ALL)
 DECODE = [n for n in NAMES if n.startswith("decode")]
-EDGE = [n for n in NAMES if ALL[n].tie_pairs or ALL[n].n == 1]
+EDGE = [n for n in NAMES if ALL[n].tie_pairs or ALL[n].flat_router or ALL[n].n == 1]
 
 
 def dev():
@@ -149,8 +149,9 @@ def test_decode_cases_cover_their_paths(name):
 def test_edge_cases_exercise_the_rule(name):
     """The tie workloads really put an exact tie at every token's k-th choice
     (k odd, twins adjacent: the lower index is kept, its twin dropped) and
-    inside the kept list (a pair in index order); the single-expert
-    workloads give every token gate one."""
+    inside the kept list (a pair in index order); the flat-router workloads
+    tie all n experts, so every token keeps 0 .. k-1 with gate 1/n; the
+    single-expert workloads give every token gate one."""
     cfg = ALL[name]
     inp = inputs(name)
     r = oracle.route(inp["u"], inp["centroids"], cfg.k)
@@ -161,6 +162,9 @@ def test_edge_cases_exercise_the_rule(name):
         assert (last % 2 == 0).all()
         assert not (idx[:, :cfg.k - 1] == (last + 1)[:, None]).any()
         assert (idx[:, 1] == idx[:, 0] + 1).all()
+    elif cfg.flat_router:
+        assert (idx == np.arange(cfg.k)[None, :]).all()
+        assert np.allclose(gate, 1.0 / cfg.n, rtol=0, atol=1e-7)
     else:
         assert cfg.n == 1
         assert (idx == 0).all() and (gate == 1.0).all()

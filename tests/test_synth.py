@@ -72,6 +72,26 @@ def test_tie_pairs_are_exact_twins_and_certified():
     assert (lg[:, 0::2] == lg[:, 1::2]).all()
 
 
+def test_flat_router_ties_every_expert_and_the_oracle_keeps_the_lowest():
+    """All-zero centroids: every logit is exactly 0, the whole row is one twin
+    group (no redraw), and the oracle's selection rule (larger logit, then
+    lower index) keeps experts 0 .. k-1 in that order with the uniform
+    softmax 1/n as gates; counts, f and P follow in closed form."""
+    import oracle
+    cfg = moe_synth.MoEConfig("f", T=70, d=64, N=8, m=2, K=2, K_s=1, d_ff=32,
+                              dtype="bf16", flat_router=True)
+    u, c, redraws = moe_synth.make_router_inputs(cfg, seed=0)
+    assert redraws == 0 and not moe_synth.as_f32(c).any()
+    r = oracle.route(u, c, cfg.k)
+    assert (r["topk_idx"] == np.arange(cfg.k)[None, :]).all()
+    assert np.allclose(r["topk_gate"], 1.0 / cfg.n, rtol=0, atol=1e-7)
+    want = np.zeros(cfg.n, np.int64)
+    want[:cfg.k] = cfg.T
+    assert np.array_equal(r["counts"], want)
+    assert np.allclose(r["f"], want * cfg.n / (cfg.k * cfg.T), rtol=1e-6)
+    assert np.allclose(r["P"], 1.0 / cfg.n, rtol=1e-5)
+
+
 def test_margin_violation_is_detected():
     """Two experts whose logits differ by less than the margin for one token."""
     u = np.zeros((2, 32), np.float32)
