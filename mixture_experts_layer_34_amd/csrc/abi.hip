@@ -104,7 +104,7 @@ Layout layout(const Dims& d) {
   L.t_row0 = take((size_t)L.max_tiles * 4);
   L.t_rows = take((size_t)L.max_tiles * 4);
   L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
-  L.t_count = take(4);
+  L.t_count = take(4 + 64);  // the count, then 16 claim counters at int 16
   L.lg = take((size_t)(d.T < moe::kSmallBatch ? d.T : moe::kSmallBatch) * d.n * 4);
   const size_t hs_el = (size_t)d.T * d.K_s * d.d_ff;
   L.hcap = R * d.d_ff > hs_el ? R * d.d_ff : hs_el;
@@ -125,9 +125,12 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// The tile count's 256-byte region also holds the 16 claim counters of the
+// two grouped-GEMM launches (ints 16 .. 31).
 moe::TileList tiles_of(void* ws, const Layout& L) {
   return moe::TileList{at<int32_t>(ws, L.t_row0), at<int32_t>(ws, L.t_rows),
-                       at<int32_t>(ws, L.t_off), at<int32_t>(ws, L.t_count), L.max_tiles};
+                       at<int32_t>(ws, L.t_off),  at<int32_t>(ws, L.t_count),
+                       L.max_tiles,               at<int32_t>(ws, L.t_count) + 16};
 }
 
 // Last HIP error an entry point hit on this host thread.
@@ -203,7 +206,7 @@ BwdLayout bwd_layout(const Dims& d) {
   L.t_row0 = take((size_t)L.max_tiles * 4);
   L.t_rows = take((size_t)L.max_tiles * 4);
   L.t_off = take((size_t)(MOE_MAX_EXPERTS + 1) * 4);
-  L.t_count = take(4);
+  L.t_count = take(4 + 64);  // the count, then 16 claim counters at int 16
   L.wctr = take(moe::kWgQueues * 4);
   L.gperm = take(R * 4);
   L.xp = take(R * d.d * 2);

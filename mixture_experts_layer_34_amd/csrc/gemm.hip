@@ -74,7 +74,66 @@ struct GemmSeg {
 struct GemmArgs {
   GemmSeg seg[2];
   int nseg;
+  int32_t* steal;  // nullable: [8] per-XCD claim counters, zero at launch
 };
+
+// Launch tail.  Workgroup w runs on XCD w % 8 and xcd_remap2 gives each XCD
+// a contiguous run of tiles; the XCDs' finishing times still spread by
+// several percent.  With claim counters, the last eighth of each XCD's run
+// (routed tiles only: the shared ones are dealt first) is handed out by an
+// atomic per XCD: its own workgroups claim from it first, and workgroups
+// with no tile of their own (the grid is sized for the largest possible
+// tile list) and those whose XCD ran dry claim from the XCD with the most
+// left.  Every claimable tile has at least one claimer on its own XCD and
+// each claim index is unique, so every tile runs exactly once; nothing
+// waits on another workgroup.
+__device__ __forceinline__ int xcd_items(int G, int x) { return G / 8 + (x < G % 8 ? 1 : 0); }
+
+__device__ __forceinline__ int xcd_claimable(int G, int G1, int x) {
+  const int q = xcd_items(G, x), q0 = q - xcd_items(G1, x);
+  const int c = q >> 3;
+  return c < q0 ? c : q0;
+}
+
+// The workgroup slot this workgroup runs (a workgroup index in the static
+// deal), or -1: none left.
+__device__ int claim_tile(int w, int G, int G1, int32_t* steal) {
+  __shared__ int s_claim;
+  const int x = w & 7, i = w >> 3;
+  const int q = xcd_items(G, x), sn = xcd_claimable(G, G1, x);
+  if (i < q - sn) return w;  // the static part of this XCD's run
+  if (threadIdx.x == 0) {
+    int got = -1;
+    if (i < q) {  // own claim first
+      const int c = __hip_atomic_fetch_add(&steal[x], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (c < sn) got = 8 * (q - sn + c) + x;
+    }
+    for (int attempt = 0; got < 0 && attempt < 3; ++attempt) {
+      int cnt[8];  // all eight counters in flight at once
+#pragma unroll
+      for (int y = 0; y < 8; ++y)
+        cnt[y] = __hip_atomic_load(&steal[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int best = -1, left = 0;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int l = xcd_claimable(G, G1, y) - cnt[y];
+        if (l > left) {
+          left = l;
+          best = y;
+        }
+      }
+      if (best < 0) break;
+      const int c = __hip_atomic_fetch_add(&steal[best], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      const int sy = xcd_claimable(G, G1, best);
+      if (c < sy) got = 8 * (xcd_items(G, best) - sy + c) + best;
+    }
+    s_claim = got;
+  }
+  __syncthreads();
+  return s_claim;
+}
 
 // Weight packing: [rows][K] row-major -> 32-row bands, each a run of 16-wide
 // k blocks of 512 elements in MFMA operand order (lane l holds row l % 32,
@@ -331,9 +390,15 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
   const int G0 = seg_m_tiles(args.seg[0]) * args.seg[0].nN;
   const int G1 = args.nseg > 1 ? seg_m_tiles(args.seg[1]) * args.seg[1].nN : 0;
   const int G = G0 + G1;
-  if ((int)blockIdx.x >= G) return;
+  int w = (int)blockIdx.x;
+  if (args.steal) {
+    w = claim_tile(w, G, G1, args.steal);
+    if (w < 0) return;
+  } else if (w >= G) {
+    return;
+  }
   int si, L;
-  xcd_remap2((int)blockIdx.x, G0, G1, si, L);
+  xcd_remap2(w, G0, G1, si, L);
   const GemmSeg& g = args.seg[si];
 
   // Logical order within a segment: group, then column tile, then M-tile,
@@ -610,6 +675,9 @@ static hipError_t launch_bf16_t(const FfnArgs* segs, int nseg, hipStream_t s) {
     ++args.nseg;
   }
   if (args.nseg == 0) return hipSuccess;
+  // claim counters: with a device tile list that carries them
+  const TileList* tl = segs[0].rows > 0 ? segs[0].tiles : nullptr;
+  args.steal = tl && tl->steal ? tl->steal + (UP ? 0 : 8) : nullptr;
   hipLaunchKernelGGL((gemm_bf16_kernel<UP, PACKED, NBW>), dim3((unsigned)grid), dim3(kThreads), 0,
                      s, args);
   return hipGetLastError();

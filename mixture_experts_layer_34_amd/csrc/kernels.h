@@ -21,6 +21,9 @@ struct TileList {
   int32_t* off;     // [n_groups+1] first M-tile of each group
   int32_t* count;   // [1] number of M-tiles
   int max_tiles;    // capacity (host bound)
+  // nullable: [16] per-XCD claim counters of the up (0..7) and down (8..15)
+  // projections' launch tails, zeroed by the kernel that writes the list
+  int32_t* steal = nullptr;
 };
 
 // Router: logits, softmax, top-k, per-block P partial sums, per-block

@@ -537,6 +537,7 @@ __device__ void emit_tile_list(const TileList& tl, int n, const int* s_cnt, cons
     tl.off[n] = *s_total;
     *tl.count = *s_total;
   }
+  if (tl.steal && tid < 16) tl.steal[tid] = 0;
   __syncthreads();
   // Tile t belongs to the last expert whose first tile is <= t.
   const int total = s_toff[n];
@@ -685,6 +686,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
       tl.off[n] = s_total;
       *tl.count = s_total;
     }
+    if (tl.steal && tid < 16) tl.steal[tid] = 0;
   }
   __syncthreads();
   if (has_tiles) {
@@ -1024,6 +1026,7 @@ __global__ __launch_bounds__(kTileThreads) void tiles_kernel(const int32_t* __re
     tl.off[G] = total;
     *tl.count = total;
   }
+  if (tl.steal && tid < 16) tl.steal[tid] = 0;
 }
 
 }  // namespace
