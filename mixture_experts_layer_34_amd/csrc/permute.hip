@@ -53,6 +53,32 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
 
 constexpr int kCombineThreads = 256;
 
+// Eight consecutive elements of a row, loaded whole (16 bytes of bf16, 32 of
+// fp32) and read back as fp32.
+template <typename T>
+struct Chunk;
+template <>
+struct Chunk<uint16_t> {
+  u32x4 v;
+  static __device__ __forceinline__ Chunk load(const uint16_t* p) {
+    return Chunk{*reinterpret_cast<const u32x4*>(p)};
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = v[i >> 1];
+    return bf16_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+  }
+};
+template <>
+struct Chunk<float> {
+  u32x4 a, b;
+  static __device__ __forceinline__ Chunk load(const float* p) {
+    return Chunk{*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 4)};
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return __uint_as_float(i < 4 ? a[i] : b[i - 4]);
+  }
+};
+
 // One workgroup per token; each thread owns chunks of 8 elements.
 template <int DT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
@@ -80,21 +106,36 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const typename E::T* row = y + (int64_t)s_slot[j] * d + c * 8;
-      const float g = s_g[j];
+    // The chunk's shared and residual rows and up to kBatch gathered rows
+    // are loaded before any is summed, so a token costs one memory round
+    // trip per kBatch slots (the sum keeps the order: slots ascending, then
+    // shared, then residual).
+    typedef typename E::T ET;
+    constexpr int kBatch = 8;
+    Chunk<ET> sh{}, rs{};
+    if (shared_out) sh = Chunk<ET>::load(shared_out + t * d + c * 8);
+    if (residual) rs = Chunk<ET>::load(residual + t * d + c * 8);
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      Chunk<ET> v[kBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += g * E::ld(row, i);
+      for (int jj = 0; jj < kBatch; ++jj)
+        if (j0 + jj < k) v[jj] = Chunk<ET>::load(y + (int64_t)s_slot[j0 + jj] * d + c * 8);
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) {
+        if (j0 + jj < k) {
+          const float g = s_g[j0 + jj];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += g * v[jj].get(i);
+        }
+      }
     }
     if (shared_out) {
-      const typename E::T* row = shared_out + t * d + c * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += E::ld(row, i);
+      for (int i = 0; i < 8; ++i) acc[i] += sh.get(i);
     }
     if (residual) {
-      const typename E::T* row = residual + t * d + c * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += E::ld(row, i);
+      for (int i = 0; i < 8; ++i) acc[i] += rs.get(i);
     }
     typename E::T* out = h + t * d + c * 8;
 #pragma unroll
