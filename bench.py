@@ -818,6 +818,14 @@ def main():
         out["backward_16b"] = backward_regime(torch, moe, hip, args, cfg, inp, layer)
         out["backward_16b_saved"] = backward_regime(torch, moe, hip, args, cfg, inp, layer,
                                                     saved=True)
+        # Both halves on the packed weights the forward holds: a weight update
+        # then needs no second copy (the backward's own kernels are slower on
+        # the packed layout, the step as a whole is the fastest honest one).
+        for key, sv in (("backward_16b_packed", False), ("backward_16b_packed_saved", True)):
+            b = backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=True, saved=sv)
+            out[key] = {k: b[k] for k in ("ms_per_step", "tokens_per_s", "weight_layout",
+                                          "train_step")}
+            out[key]["kernel_us"] = {k: v["us"] for k, v in b["kernels"].items()}
     del layer
     if not args.no_decode:
         out["decode_64tok"] = decode_regime(torch, moe, hip, args, inp, sets)
