@@ -120,14 +120,31 @@ __device__ __forceinline__ void kc_store(uint16_t* s, const u32x4 v[4], int tid)
 }
 
 // ---- K-strided operand: 64 k rows x 128 columns of the tile.  Thread:
-// columns mb*8 .. +7 with mb = 4 wave + (lane & 3), k rows kg*4 .. +3 with
-// kg = lane >> 2 (four lanes read 64 contiguous bytes of a row).  Rows are
-// addressed directly: a row map would put a dependent load in front of every
-// load, and the in-order load counter would then wait for all loads in flight.
+// columns mb*8 .. +7, k rows kg*4 .. +3.  Row-major: mb = 4 wave + lane % 4,
+// kg = lane / 4, so four lanes read 64 contiguous bytes of a row (16 rows per
+// load instruction; both other assignments tried, a whole 128-byte row per 8
+// lanes and 8 k groups per column block, measured slower).  Packed (32-row
+// bands of 16-wide k blocks, 1 KB each, consecutive along k): mb = lane / 8 +
+// 8 (wave & 1), kg = lane % 8 + 8 (wave / 2), so a wave's four loads cover
+// one band's four consecutive blocks, 4 KB of contiguous memory, instead of
+// two 2 KB pieces of two bands (dgrad with packed weights 10 % faster).  The
+// transposing LDS stores below stay on distinct banks either way (checked
+// on the host).  Rows are addressed directly: a row map would put a
+// dependent load in front of every load, and the in-order load counter would
+// then wait for all loads in flight.
+template <bool PK>
+__device__ __forceinline__ int ks_mb(int tid) {
+  return PK ? ((tid & 63) >> 3) + 8 * ((tid >> 6) & 1) : 4 * (tid >> 6) + (tid & 3);
+}
+template <bool PK>
+__device__ __forceinline__ int ks_kg(int tid) {
+  return PK ? (tid & 7) + 8 * (tid >> 7) : (tid & 63) >> 2;
+}
+
 template <bool PK = false>
 __device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld, int kbase,
                                         int klim, int col0, int clim, int tid) {
-  const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
+  const int mb = ks_mb<PK>(tid), kg = ks_kg<PK>(tid);
   const int col = col0 + mb * 8;
   const bool cin = col < clim;
 #pragma unroll
@@ -142,9 +159,11 @@ __device__ __forceinline__ void ks_load(u32x4 v[4], const void* base, int64_t ld
 }
 
 // Transposes the thread's 4 (k) x 8 (columns) block into LDS rows = columns
-// (rows roff + 0 .. 127 of the staged tile).
+// (rows roff + 0 .. 127 of the staged tile); PK as in the ks_load that
+// filled v.
+template <bool PK = false>
 __device__ __forceinline__ void ks_store(uint16_t* s, const u32x4 v[4], int tid, int roff = 0) {
-  const int mb = 4 * (tid >> 6) + (tid & 3), kg = (tid & 63) >> 2;
+  const int mb = ks_mb<PK>(tid), kg = ks_kg<PK>(tid);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int w = i >> 1, sh = (i & 1) * 16;
@@ -270,8 +289,8 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
     auto store = [&](int st, int b) {
       kc_store(sA[b], ra[st], tid);
       if constexpr (BKS) {
-        ks_store(sB[b], rbv[st], tid);
-        if constexpr (DUAL) ks_store(sB2[b], rb2[st], tid);
+        ks_store<PK>(sB[b], rbv[st], tid);
+        if constexpr (DUAL) ks_store<PK>(sB2[b], rb2[st], tid);
       } else {
         kc_store(sB[b], rbv[st], tid);
         if constexpr (DUAL) kc_store(sB2[b], rb2[st], tid);
