@@ -9,7 +9,7 @@
 // gradients, each expert reducing over its own rows, on 256 x 256 tiles.
 // Operands that are K-strided in memory (weights read against their stored
 // orientation, activations reduced over tokens) are transposed on their way
-// into LDS; see rb() for the bank layout.
+// into LDS; see lpos() for the bank layout.
 #include "bwd.h"
 #include "common.h"
 #include "kernels.h"
@@ -18,20 +18,30 @@ namespace moe {
 namespace {
 
 constexpr int BM = kBgTile, BN = kBgTile, BK = kBgK;
-constexpr int LDK = BK + 8;  // LDS row pitch (elements)
-constexpr int BAND = 32;     // extra elements before every band of 16 rows
-constexpr int TILE_EL = BM * LDK + BAND * (BM / 16);  // one staged operand tile (see rb)
+// One staged operand tile (BM rows of BK elements, see lpos), with room for
+// the epilogue's fp32 staging (four waves x 32 rows x 68 floats over the two
+// buffers of sA).
+constexpr int kStageF32El = 4 * 32 * (64 + 4) * 2;
+constexpr int TILE_EL = BM * BK > kStageF32El / 2 ? BM * BK : kStageF32El / 2;
 constexpr int NT = 256;
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_DU = 3 };
 
-// LDS position of tile row m (elements).  With 36-word rows, the MFMA
-// fragment reads (16 lanes on 16 consecutive rows, 16 bytes each) fall on
-// distinct banks; 16 more words before every band of 16 rows (16 (band mod 4)
-// modulo the 64 banks) also spread the transposing store of a K-strided
-// operand, where the 32 lanes of a half-wave write 8-byte pieces of 4 rows
-// 8 apart in each of 8 K groups.
-__device__ __forceinline__ int rb(int m) { return m * LDK + BAND * (m >> 4); }
+// LDS layout of a staged tile: row m holds its 64 K elements as eight
+// 16-byte chunks at 128-byte pitch, chunk c at position c ^ swz(m).  Measured
+// on gfx950 (bank-conflict counters on single access patterns): a 16-byte
+// read is served in four passes of 16 lanes (lane bit 5, and the parity of
+// lane bits 2..4) over 64 four-byte banks, and an 8-byte write in passes of
+// 16 consecutive lanes over 32 banks.  The MFMA fragment reads (lane l on
+// row l % 32) then need swz to take 8 values on the even rows of each pass,
+// and the transposing stores (4 rows 8 apart, or 2 rows 8 apart, per pass)
+// need rows differing in bits 3 and 4 on disjoint chunks; this swz does both
+// (4 cycles per read and per 8-byte write, against 8 for the padded pitch it
+// replaces).
+__device__ __forceinline__ int swz(int m) {
+  return ((m >> 1) & 1) | (((m >> 4) & 1) << 1) | (((m >> 3) & 1) << 2);
+}
+__device__ __forceinline__ int lpos(int m, int c) { return m * BK + ((c ^ swz(m)) << 3); }
 
 struct BgArgs {
   BgSeg seg[kBgMaxSeg];
@@ -115,7 +125,7 @@ __device__ __forceinline__ void kc_store(uint16_t* s, const u32x4 v[4], int tid)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + 32 * i;
-    *reinterpret_cast<u32x4*>(&s[rb(r) + kc]) = v[i];
+    *reinterpret_cast<u32x4*>(&s[lpos(r, kc >> 3)]) = v[i];
   }
 }
 
@@ -169,7 +179,8 @@ __device__ __forceinline__ void ks_store(uint16_t* s, const u32x4 v[4], int tid,
     const int w = i >> 1, sh = (i & 1) * 16;
     const uint32_t lo = ((v[0][w] >> sh) & 0xFFFFu) | (((v[1][w] >> sh) & 0xFFFFu) << 16);
     const uint32_t hi = ((v[2][w] >> sh) & 0xFFFFu) | (((v[3][w] >> sh) & 0xFFFFu) << 16);
-    *reinterpret_cast<uint2*>(&s[rb(roff + mb * 8 + i) + kg * 4]) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(&s[lpos(roff + mb * 8 + i, kg >> 1) + (kg & 1) * 4]) =
+        make_uint2(lo, hi);
   }
 }
 
@@ -251,12 +262,13 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
       }
     }
 
-  // Fragment rows of this lane (LDS element offsets, k = 0).
+  // Fragment rows of this lane (LDS element offsets of k step 0; step kk
+  // is at offset ^ 16 kk).
   int fa[2], fb[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    fa[i] = rb(wm * 64 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
-    fb[i] = rb(wn * 64 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+    fa[i] = lpos(wm * 64 + i * 32 + (lane & 31), lane >> 5);
+    fb[i] = lpos(wn * 64 + i * 32 + (lane & 31), lane >> 5);
   }
 
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
@@ -302,8 +314,8 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
         bf16x8 af[2], bfr[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] + kk * 16]);
-          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] + kk * 16]);
+          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] ^ (kk * 16)]);
+          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] ^ (kk * 16)]);
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
@@ -315,7 +327,7 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
           bf16x8 b2[2];
 #pragma unroll
           for (int i = 0; i < 2; ++i)
-            b2[i] = *reinterpret_cast<const bf16x8*>(&sB2[b][fb[i] + kk * 16]);
+            b2[i] = *reinterpret_cast<const bf16x8*>(&sB2[b][fb[i] ^ (kk * 16)]);
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -359,6 +371,8 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   // loads and stores run along rows.
   constexpr int SPF = 64 + 4;  // fp32 staging pitch (floats)
   constexpr int SPH = 64 + 8;  // bf16 staging pitch (elements)
+  static_assert(4 * 32 * SPF * 2 <= 2 * TILE_EL && 4 * 32 * SPH <= 2 * TILE_EL,
+                "epilogue staging fits the two buffers of sA");
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
     char* C = static_cast<char*>(g.C);
 #pragma unroll
@@ -545,7 +559,9 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 // row offsets are read from LDS for the same reason (a global load of them
 // at a tile's start would wait for the previous tile's stores).
 constexpr int WB = 256;
-constexpr int WTILE_EL = WB * LDK + BAND * (WB / 16);
+// (a staged 256-row tile, or two waves' epilogue staging of 32 rows x 132
+// floats, whichever is larger)
+constexpr int WTILE_EL = WB * BK > 2 * 32 * 132 * 2 ? WB * BK : 2 * 32 * 132 * 2;
 constexpr int kWgMaxGroups = 256;
 constexpr int kXcds = kWgQueues;
 // Buffer resource word 3 for raw 32-bit accesses on gfx9, and an offset
@@ -668,8 +684,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   int fa[4], fb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa[i] = rb(wm * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
-    fb[i] = rb(wn * 128 + i * 32 + (lane & 31)) + (lane >> 5) * 8;
+    fa[i] = lpos(wm * 128 + i * 32 + (lane & 31), lane >> 5);
+    fb[i] = lpos(wn * 128 + i * 32 + (lane & 31), lane >> 5);
   }
   const WQueues wq = wqueues(args);
   if (wq.k1 > wq.k0) {
@@ -754,8 +770,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         bf16x8 af[4], bfr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] + kk * 16]);
-          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] + kk * 16]);
+          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] ^ (kk * 16)]);
+          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] ^ (kk * 16)]);
         }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
