@@ -947,6 +947,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     x.C = C;
     x.ldc = ldc;
     x.c_gstride = (int64_t)M * N;
+    x.c_stream = 1;
   };
   {
     moe::BgSeg g[7] = {};
@@ -964,6 +965,7 @@ moe_status moe_layer_bwd_marked(const moe_problem* p, const void* u, const void*
     wseg(g[c++], dhp, d.d, gh, d.d_ff, d.d, d.d_ff, offsets, 0, 0, d.n, dw2, d.d_ff);
     // dE = dl^T u over token chunks: M = n, N = d
     wseg(g[c++], dl, L.ldl, u, d.d, d.n, d.d, nullptr, L.kchunk, (int)d.T, L.G, slabs, d.d);
+    g[c - 1].c_stream = 0;  // the slab sum reads these partials next
     MOE_TRY(moe::launch_bg(moe::BG_WGRAD, g, c, s, wctr));
   }
   MOE_TRY(mark());

@@ -44,6 +44,9 @@ struct BgSeg {
   void* C;
   int64_t ldc;
   int64_t c_gstride;
+  int c_stream;          // k grouping: C is a final result no later kernel of the
+                         // call reads: stored non-temporal, so it does not evict
+                         // the operands the other tiles share in L2
   // SwiGLU-backward epilogue (rows grouping, dual product): q, da, db, gh
   // share C's row pitch ldc.
   const void* q;

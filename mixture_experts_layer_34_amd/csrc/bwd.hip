@@ -839,17 +839,26 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int c = ncol0 + 4 * (lane & 31);
+        // AUX 2: non-temporal (final gradients: 2.2 GB at the 16B shape
+        // would otherwise push the shared operands out of L2; measured 30 %
+        // fewer HBM reads and 4 % faster)
+        auto round = [&](auto aux) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 2 * i + (lane >> 5);
-          const int m = mrow0 + mb * 32 + row;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row * SP + 4 * (lane & 31)]);
-          const int off = (m < M && c < N) ? (m * ldc + c) * 4 : kBufDrop;
-          __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, 0);
-        }
-        // all 16 LDS reads in flight at once, then the 16 stores
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x040, 16, 0);
+          for (int i = 0; i < 16; ++i) {
+            const int row = 2 * i + (lane >> 5);
+            const int m = mrow0 + mb * 32 + row;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row * SP + 4 * (lane & 31)]);
+            const int off = (m < M && c < N) ? (m * ldc + c) * 4 : kBufDrop;
+            __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, decltype(aux)::value);
+          }
+          // all 16 LDS reads in flight at once, then the 16 stores
+          __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+          __builtin_amdgcn_sched_group_barrier(0x040, 16, 0);
+        };
+        if (g.c_stream)
+          round(std::integral_constant<int, 2>{});
+        else
+          round(std::integral_constant<int, 0>{});
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
