@@ -6,7 +6,7 @@
 // 128 x 128 output tiles, 64-deep K slices staged through LDS with the next
 // slices' global loads in flight, four waves of 64 x 64 each (2 x 2 blocks
 // of 32x32x16 bf16 MFMAs, fp32 accumulators).  wgrad_kernel: the weight
-// gradients, each expert reducing over its own rows, on 256 x 256 tiles.
+// gradients, each expert reducing over its own rows, on 256 x 128 tiles.
 // Operands that are K-strided in memory (weights read against their stored
 // orientation, activations reduced over tokens) are transposed on their way
 // into LDS; see lpos() for the bank layout.
@@ -538,11 +538,14 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 }
 
 // Weight gradients (k grouping, both operands K-strided, fp32 out) on
-// 256 x 256 tiles: an expert's K range is only its rows (a few hundred), so
-// a tile reuses each staged slice over four times the output of the
-// 128 x 128 kernel, and each wave's 128 x 128 block (16 accumulator blocks,
-// held in AGPRs) takes two MFMAs per fragment read from LDS.  One workgroup
-// per CU, persistent, taking tiles from work queues.
+// 256 x 128 tiles: an expert's K range is only its rows (a few hundred), so
+// a tile reuses each staged slice over twice the output of the 128 x 128
+// kernel, and each wave's 128 x 64 block (8 accumulator blocks) takes 8
+// MFMAs per 6 fragment reads.  Two persistent workgroups per CU (one K
+// slice staged at a time, 50 KB of LDS and 252 registers each) taking tiles
+// from work queues: one workgroup's slice staging, barriers and epilogue
+// run beside the other's MFMAs (measured 10 % faster than one 256 x 256
+// workgroup per CU with two staged slices).
 //
 // Queues: one per XCD (workgroup b runs on XCD b % 8).  XCD x's queue holds
 // the experts e = x, x + 8, ... of the segments with a row-offset table
@@ -552,16 +555,15 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 // from the other queues, so tiles of unequal length (each expert reduces
 // over its own rows) still balance.
 //
-// The next tile's first slice is loaded during the current tile's last one
-// and staged before its epilogue, so that the epilogue's stores drain while
-// the next tile's MFMAs run: the load counter counts stores too, and a wait
-// for any load issued after them would otherwise wait for them all.  Expert
-// row offsets are read from LDS for the same reason (a global load of them
-// at a tile's start would wait for the previous tile's stores).
-constexpr int WB = 256;
-// (a staged 256-row tile, or two waves' epilogue staging of 32 rows x 132
-// floats, whichever is larger)
-constexpr int WTILE_EL = WB * BK > 2 * 32 * 132 * 2 ? WB * BK : 2 * 32 * 132 * 2;
+// The next tile's first slice is loaded during the current tile's last one,
+// before the epilogue's stores: the load counter counts stores too, and a
+// wait for a load issued after them would wait for them all.  Expert row
+// offsets are read from LDS for the same reason (a global load of them at a
+// tile's start would wait for the previous tile's stores).
+constexpr int WBM = 256, WBN = 128;  // weight-gradient tile (M x N)
+constexpr int WTILE_EL = (WBM + WBN) * BK;  // one staged slice of both operands
+constexpr int kWgSP = 64 + 4;                // epilogue staging pitch (floats)
+static_assert(4 * 32 * kWgSP * 2 <= WTILE_EL, "four waves' epilogue staging fits the slice");
 constexpr int kWgMaxGroups = 256;
 constexpr int kXcds = kWgQueues;
 // Buffer resource word 3 for raw 32-bit accesses on gfx9, and an offset
@@ -574,7 +576,7 @@ struct WTile {
 };
 
 __device__ __forceinline__ int wg_tiles(const BgSeg& g) {
-  return ((g.M + WB - 1) / WB) * ((g.N + WB - 1) / WB);  // per group
+  return ((g.M + WBM - 1) / WBM) * ((g.N + WBN - 1) / WBN);  // per group
 }
 
 // Segments [k0, k1) carry the row-offset table (contiguous, same G; k0 = k1
@@ -650,13 +652,13 @@ __device__ __forceinline__ void wq_tile(const BgArgs& a, const WQueues& q, int x
 __device__ __forceinline__ WTile wtile_of(const BgArgs& a, const int* koff, int s, int t) {
   WTile w{};
   const BgSeg& g = a.seg[s];
-  const int nN = (g.N + WB - 1) / WB, nM = (g.M + WB - 1) / WB;
+  const int nN = (g.N + WBN - 1) / WBN, nM = (g.M + WBM - 1) / WBM;
   w.si = s;
   w.e = t / (nM * nN);
   const int r = t - w.e * nM * nN;
   const int nt = r / nM, mt = r - nt * nM;
-  w.m0 = mt * WB;
-  w.n0 = nt * WB;
+  w.m0 = mt * WBM;
+  w.n0 = nt * WBN;
   if (g.koff) {
     w.kb = koff[w.e];
     w.ke = koff[w.e + 1];
@@ -671,22 +673,24 @@ __device__ __forceinline__ WTile wtile_of(const BgArgs& a, const int* koff, int 
 // A queue entry for s_next: XCD in the top bits, -1 for none.
 __device__ __forceinline__ int wq_pack(int x, int i) { return (x << 24) | i; }
 
-__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void wgrad_kernel(
-    BgArgs args, int* __restrict__ ctr) {
-  // two slice buffers per operand; buffer 1 also stages the epilogue
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][WTILE_EL];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][WTILE_EL];
+__global__ __launch_bounds__(NT, 2) void wgrad_kernel(BgArgs args, int* __restrict__ ctr) {
+  // One staged K slice of both operands (A: 256 rows, B: 128 rows); it also
+  // holds the epilogue's staging.  Single-buffered, so two workgroups fit a
+  // CU and one's LDS staging, barriers and epilogue run beside the other's
+  // MFMAs.
+  __shared__ __attribute__((aligned(16))) uint16_t sT[WTILE_EL];
   __shared__ int s_koff[kWgMaxGroups + 1];
   __shared__ int s_next[2];
+  uint16_t* const sTa = sT;
+  uint16_t* const sTb = sT + WBM * BK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  int fa[4], fb[4];
+  const int wm = wave & 1, wn = wave >> 1;  // 128 x 64 block of the tile
+  int fa[4], fb[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[i] = lpos(wm * 128 + i * 32 + (lane & 31), lane >> 5);
-    fb[i] = lpos(wn * 128 + i * 32 + (lane & 31), lane >> 5);
-  }
+  for (int i = 0; i < 4; ++i) fa[i] = lpos(wm * 128 + i * 32 + (lane & 31), lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fb[i] = lpos(wn * 64 + i * 32 + (lane & 31), lane >> 5);
   const WQueues wq = wqueues(args);
   if (wq.k1 > wq.k0) {
     const int32_t* koff = args.seg[wq.k0].koff;
@@ -706,22 +710,18 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     }
     return -1;
   };
-  u32x4 ra[2][4], rbv[2][4];
+  u32x4 ra[2][4], rbv[4];
   auto load = [&](const WTile& w, int kt) {
     const BgSeg& g = args.seg[w.si];
     const int k0 = w.kb + kt * BK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ks_load(ra[h], g.A[0], g.lda, k0, w.ke, w.m0 + 128 * h, g.a_lim, tid);
-      ks_load(rbv[h], g.B[0], g.ldb, k0, w.ke, w.n0 + 128 * h, g.b_lim, tid);
-    }
+    for (int h = 0; h < 2; ++h) ks_load(ra[h], g.A[0], g.lda, k0, w.ke, w.m0 + 128 * h, g.a_lim, tid);
+    ks_load(rbv, g.B[0], g.ldb, k0, w.ke, w.n0, g.b_lim, tid);
   };
-  auto store = [&](int b) {
+  auto store = [&]() {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ks_store(sA[b], ra[h], tid, 128 * h);
-      ks_store(sB[b], rbv[h], tid, 128 * h);
-    }
+    for (int h = 0; h < 2; ++h) ks_store(sTa, ra[h], tid, 128 * h);
+    ks_store(sTb, rbv, tid);
   };
 
   // Tile j of this workgroup finds tile j + 1's entry in s_next[(j + 1) & 1]
@@ -739,14 +739,12 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   wq_tile(args, wq, cur >> 24, cur & 0xffffff, s0, t0);
   WTile w = wtile_of(args, s_koff, s0, t0);
   load(w, 0);
-  store(0);
-  __syncthreads();
   for (int j = 0;; ++j) {
     const int nxt = s_next[(j + 1) & 1];
     const bool more = nxt >= 0;
-    // The queue's reply is first used after this tile's K loop, where the
-    // wave waits for its loads anyway (the library builds this file without
-    // the compiler's wave-level atomic combining, which would wait here).
+    // The queue's reply is first used after this tile's K loop (the library
+    // builds this file without the compiler's wave-level atomic combining,
+    // which would wait here).
     int fetched;
     if (tid == 0 && more) fetched = atomicAdd(&ctr[qx], 1);
     WTile w2{};
@@ -756,104 +754,98 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       w2 = wtile_of(args, s_koff, s2, t2);
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[nb][mb][q] = 0.0f;
 
-    auto slice = [&](int b) {
+    auto slice = [&]() {
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[4], bfr[4];
+        bf16x8 af[4], bfr[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          af[i] = *reinterpret_cast<const bf16x8*>(&sA[b][fa[i] ^ (kk * 16)]);
-          bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[b][fb[i] ^ (kk * 16)]);
-        }
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(&sTa[fa[i] ^ (kk * 16)]);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int i = 0; i < 2; ++i) bfr[i] = *reinterpret_cast<const bf16x8*>(&sTb[fb[i] ^ (kk * 16)]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
             acc[nb][mb] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
       }
     };
-    // (the last slice is peeled off, so that the loop's loads are
-    // unconditional and no wait at its head covers the previous stores)
-    int kt = 0;
-    for (; kt + 1 < w.nk; ++kt) {
-      load(w, kt + 1);
-      slice(kt & 1);
-      store((kt & 1) ^ 1);
-      __syncthreads();
-    }
-    // The last slice, with the next tile's first slice in flight; that slice
-    // then goes to buffer 0 (free: the last reads ended at the barrier).
-    // Loaded and stored unconditionally (an empty range loads nothing and
-    // stores zeros nobody reads): a load under one branch and its use under
-    // another make the compiler assume a load still pending, and wait for
-    // the epilogue's stores before the next tile's first load.
-    load(w2, 0);
-    if (w.nk > 0) slice(kt & 1);
+    // Slice kt is staged from registers, then slice kt + 1 (or, for the last
+    // slice, the next tile's first) loads while slice kt is multiplied.  The
+    // loads are unconditional (an empty range loads nothing), so no wait for
+    // them covers stores issued after them.
+    store();
     __syncthreads();
-    store(0);
+    int kt = 0;
+    do {
+      const bool last = kt + 1 >= w.nk;
+      load(last ? w2 : w, last ? 0 : kt + 1);
+      if (w.nk > 0) slice();
+      __syncthreads();
+      if (!last) {
+        store();
+        __syncthreads();
+      }
+      ++kt;
+    } while (kt < w.nk);
     if (tid == 0 && more)
       s_next[j & 1] =
           fetched < wq_count(args, wq, qx) ? wq_pack(qx, fetched) : take_sync(qx + 1);
 
-    // Epilogue through LDS buffer 1, 32 rows of the wave's block at a time:
-    // the accumulator layout puts one row per lane, so direct stores would
-    // send 32-byte pieces of 32 rows per instruction; staged, each store
-    // instruction writes two whole 512-byte rows.  Each wave stages in its
-    // own region (a wave's LDS accesses complete in order, so fences that
-    // keep the compiler from reordering them suffice); one barrier at the
-    // end keeps the next tile's slice stores out of regions still read.
+    // Epilogue through LDS, 32 rows of the wave's block at a time: the
+    // accumulator layout puts one row per lane, so direct stores would send
+    // 32-byte pieces of 32 rows per instruction; staged, each store
+    // instruction writes four whole 256-byte row pieces.  Each wave stages
+    // in its own region (a wave's LDS accesses complete in order, so fences
+    // that keep the compiler from reordering them suffice); the barrier at
+    // the end keeps the next tile's slice out of regions still read.
     {
       const BgSeg& g = args.seg[w.si];
-      constexpr int SP = 128 + 4;  // staging row pitch (floats)
-      static_assert(2 * 32 * SP * 4 <= WTILE_EL * 2, "two waves' staging per buffer");
-      float* stage = reinterpret_cast<float*>(wave < 2 ? &sA[1][0] : &sB[1][0]) +
-                     (wave & 1) * 32 * SP;
+      float* stage = reinterpret_cast<float*>(sT) + wave * 32 * kWgSP;
       // Stores through a buffer resource over this group's M x ldc output: a
       // row or column outside the output gets an offset past its end, which
-      // the hardware drops, so the 16 stores of a round need no branches.
+      // the hardware drops, so the stores of a round need no branches.
       const int M = g.M, N = g.N, ldc = (int)g.ldc;
       const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<float*>(g.C) + (int64_t)w.e * g.c_gstride, 0, M * ldc * 4, kBufWord3);
-      const int mrow0 = w.m0 + wm * 128, ncol0 = w.n0 + wn * 128;
+      const int mrow0 = w.m0 + wm * 128, ncol0 = w.n0 + wn * 64;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x16& a = acc[nb][mb];
             *reinterpret_cast<float4*>(
-                &stage[(lane & 31) * SP + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
+                &stage[(lane & 31) * kWgSP + nb * 32 + 8 * q + 4 * (lane >> 5)]) =
                 make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int c = ncol0 + 4 * (lane & 31);
+        const int c = ncol0 + 4 * (lane & 15);
         // AUX 2: non-temporal (final gradients: 2.2 GB at the 16B shape
-        // would otherwise push the shared operands out of L2; measured 30 %
-        // fewer HBM reads and 4 % faster)
+        // would otherwise push the shared operands out of L2)
         auto round = [&](auto aux) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = 2 * i + (lane >> 5);
+          for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4);
             const int m = mrow0 + mb * 32 + row;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row * SP + 4 * (lane & 31)]);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row * kWgSP + 4 * (lane & 15)]);
             const int off = (m < M && c < N) ? (m * ldc + c) * 4 : kBufDrop;
             __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, decltype(aux)::value);
           }
-          // all 16 LDS reads in flight at once, then the 16 stores
-          __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-          __builtin_amdgcn_sched_group_barrier(0x040, 16, 0);
+          // all 8 LDS reads in flight at once, then the 8 stores
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x040, 8, 0);
         };
         if (g.c_stream)
           round(std::integral_constant<int, 2>{});
@@ -1051,7 +1043,7 @@ __global__ void slab_sum_kernel(const float4* __restrict__ slabs, int G, int64_t
 
 int seg_blocks(BgKind kind, const BgSeg& g) {
   const int nN = (g.N + BN - 1) / BN;
-  if (kind == BG_WGRAD) return g.G * ((g.M + WB - 1) / WB) * ((g.N + WB - 1) / WB);
+  if (kind == BG_WGRAD) return g.G * ((g.M + WBM - 1) / WBM) * ((g.N + WBN - 1) / WBN);
   if (g.t_off) return g.max_tiles * nN;
   return (int)((g.rows + BM - 1) / BM) * nN;
 }
@@ -1116,7 +1108,7 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s, in
     int cus = 0;
     const hipError_t e = cu_count(&cus);
     if (e != hipSuccess) return e;
-    const int nwg = total < cus ? total : cus;
+    const int nwg = total < 2 * cus ? total : 2 * cus;  // two per CU
     hipLaunchKernelGGL(wgrad_kernel, dim3(nwg), dim3(NT), 0, s, args, work_ctr);
     return hipGetLastError();
   }
