@@ -641,7 +641,7 @@ def backward_regime(torch, moe, hip, args, cfg, inp, layer, packed=False, alpha=
                     f"expert weights, balance loss alpha = {alpha}",
         "ms_per_step": round(ms, 4),
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
-        "flop_per_step": int(sum(w["flop"] for w in work.values())),
+        "flop_per_step": int(sum(work[nm]["flop"] for nm in names)),  # the launches that ran
         "gemm_tflops": round(gflop / gsec / 1e12, 1),
         "gemm_mfma_frac": round(gflop / gsec / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": droof,
