@@ -199,11 +199,21 @@ __device__ __forceinline__ void unpack4(uint2 p, float* o) {
 // Rows grouping (the tile list of the forward's grouping, or one group of
 // `rows` rows).  A is K-contiguous; BKS: B K-strided in memory; DUAL: second
 // B with its own accumulators (SwiGLU's a and b); PK: B (and B2) packed.
-template <bool BKS, int EPI, bool DUAL, bool PK>
-__global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TILE_EL];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TILE_EL];
-  __shared__ __attribute__((aligned(16))) uint16_t sB2[DUAL ? 2 : 1][DUAL ? TILE_EL : 8];
+// SB: one staged slice and one register set, so the dual product (128
+// accumulators) fits two workgroups per CU instead of one and the single
+// product three instead of two; the other workgroups' MFMAs then run while
+// one stages a slice (16B: a/b recompute 776 -> 570 us, q 305 -> 272 us,
+// dx 540-560 -> 513-523 us).
+template <bool BKS, int EPI, bool DUAL, bool PK, bool SB = false>
+__global__ __launch_bounds__(NT, DUAL ? (SB ? 2 : 1) : (SB ? 3 : 2)) void bg_kernel(BgArgs args) {
+  static_assert(!SB || EPI == EPI_SWIGLU || EPI == EPI_BF16,
+                "single-buffered tiles stage at most the bf16 epilogue");
+  constexpr int NBUF = SB ? 1 : 2;
+  // a single sA buffer also holds the bf16 epilogue's staging (4 x 32 x 72)
+  constexpr int TEA = (SB && TILE_EL < 4 * 32 * 72) ? 4 * 32 * 72 : TILE_EL;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][TEA];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[DUAL ? NBUF : 1][DUAL ? TILE_EL : 8];
 
   int si = 0, L = 0;
   if (!xcd_pick(args, BN, si, L)) return;
@@ -273,9 +283,8 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
 
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
   // K slices kt+1 and kt+2 wait in registers (two sets, filled in turn)
-  // while slice kt is multiplied out of LDS.
-  constexpr int PF = 2;
-  static_assert(PF == 2, "the main loop below is unrolled for two register sets");
+  // while slice kt is multiplied out of LDS; SB: slice kt+1 in one set.
+  constexpr int PF = SB ? 1 : 2;
   for (int p = 0; p < g.npass && nk > 0; ++p) {
     const void* Ab = g.A[p];
     const void* Bb =
@@ -342,21 +351,38 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
     // every step issues its prefetch, clamped to the last slice: a load
     // under a branch leaves the compiler unsure how many loads are in flight
     // where the paths merge, and it then waits for all of them.
-    const int nkp = (nk + 1) & ~1;
-    load(0, 0);
-    load(1, 1);
-    store(0, 0);
-    __syncthreads();
-    // Unrolled by two so register sets and LDS buffers are static: slice
-    // kt = base + j sits in set j and LDS buffer j.
-    for (int base = 0; base < nkp; base += 2) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int kt = base + j;
-        load(kt + 2 < nkp ? kt + 2 : nkp - 1, j);
-        compute(j);
-        if (kt + 1 < nkp) store(j ^ 1, j ^ 1);
+    if constexpr (SB) {
+      // slice kt + 1 loads while slice kt is multiplied, then takes its
+      // place in LDS
+      load(0, 0);
+      store(0, 0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        load(kt + 1 < nk ? kt + 1 : nk - 1, 0);
+        compute(0);
         __syncthreads();
+        if (kt + 1 < nk) {
+          store(0, 0);
+          __syncthreads();
+        }
+      }
+    } else {
+      const int nkp = (nk + 1) & ~1;
+      load(0, 0);
+      load(1 % PF, 1 % PF);
+      store(0, 0);
+      __syncthreads();
+      // Unrolled by two so register sets and LDS buffers are static: slice
+      // kt = base + j sits in set j and LDS buffer j.
+      for (int base = 0; base < nkp; base += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kt = base + j;
+          load(kt + 2 < nkp ? kt + 2 : nkp - 1, j % PF);
+          compute(j % NBUF);
+          if (kt + 1 < nkp) store((j ^ 1) % PF, (j ^ 1) % NBUF);
+          __syncthreads();
+        }
       }
     }
   }
@@ -371,8 +397,8 @@ __global__ __launch_bounds__(NT, DUAL ? 1 : 2) void bg_kernel(BgArgs args) {
   // loads and stores run along rows.
   constexpr int SPF = 64 + 4;  // fp32 staging pitch (floats)
   constexpr int SPH = 64 + 8;  // bf16 staging pitch (elements)
-  static_assert(4 * 32 * SPF * 2 <= 2 * TILE_EL && 4 * 32 * SPH <= 2 * TILE_EL,
-                "epilogue staging fits the two buffers of sA");
+  static_assert((SB || 4 * 32 * SPF * 2 <= NBUF * TEA) && 4 * 32 * SPH <= NBUF * TEA,
+                "epilogue staging fits the buffers of sA");
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
     char* C = static_cast<char*>(g.C);
 #pragma unroll
@@ -1067,9 +1093,9 @@ hipError_t cu_count(int* out) {
   return hipSuccess;
 }
 
-template <bool BKS, int EPI, bool DUAL, bool PK = false>
+template <bool BKS, int EPI, bool DUAL, bool PK = false, bool SB = false>
 hipError_t launch_t(const BgArgs& args, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((bg_kernel<BKS, EPI, DUAL, PK>), dim3(grid), dim3(NT), 0, s, args);
+  hipLaunchKernelGGL((bg_kernel<BKS, EPI, DUAL, PK, SB>), dim3(grid), dim3(NT), 0, s, args);
   return hipGetLastError();
 }
 
@@ -1114,10 +1140,10 @@ hipError_t launch_bg(BgKind kind, const BgSeg* segs, int nseg, hipStream_t s, in
   }
   switch (kind) {
     case BG_LOGITS: return launch_t<false, EPI_F32, false>(args, grid, s);
-    case BG_PROJ: return launch_t<true, EPI_BF16, false>(args, grid, s);
-    case BG_SWIGLU: return launch_t<false, EPI_SWIGLU, true>(args, grid, s);
-    case BG_PROJ_PACKED: return launch_t<true, EPI_BF16, false, true>(args, grid, s);
-    case BG_SWIGLU_PACKED: return launch_t<false, EPI_SWIGLU, true, true>(args, grid, s);
+    case BG_PROJ: return launch_t<true, EPI_BF16, false, false, true>(args, grid, s);
+    case BG_SWIGLU: return launch_t<false, EPI_SWIGLU, true, false, true>(args, grid, s);
+    case BG_PROJ_PACKED: return launch_t<true, EPI_BF16, false, true, true>(args, grid, s);
+    case BG_SWIGLU_PACKED: return launch_t<false, EPI_SWIGLU, true, true, true>(args, grid, s);
     case BG_DU: return launch_t<true, EPI_DU, false>(args, grid, s);
     case BG_WGRAD: break;  // above
   }
