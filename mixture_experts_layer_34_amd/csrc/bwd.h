@@ -76,7 +76,7 @@ enum BgKind {
   BG_PROJ = 1,    // rows, K-strided B, bf16 out (q = dh W2, dx = da W1 + db W3)
   BG_SWIGLU = 2,  // rows, K-contiguous dual B, SwiGLU-backward epilogue
   BG_DU = 3,      // rows, K-strided B, du epilogue
-  BG_WGRAD = 4,   // k grouping, both operands K-strided, fp32 out, 256 x 256 tiles
+  BG_WGRAD = 4,   // k grouping, both operands K-strided, fp32 out, 256 x 128 tiles
   BG_PROJ_PACKED = 5,   // BG_PROJ with B in the packed weight layout (row length ldb)
   BG_SWIGLU_PACKED = 6  // BG_SWIGLU with B and B2 packed
 };
