@@ -138,8 +138,8 @@ __device__ __forceinline__ void kc_store(uint16_t* s, const u32x4 v[4], int tid)
 // 8 (wave & 1), kg = lane % 8 + 8 (wave / 2), so a wave's four loads cover
 // one band's four consecutive blocks, 4 KB of contiguous memory, instead of
 // two 2 KB pieces of two bands (dgrad with packed weights 10 % faster).  The
-// transposing LDS stores below stay on distinct banks either way (checked
-// on the host).  Rows are addressed directly: a row map would put a
+// transposing LDS stores below stay on distinct banks either way (measured:
+// 4 cycles per 8-byte store instruction).  Rows are addressed directly: a row map would put a
 // dependent load in front of every load, and the in-order load counter would
 // then wait for all loads in flight.
 template <bool PK>
