@@ -60,16 +60,39 @@ struct SkArgs {
 };
 
 // All passes of one item over its group's rows.  TWO: a second weight band
-// (the up projection's W3 band) is streamed next to the first.
+// (the up projection's W3 band) is streamed next to the first.  The first
+// ring of weight blocks depends only on the item's expert and band, so it is
+// requested before the group's rows are read (offs: the groups' row offsets,
+// nullable for a fixed r0 / nrows): the weight stream does not wait for the
+// offsets -> row map -> activation chain.
 template <bool UP, bool TWO>
-__device__ __forceinline__ void skinny_item(const SkSeg& g, int64_t r0, int64_t nrows,
-                                            const uint16_t* wa, const uint16_t* wb, int row_a,
-                                            int row_b) {
+__device__ __forceinline__ void skinny_item(const SkSeg& g, const int32_t* offs, int e, int64_t r0,
+                                            int64_t nrows, const uint16_t* wa, const uint16_t* wb,
+                                            int row_a, int row_b) {
   const int lane = threadIdx.x;
   const int KB = g.K / 16;
   const uint32_t wl = (uint32_t)lane * 16u;  // this lane's bytes in a 1 KB k block
   const int tok = lane & 31;                 // activation row of this lane in a pass
   const int kq = (lane >> 5) * 8;            // its k sub-offset in a 16-wide block
+  constexpr int kDepth = sk_depth<TWO>();
+  bf16x8 fa[kDepth], fb[TWO ? kDepth : 1], fx[kDepth];
+  auto wload = [&](int slot, int kb) {
+    kb = kb < KB ? kb : KB - 1;  // past the end: a block nobody reads
+    fa[slot] = ld_off<bf16x8>(wa, wl + (uint32_t)kb * 1024u);
+    if constexpr (TWO) fb[slot] = ld_off<bf16x8>(wb, wl + (uint32_t)kb * 1024u);
+  };
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) wload(j, j);
+  if (offs) {  // caller data: clamped into [0, rows]
+    int64_t a = offs[e], b = offs[e + 1];
+    a = a < 0 ? 0 : (a > g.rows ? g.rows : a);
+    b = b < a ? a : (b > g.rows ? g.rows : b);
+    r0 = a;
+    nrows = b - a;
+  }
+  // An expert nobody chose: its weights are not read past the first ring
+  // (s_endpgm waits for the ring's loads).
+  if (nrows <= 0) return;
 
   for (int64_t p0 = 0; p0 < nrows; p0 += 32) {
     int64_t pr = p0 + tok;
@@ -85,21 +108,25 @@ __device__ __forceinline__ void skinny_item(const SkSeg& g, int64_t r0, int64_t 
       acc_a[j] = 0.f;
       acc_b[j] = 0.f;
     }
-    constexpr int kDepth = sk_depth<TWO>();
-    bf16x8 fa[kDepth], fb[TWO ? kDepth : 1], fx[kDepth];
-    auto load = [&](int slot, int kb) {
-      kb = kb < KB ? kb : KB - 1;  // past the end: a block nobody reads
-      fa[slot] = ld_off<bf16x8>(wa, wl + (uint32_t)kb * 1024u);
-      if constexpr (TWO) fb[slot] = ld_off<bf16x8>(wb, wl + (uint32_t)kb * 1024u);
+    auto xload = [&](int slot, int kb) {
+      kb = kb < KB ? kb : KB - 1;
       fx[slot] = ld_off<bf16x8>(g.X, xo + (uint32_t)kb * 32u);
+    };
+    auto load = [&](int slot, int kb) {
+      wload(slot, kb);
+      xload(slot, kb);
     };
     auto mma = [&](int slot) {
       acc_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot], fx[slot], acc_a, 0, 0, 0);
       if constexpr (TWO)
         acc_b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot], fx[slot], acc_b, 0, 0, 0);
     };
+    if (p0 > 0) {  // a further pass streams the band again
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) load(j, j);
+      for (int j = 0; j < kDepth; ++j) wload(j, j);
+    }
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) xload(j, j);
     int kb0 = 0;
     for (; kb0 + kDepth <= KB; kb0 += kDepth) {
 #pragma unroll
@@ -154,13 +181,7 @@ __global__ __launch_bounds__(kSkThreads, kSkWavesPerSimd) void skinny_kernel(SkA
   const int e = L / g.nblk;
   int blk = L - e * g.nblk;
   int64_t r0 = 0, nrows = g.rows;
-  if (g.offsets) {  // caller data: clamped into [0, rows]
-    int64_t a = g.offsets[e], b = g.offsets[e + 1];
-    a = a < 0 ? 0 : (a > g.rows ? g.rows : a);
-    b = b < a ? a : (b > g.rows ? g.rows : b);
-    r0 = a;
-    nrows = b - a;
-  } else if (g.passes > 1) {
+  if (!g.offsets && g.passes > 1) {
     // Runs of 8 * passes items: 8 bands x passes row passes, the passes of
     // one band 8 items apart so they are dispatched to the same XCD and
     // share its L2 for the band's weights.
@@ -170,21 +191,19 @@ __global__ __launch_bounds__(kSkThreads, kSkWavesPerSimd) void skinny_kernel(SkA
     r0 = (int64_t)pass * 32;
     nrows = g.rows - r0 < 32 ? g.rows - r0 : 32;
   }
-  if (nrows <= 0) return;  // an expert nobody chose: its weights are not read
-
   const int KB = g.K / 16;
   const uint16_t* base = g.W0 + (int64_t)e * g.w_stride;
   if (UP) {
     const int row = blk * 32;  // W1 rows == W3 rows
     if (row >= g.N) return;
     const int64_t bo = (int64_t)(row >> 5) * KB * 512;
-    skinny_item<true, true>(g, r0, nrows, base + bo, g.W1 + (int64_t)e * g.w_stride + bo, row,
-                            row);
+    skinny_item<true, true>(g, g.offsets, e, r0, nrows, base + bo,
+                            g.W1 + (int64_t)e * g.w_stride + bo, row, row);
   } else {
     const int row = blk * 32;
     if (row >= g.N) return;
     const uint16_t* wa = base + (int64_t)(row >> 5) * KB * 512;
-    skinny_item<false, false>(g, r0, nrows, wa, wa, row, row);
+    skinny_item<false, false>(g, g.offsets, e, r0, nrows, wa, wa, row, row);
   }
 }
 
