@@ -334,24 +334,33 @@ struct PipePacked {
     }
   }
   // Loads of one slice's weights (and, for an even slice, of the activation
-  // pair two ahead), in the order a steady-state slice issues them.
-  template <bool EVEN>
+  // pair two ahead), in the order a steady-state slice issues them.  SKIP0:
+  // the first k half's weights are already in flight (first_weights).
+  template <bool EVEN, bool SKIP0 = false>
   __device__ __forceinline__ void preload(bf16x8 (&b)[2][NBW], int sb, u32x4 (&r)[4],
                                           int pa) const {
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       const int q = i / NBW, nb = i % NBW, kk = q >> 2, mi = q & 3;
-      if (mi == 3) bload(b, kk, nb, sb);
+      if (mi == 3 && !(SKIP0 && kk == 0)) bload(b, kk, nb, sb);
       if (EVEN && i == kAst + 2) aload(r, pa);
     }
   }
-  __device__ __forceinline__ void run(f32x16 (&acc)[4][NBW]) const {
+  // Slice 0's first k half of weights: they depend only on the tile's
+  // expert and column tile, so they are requested before the activation
+  // rows' gather indices are read.
+  __device__ __forceinline__ void first_weights(bf16x8 (&b)[2][NBW]) const {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) bload(b, 0, nb, 0);
+  }
+  // B0: slice 0's weights with the first k half in flight (first_weights).
+  __device__ __forceinline__ void run(f32x16 (&acc)[4][NBW], bf16x8 (&B0)[2][NBW]) const {
     u32x4 R[4];
-    bf16x8 A[2][4], B0[2][NBW], B1[2][NBW];
+    bf16x8 A[2][4], B1[2][NBW];
     aload(R, 0);
     astore(R, 0);
     __builtin_amdgcn_sched_barrier(0);
-    preload<true>(B0, 0, R, 1);
+    preload<true, true>(B0, 0, R, 1);
     preload<false>(B1, 1, R, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -387,6 +396,21 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
   __shared__ __attribute__((aligned(16))) uint16_t sA[PACKED ? 4 : 2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kSB];
 
+  // Packed weights: the first tile of each group (only segment 0 carries a
+  // tile list), read in one batch next to the tile count: lane l holds
+  // entries l, l + 64, ... (n_groups + 1 <= 257 of them), so finding a
+  // tile's group below takes ballots instead of a chain of dependent loads.
+  // (The row-major pipeline has no registers to spare for it and searches.)
+  const int lane_id = threadIdx.x & 63;
+  int toff[5] = {0, 0, 0, 0, 0};
+  if (PACKED && args.seg[0].tile_off) {
+    const GemmSeg& gl = args.seg[0];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {  // lanes past the end repeat the last entry
+      const int i = 64 * j + lane_id;
+      toff[j] = gl.tile_off[i < gl.n_groups ? i : gl.n_groups];
+    }
+  }
   const int G0 = seg_m_tiles(args.seg[0]) * args.seg[0].nN;
   const int G1 = args.nseg > 1 ? seg_m_tiles(args.seg[1]) * args.seg[1].nN : 0;
   const int G = G0 + G1;
@@ -403,8 +427,8 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
 
   // Logical order within a segment: group, then column tile, then M-tile,
   // so the M-tiles that share a weight tile run next to each other on one XCD.
-  int e, nt, row0, rows;
-  if (g.tile_off) {
+  int e, nt, row0, rows, mt_deferred = -1;
+  if (!PACKED && g.tile_off) {
     int lo = 0, hi = g.n_groups;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -420,6 +444,31 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
     const int mt = t0 + (local - nt * te);
     row0 = g.tile_row0[mt];
     rows = g.tile_rows[mt];
+  } else if (g.tile_off) {
+    // The group of logical tile L is the last one whose first tile * nN is
+    // <= L: the count of such groups, less one (the entries do not
+    // decrease).
+    const int t0v = toff[0], t1v = toff[1], t2v = toff[2], t3v = toff[3], t4v = toff[4];
+    const int nN = g.nN, ng = g.n_groups;
+    const int cnt = __popcll(__ballot((lane_id < ng) & (t0v * nN <= L))) +
+                    __popcll(__ballot((64 + lane_id < ng) & (t1v * nN <= L))) +
+                    __popcll(__ballot((128 + lane_id < ng) & (t2v * nN <= L))) +
+                    __popcll(__ballot((192 + lane_id < ng) & (t3v * nN <= L))) +
+                    __popcll(__ballot((256 + lane_id < ng) & (t4v * nN <= L)));
+    e = cnt - 1;
+    auto entry = [&](int i) {  // tile_off[i], i uniform: lane i % 64 of slot i / 64
+      const int l = i & 63, j = i >> 6;
+      const int r0 = __builtin_amdgcn_readlane(t0v, l), r1 = __builtin_amdgcn_readlane(t1v, l),
+                r2 = __builtin_amdgcn_readlane(t2v, l), r3 = __builtin_amdgcn_readlane(t3v, l),
+                r4 = __builtin_amdgcn_readlane(t4v, l);
+      return j == 0 ? r0 : j == 1 ? r1 : j == 2 ? r2 : j == 3 ? r3 : r4;
+    };
+    const int t0 = entry(e), te = entry(e + 1) - t0;
+    const int local = L - t0 * g.nN;
+    nt = local / te;
+    mt_deferred = t0 + (local - nt * te);  // its rows are read after the first weights
+    row0 = 0;
+    rows = 0;
   } else {
     const int num_m = seg_m_tiles(g);
     e = 0;
@@ -453,19 +502,11 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mi][nb][j] = 0.f;
 
-  // 32-row blocks holding at least one real row (uniform over the block).
-  // The main loop always computes all four: a second loop specialisation
-  // for shorter tiles would not fit the register budget next to this one.
-  const int mblocks = (rows + 31) >> 5;
   const int ns = g.K / BK;  // K is a multiple of 32
   if constexpr (PACKED) {
     // Packed weights: 32-row bands of 16-wide k blocks (512 elements each).
     const uint32_t KB = (uint32_t)(g.K / 16);
-    uint32_t arow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = arow_off(32 * wave + 8 * i + (lane >> 3));
-    PipePacked<UP, NBW> pipe{g, {}, {}, {arow[0], arow[1], arow[2], arow[3]}, ns, lane, wave,
-                             &sA[0][0]};
+    PipePacked<UP, NBW> pipe{g, {}, {}, {}, ns, lane, wave, &sA[0][0]};
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       // up: bands 0..NBW/2-1 of W1, then the same bands of W3; down: W2
@@ -474,7 +515,16 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
       pipe.bb[nb] = (UP && nb >= NBW / 2) ? b1base : b0base;
       pipe.bo[nb] = ((uint32_t)(brow >> 5) * KB * 512u + lane * 8) * 2u;
     }
-    pipe.run(acc);
+    bf16x8 B0[2][NBW];
+    pipe.first_weights(B0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (mt_deferred >= 0) {
+      row0 = g.tile_row0[mt_deferred];
+      rows = g.tile_rows[mt_deferred];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pipe.arow[i] = arow_off(32 * wave + 8 * i + (lane >> 3));
+    pipe.run(acc, B0);
   } else {
     static_assert(NBW == 4, "row-major weights take the 128 x 512 tile");
     const int lc = tid & 3, lr = tid >> 2;  // 16-byte chunk of a 32-wide row; row 0..63
@@ -495,6 +545,11 @@ __global__ __launch_bounds__(kThreads, NBW == 2 ? 2 : 1) void gemm_bf16_kernel(G
                         reinterpret_cast<uint16_t(*)[BN * LDK]>(&sB[0])};
     pipe.run(acc);
   }
+
+  // 32-row blocks holding at least one real row (uniform over the block).
+  // The main loop always computes all four: a second loop specialisation
+  // for shorter tiles would not fit the register budget next to this one.
+  const int mblocks = (rows + 31) >> 5;
 
   // Epilogue in two passes of 64 rows through an LDS staging tile (in sB).
   // The MFMAs computed the transposed tile (weights as the first operand),
@@ -670,6 +725,8 @@ static hipError_t launch_bf16_t(const FfnArgs* segs, int nseg, hipStream_t s) {
   args.nseg = 0;
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].rows == 0) continue;
+    // the kernel reads a tile list of segment 0 only
+    if (segs[i].tiles && args.nseg > 0) return hipErrorInvalidValue;
     args.seg[args.nseg] = UP ? up_seg<NBW>(segs[i]) : down_seg<NBW>(segs[i]);
     grid += max_m_tiles(segs[i]) * args.seg[args.nseg].nN;
     ++args.nseg;
