@@ -134,6 +134,12 @@ SMALL.update({
 })
 FULL = {k: v for k, v in moe_synth.CONFIGS.items() if k != "tiny"}
 FULL.update(moe_synth.GRANULARITY)
+# Tile lists that span more than one round of the GEMM launches' 512
+# workgroup slots (so the tail-claiming path runs) on small matrices, with
+# an odd number of K slices in the up projection (d = 416: 13 slices of 32)
+# and column tails in both projections.
+FULL["multi_round_bf16"] = moe_synth.MoEConfig("multi_round_bf16", T=4096, d=416, N=16, m=1,
+                                               K=9, K_s=1, d_ff=256, dtype="bf16")
 ALL = dict(SMALL, **FULL)
 
 _cache: dict = {}
