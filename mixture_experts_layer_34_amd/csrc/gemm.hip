@@ -283,7 +283,9 @@ struct PipeLds {
 template <bool UP, int NBW>
 struct PipePacked {
   static constexpr int kSteps = 8 * NBW;
-  static constexpr int kAst = kSteps - 12 + (NBW == 2 ? 2 : 0);  // 20 (NBW 4), 10 (NBW 2)
+  // 20 (NBW 4); 8 (NBW 2: swept over 2..12 on the 16B shape, up projection
+  // 376-377 us at 8 and 10 against 378-381 us at 2, 4, 6 and 12)
+  static constexpr int kAst = NBW == 2 ? 8 : kSteps - 12;
   static constexpr int kPairElems = 2 * BM * LDK;                // one pair buffer
   const GemmSeg& g;
   const uint16_t* bb[NBW];
