@@ -5,17 +5,19 @@
 // DeepSeekMoE card); grouping tokens per expert and fusing the weight
 // matrices is the page's note on production layers.
 //
-// bf16 path.  A workgroup of 4 waves computes a 128-row x 512-column tile;
-// each wave owns all 128 rows and 128 columns as 4 x 4 MFMA 32x32x16 blocks
-// (fp32 accumulators in AGPRs, one wave per SIMD).  K advances in 32-wide
-// slices through a software pipeline: while the MFMAs of slice s run, the
-// wave reads the operand fragments of slice s+1 from LDS, writes slice s+2
-// (staged in registers) into the LDS buffer slice s vacated, and issues the
-// global loads of slice s+3; the instruction groups are interleaved one
-// MFMA at a time so the LDS and the matrix cores work concurrently.
-// For the up projection a wave's 128 columns are 64 rows of W1 followed by
-// the same 64 rows of W3, so gate and up values of one output land in the
-// same lane and the SwiGLU is applied in registers.  The MFMAs take the
+// bf16 path.  A workgroup of 4 waves computes a 128-row tile; each wave
+// owns all 128 rows and NBW 32-column weight bands as 4 x NBW MFMA 32x32x16
+// blocks (fp32 accumulators).  Packed weights (the fast path, PipePacked):
+// NBW = 2, 128 x 256 tiles, two workgroups per CU, each wave streaming its
+// weight fragments straight into registers while the activations go
+// through LDS.  Row-major weights (PipeLds): NBW = 4, 128 x 512 tiles, one
+// workgroup per CU, both operands staged through LDS.  K advances in 32-wide
+// slices through a software pipeline whose loads, LDS traffic and MFMAs are
+// interleaved one MFMA at a time so the memory system and the matrix cores
+// work concurrently.
+// For the up projection a wave's columns are bands of W1 followed by the
+// same bands of W3, so gate and up values of one output land in the same
+// lane and the SwiGLU is applied in registers.  The MFMAs take the
 // weights as their first operand, so each accumulator holds the transposed
 // block: a lane owns one token and four consecutive output columns per
 // register group, which leave as one packed 8-byte LDS write, then through
