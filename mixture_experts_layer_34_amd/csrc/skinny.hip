@@ -90,8 +90,8 @@ __device__ __forceinline__ void skinny_item(const SkSeg& g, const int32_t* offs,
     r0 = a;
     nrows = b - a;
   }
-  // An expert nobody chose: its weights are not read past the first ring
-  // (s_endpgm waits for the ring's loads).
+  // An expert nobody chose: its weights are not read past the first ring,
+  // whose values go unused.
   if (nrows <= 0) return;
 
   for (int64_t p0 = 0; p0 < nrows; p0 += 32) {
