@@ -396,6 +396,8 @@ def other_shape(name, cfg, torch, moe, hip, steps, warmup, args=None, bwd_alpha=
                                                           if cfg.zipf_s else ""),
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
         "ms_per_step": round(ms, 4),
+        "steps": steps,
+        "warmup": warmup,
         "marked_ms_per_step": round(res["marked_ms_per_step"], 4),
         "median_ms_per_step": round(res["marked_median_ms_per_step"], 4),
         "steady_ms_per_step": round(res["steady_ms_per_step"], 4),
@@ -472,8 +474,10 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
         dinp = dict(inp, u=du, centroids=dc)
         host = dinp
     dl = Layer(dcfg, dinp, sets, moe, torch, moe.MOE_PACKED_WEIGHTS)
-    dres = time_layer(dl, hip, max(args.steps, 20), args.warmup)
-    gms = time_graph(dl, max(args.steps, 20), args.warmup)
+    # at least 10 warm-up and 200 timed steps: the step is 0.2 ms
+    dsteps, dwarm = max(args.steps, 200), max(args.warmup, 10)
+    dres = time_layer(dl, hip, dsteps, dwarm)
+    gms = time_graph(dl, dsteps, dwarm)
     dcounts = dl.counts.cpu().numpy()
     dwork = kernel_work(dcfg, int((dcounts > 0).sum()))
     dbytes = sum(dwork[name]["bytes"] for name in dres["kernels"])  # the launched kernels
@@ -482,6 +486,8 @@ def decode_regime(torch, moe, hip, args, inp=None, sets=None) -> dict:
     out = {
         "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
         "ms_per_step": round(dms, 4),
+        "steps": dsteps,
+        "warmup": dwarm,
         "marked_ms_per_step": round(dres["marked_ms_per_step"], 4),
         "median_ms_per_step": round(dres["marked_median_ms_per_step"], 4),
         "steady_ms_per_step": round(dres["steady_ms_per_step"], 4),
@@ -663,9 +669,12 @@ def tiny_regime(torch, moe, hip, args) -> dict:
     inp = moe_synth.make_inputs(cfg, seed=0)
     sets = [{k: to_device(inp[k], "cuda") for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}]
     layer = Layer(cfg, inp, sets, moe, torch, 0)
-    res = time_layer(layer, hip, max(args.steps, 50), args.warmup)
+    tsteps, twarm = max(args.steps, 200), max(args.warmup, 10)
+    res = time_layer(layer, hip, tsteps, twarm)
     ms = res["ms_per_step"]
     out = {
+        "steps": tsteps,
+        "warmup": twarm,
         "workload": f"tiny: T={cfg.T}, d={cfg.d}, {cfg.n} routed (top-{cfg.k}) + {cfg.K_s} shared,"
                     f" SwiGLU d_ff={cfg.d_ff}, fp32, row-major weights",
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
@@ -834,7 +843,8 @@ def main():
         for name in ("2b", "145b"):
             log(f"timing the {name}-shaped layer")
             out["other_shapes"][name] = other_shape(
-                name, moe_synth.CONFIGS[name], torch, moe, hip, max(20, args.steps), 3, args,
+                name, moe_synth.CONFIGS[name], torch, moe, hip, max(50, args.steps),
+                max(10, args.warmup), args,
                 moe_synth.BALANCE_ALPHA["2b" if name == "2b" else "16b"],
                 cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 3)
     if not args.no_tiny:
@@ -847,7 +857,7 @@ def main():
         out["granularity_sweep"] = {}
         for name, gcfg in moe_synth.GRANULARITY.items():
             log(f"timing the granularity sweep: {name}")
-            r = other_shape(name, gcfg, torch, moe, hip, max(20, args.steps), 3)
+            r = other_shape(name, gcfg, torch, moe, hip, max(50, args.steps), max(10, args.warmup))
             r["m"], r["n_routed"], r["top_k"], r["d_ff"] = gcfg.m, gcfg.n, gcfg.k, gcfg.d_ff
             out["granularity_sweep"][name] = r
     if not args.no_cpu_baseline:
