@@ -164,6 +164,18 @@ moe_status moe_combine(const moe_problem *p, const void *residual, const void *s
                        void *h, void *stream);
 
 /*
+ * The expert-level balance loss of "Expert-level balance loss":
+ *   loss[0] = alpha * sum_i f_i * P_i      over the n = m*N routed experts,
+ * from the statistics f [n] and P [n] that moe_route / moe_layer_fwd write
+ * (device pointers).  fp32: each product rounded, then added in ascending i
+ * starting from 0, then the product with alpha rounded (no fused
+ * multiply-add), so the value does not depend on any reduction tree.
+ * Asynchronous on `stream`; errors as for the other entry points.
+ */
+moe_status moe_balance_loss(const moe_problem *p, const float *f, const float *P, float alpha,
+                            float *loss, void *stream);
+
+/*
  * The whole layer: the equation of "Routing in a classic MoE layer"
  * (affinities, TopK gates, h = sum_i g_i FFN_i(u) + u) with the fine-grained
  * experts and the always-on shared experts of "What the 16B configuration

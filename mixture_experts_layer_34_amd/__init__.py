@@ -15,7 +15,7 @@ _EXPORTS = ("MOE_BF16", "MOE_F32", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_NO_RE
             "moe_status_str", "moe_workspace_bytes", "problem", "moe_layer_bwd",
             "moe_layer_bwd_marked", "moe_layer_bwd_kernels", "moe_bwd_workspace_bytes",
             "moe_train_workspace_bytes", "MOE_SAVE_FOR_BACKWARD", "moe_layer_fwd_noalloc",
-            "MOE_NOALLOC_SCRATCH_BYTES")
+            "MOE_NOALLOC_SCRATCH_BYTES", "moe_balance_loss")
 __all__ = list(_EXPORTS)
 
 

@@ -73,6 +73,8 @@ def _load():
     lib.moe_pack_weights.restype = st
     lib.moe_combine.argtypes = [PP, P, P, P, P, P, P, P]
     lib.moe_combine.restype = st
+    lib.moe_balance_loss.argtypes = [PP, P, P, ctypes.c_float, P, P]
+    lib.moe_balance_loss.restype = st
     lib.moe_layer_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int,
                                   P, sz, P]
     lib.moe_layer_fwd.restype = st
@@ -183,6 +185,11 @@ def moe_combine(p, residual, shared_out, y_perm, slot_of, topk_gate, h, stream=N
     _check("moe_combine", lib.moe_combine(
         ctypes.byref(p), _ptr(residual), _ptr(shared_out), _ptr(y_perm), _ptr(slot_of),
         _ptr(topk_gate), _ptr(h), _stream(stream)))
+
+
+def moe_balance_loss(p, f, P, alpha, loss, stream=None):
+    _check("moe_balance_loss", lib.moe_balance_loss(
+        ctypes.byref(p), _ptr(f), _ptr(P), float(alpha), _ptr(loss), _stream(stream)))
 
 
 def moe_layer_fwd(p, u, centroids, w1, w3, w2, ws1, ws3, ws2, h, topk_idx, topk_gate, counts,

@@ -430,6 +430,17 @@ moe_status moe_combine(const moe_problem* p, const void* residual, const void* s
   return MOE_OK;
 }
 
+moe_status moe_balance_loss(const moe_problem* p, const float* f, const float* P, float alpha,
+                            float* loss, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!f || !P || !loss) return MOE_ERR_NULL;
+  if (!aligned(f) || !aligned(P) || !aligned(loss)) return MOE_ERR_ALIGN;
+  MOE_TRY(moe::launch_balance_loss(f, P, d.n, alpha, loss, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_layer_fwd(const moe_problem* p, const void* u, const void* centroids,
                          const void* w1, const void* w3, const void* w2, const void* ws1,
                          const void* ws3, const void* ws2, void* h, int32_t* topk_idx,

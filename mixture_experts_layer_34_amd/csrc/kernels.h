@@ -47,6 +47,10 @@ hipError_t launch_route_small(const float* lg, int64_t T, int n, int k, int32_t*
                               int32_t* offsets, int32_t* perm_token, int32_t* slot_of,
                               const TileList* tiles, hipStream_t s);
 
+// loss[0] = alpha * sum_{i < n} f_i P_i, ascending i (n <= kMaxExperts).
+hipError_t launch_balance_loss(const float* f, const float* P, int n, float alpha, float* loss,
+                               hipStream_t s);
+
 // Histogram and ranks from a given topk_idx (standalone grouping).
 hipError_t launch_hist(const int32_t* topk_idx, int64_t T, int n, int k, int32_t* blk_cnt,
                        int32_t* lrank, hipStream_t s);

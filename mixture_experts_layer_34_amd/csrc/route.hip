@@ -997,6 +997,24 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
   if (tl.off) emit_tile_list(tl, n, s_cnt, s_off, s_toff, wsum, s_total, kSmallThreads);
 }
 
+// The expert-level balance loss alpha * sum_i f_i P_i ("Expert-level balance
+// loss"): the products are formed in parallel into LDS, then one thread adds
+// them in ascending i, so the value is that of a plain ascending sum.
+__global__ __launch_bounds__(kMaxExperts) void balance_loss_kernel(const float* __restrict__ f,
+                                                                   const float* __restrict__ P,
+                                                                   int n, float alpha,
+                                                                   float* __restrict__ loss) {
+  __shared__ __attribute__((aligned(16))) float prod[kMaxExperts];
+  const int i = threadIdx.x;
+  prod[i] = i < n ? __fmul_rn(f[i], P[i]) : 0.0f;
+  __syncthreads();
+  if (i == 0) {
+    float acc = 0.0f;
+    for (int j = 0; j < n; ++j) acc = __fadd_rn(acc, prod[j]);
+    loss[0] = __fmul_rn(alpha, acc);
+  }
+}
+
 constexpr int kTileThreads = 256;
 
 // Offsets that break the documented contract (decreasing, outside
@@ -1091,6 +1109,12 @@ hipError_t launch_route(int dtype, const void* u, const void* cent, int64_t T, i
 }
 
 bool route_small(int dtype, int64_t T) { return dtype == 1 && T <= kSmallTok; }
+
+hipError_t launch_balance_loss(const float* f, const float* P, int n, float alpha, float* loss,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(balance_loss_kernel, dim3(1), dim3(kMaxExperts), 0, s, f, P, n, alpha, loss);
+  return hipGetLastError();
+}
 
 hipError_t launch_logits_small(const void* u, const void* cent, int64_t T, int d, int n, float* lg,
                                hipStream_t s) {

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
 # define what the boundary's compute entry points do.
 PAGE_SECTIONS = ("Routing in a classic MoE layer", "Top-k routing, from affinities to gates",
                  "Expert-level balance loss", "What the 16B configuration looks like")
-BOUNDARY = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd")
+BOUNDARY = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
+            "moe_balance_loss")
 
 
 def declaration_comment(name):
@@ -214,6 +215,19 @@ def test_combine_checks():
         assert status(moe.moe_combine, p, A, A, *args) == "MOE_ERR_ALIGN", i
     assert status(moe.moe_combine, p, MIS, None, A, A, A, A) == "MOE_ERR_ALIGN"
     assert status(moe.moe_combine, p, None, MIS, A, A, A, A) == "MOE_ERR_ALIGN"
+
+
+def test_balance_loss_checks():
+    p = p16()
+    for i in range(3):
+        args = [A] * 3
+        args[i] = None
+        assert status(moe.moe_balance_loss, p, args[0], args[1], 0.01, args[2]) == \
+            "MOE_ERR_NULL", i
+        args[i] = MIS
+        assert status(moe.moe_balance_loss, p, args[0], args[1], 0.01, args[2]) == \
+            "MOE_ERR_ALIGN", i
+    assert status(moe.moe_balance_loss, p16(T=0), A, A, 0.01, A) == "MOE_ERR_SHAPE"
 
 
 def test_layer_fwd_checks():

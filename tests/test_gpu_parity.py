@@ -133,6 +133,22 @@ def test_route(case):
     assert ep <= tp
 
 
+@pytest.mark.parametrize("alpha", [0.001, 0.1])
+def test_balance_loss(case, alpha):
+    """The expert-level balance loss alpha * sum_i f_i P_i ("Expert-level
+    balance loss") over the oracle's statistics f and P: bit-exact against
+    the oracle's plain ascending fp32 sum."""
+    cfg, p, d = case.cfg, prob(case.cfg), "cuda"
+    f = torch.from_numpy(np.ascontiguousarray(case.route["f"], np.float32)).to(d)
+    P = torch.from_numpy(np.ascontiguousarray(case.route["P"], np.float32)).to(d)
+    loss = torch.full((4,), float("nan"), dtype=torch.float32, device=d)
+    moe.moe_balance_loss(p, f, P, alpha, loss)
+    torch.cuda.synchronize()
+    got = np.float32(loss[0].item())
+    ref = np.float32(oracle.balance_loss(case.route["f"], case.route["P"], alpha))
+    assert got.view(np.uint32) == ref.view(np.uint32), (got, ref)
+
+
 @pytest.mark.parametrize("name", DECODE)
 def test_decode_cases_cover_their_paths(name):
     """The few-rows workloads really are few rows per expert, and the skewed
